@@ -1,0 +1,110 @@
+/*
+ * gla.h - C ABI of libgla.so: chunkwise Gated Linear Attention (GLA) forward
+ * pass and single-token recurrent decode step for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "Gated Linear Attention (GLA): Mathematical Foundations,
+ * Data-Dependent Gating, Chunkwise Parallel Forms ...", section "The Gated
+ * Recurrent Update"): for each independent unit (sequence n, head h) and each
+ * token t of that sequence, with the per-key-channel gate alpha_t = exp(g_t),
+ *
+ *     S_t = diag(alpha_t) S_{t-1} + k_t^T v_t          (S is d_k x d_v, fp32)
+ *     o_t = q_t S_t                                    (the updated state)
+ *
+ * starting from S_0 = initial_state (zeros when NULL).  gla_chunk_fwd evaluates
+ * it with the chunkwise-parallel form of the same page (section "Mathematical
+ * Formulation of Chunk Computations": per chunk of 64 tokens an in-chunk
+ * cumulative log-gate, gated causal intra-chunk attention, an inter-chunk term
+ * from the carried state, and the state update), which equals the recurrence
+ * up to rounding.  gla_recurrent_step is one token of the recurrence per
+ * sequence: the decode step of the FlashLinearAttention page, section "The
+ * O(1) Inference Memory Revolution".  There is no 1/sqrt(d_k) scale: callers
+ * pre-scale q or k if they want one.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent) owned
+ *     by the caller; the library keeps no pointer after the call returns,
+ *     allocates no device memory and needs no workspace.
+ *   - Layouts are row-major, last index fastest, densely packed, and every
+ *     tensor pointer must be 16-byte aligned.
+ *   - dtype selects the element type of q, k, v, g and o: GLA_BF16 (bfloat16)
+ *     or GLA_F32 (float).  States are always fp32.
+ *   - stream is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work; they never synchronize.  Results are deterministic run to run.
+ *   - g = log(alpha) must be <= 0 (alpha in (0, 1]) and not +inf; this is not
+ *     checked.  g = -inf (alpha = 0) is allowed.  NaN and Inf inputs propagate;
+ *     in gla_chunk_fwd a NaN/Inf in v or k of token t can also reach outputs of
+ *     earlier tokens of the same 64-token chunk (a masked score 0 times NaN).
+ *   - Return value: GLA_OK, or an error code with nothing enqueued.  Argument
+ *     checks happen on the host before any HIP call; the contents of device
+ *     arrays (cu_seqlens) are trusted.  gla_last_error() gives the reason for
+ *     the calling thread's last non-OK return.  No C++ exception crosses this
+ *     boundary.
+ */
+#ifndef GLA_H_
+#define GLA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GLA_OK = 0,
+  GLA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer      */
+  GLA_ERR_UNSUPPORTED = 2, /* valid but not implemented (d_k, d_v, dtype, C)   */
+  GLA_ERR_LAUNCH = 3       /* the HIP runtime refused the kernel launch        */
+} gla_status;
+
+typedef enum { GLA_BF16 = 0, GLA_F32 = 1 } gla_dtype;
+
+/*
+ * Chunkwise-parallel GLA forward.
+ *
+ *   q, k, g       [B, H, T, dk]  dtype          (g = log alpha per key channel)
+ *   v             [B, H, T, dv]  dtype
+ *   o             [B, H, T, dv]  dtype, written
+ *   initial_state [Nseq, H, dk, dv] fp32, or NULL for zeros
+ *   final_state   [Nseq, H, dk, dv] fp32, written, or NULL to skip.  It may be
+ *                 the same pointer as initial_state (updated in place).
+ *
+ * Fixed length: cu_seqlens == NULL, Nseq = B, every sequence has T tokens.
+ * Packed variable length: cu_seqlens = device int32[num_seqs + 1], B == 1,
+ * Nseq = num_seqs, cu_seqlens[0] == 0, non-decreasing, cu_seqlens[num_seqs] == T;
+ * sequence n owns tokens [cu_seqlens[n], cu_seqlens[n+1]) of the T axis, chunks
+ * restart at each sequence start, and a sequence may be empty (its final state
+ * is its initial state).
+ *
+ * Supported: chunk_size == 64; dk in {64, 128} for GLA_BF16 and dk == 64 for
+ * GLA_F32; dv a positive multiple of 64 up to 512.  T >= 0 (T == 0 only writes
+ * final_state).  B * H * T and all index products must fit in int32 per tensor.
+ */
+int gla_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
+                  const float* initial_state, void* o, float* final_state,
+                  const int32_t* cu_seqlens, int num_seqs, int B, int H, int T,
+                  int dk, int dv, int chunk_size, int dtype, void* stream);
+
+/*
+ * One recurrent decode step for N sequences x H heads, in place on the state.
+ *
+ *   q, k, g  [N, H, dk]  dtype;   v  [N, H, dv]  dtype
+ *   state    [N, H, dk, dv] fp32, read and overwritten with S_t
+ *   o        [N, H, dv]  dtype, written (o = q S_t with the updated state)
+ *
+ * Supported: dk in {64, 128, 256}, dv in {64, 128, 256}, both dtypes.
+ */
+int gla_recurrent_step(const void* q, const void* k, const void* v, const void* g,
+                       float* state, void* o, int N, int H, int dk, int dv, int dtype,
+                       void* stream);
+
+/* Static, human-readable name of a gla_status value. */
+const char* gla_status_string(int status);
+
+/* Detail of the calling thread's last non-OK return ("" if none). */
+const char* gla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H_ */

@@ -1,0 +1,151 @@
+"""Thin Python binding over libgla.so (include/gla.h).
+
+Argument marshalling only: tensors supply device pointers, torch supplies the
+current HIP stream, and every step of the computation runs in the library's
+HIP kernels.  There is no CPU fallback: a missing library or a tensor that is
+not on the GPU raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgla.so")
+
+GLA_OK, GLA_ERR_INVALID_ARG, GLA_ERR_UNSUPPORTED, GLA_ERR_LAUNCH = 0, 1, 2, 3
+GLA_BF16, GLA_F32 = 0, 1
+
+_lib = None
+
+
+class GLAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_string(status)}: {detail}")
+        self.status = status
+
+
+def load_library():
+    """Open libgla.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m sub_quadratic_sequence_amd.build` "
+                "or __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I = ctypes.c_void_p, ctypes.c_int
+        lib.gla_chunk_fwd.restype = I
+        lib.gla_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P]
+        lib.gla_recurrent_step.restype = I
+        lib.gla_recurrent_step.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
+        lib.gla_status_string.restype = ctypes.c_char_p
+        lib.gla_status_string.argtypes = [I]
+        lib.gla_last_error.restype = ctypes.c_char_p
+        lib.gla_last_error.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load_library().gla_status_string(int(status)).decode()
+
+
+def last_error() -> str:
+    return load_library().gla_last_error().decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GLA_BF16
+    if t.dtype == torch.float32:
+        return GLA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_gpu(name, t, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device}); there is no CPU path")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def gla_chunk_fwd(q, k, v, g, initial_state=None, output_final_state=False, cu_seqlens=None,
+                  chunk_size: int = 64, out=None, final_state=None):
+    """Chunkwise GLA forward (C entry point ``gla_chunk_fwd``).
+
+    q, k, g: [B, H, T, dk]; v: [B, H, T, dv] (bfloat16 or float32, same dtype);
+    initial_state: [Nseq, H, dk, dv] float32 or None; cu_seqlens: int32 [Nseq+1]
+    on the GPU for packed sequences (B == 1).  Returns ``(o, final_state)``;
+    ``final_state`` is None unless ``output_final_state`` (or ``final_state``
+    is passed, which may alias ``initial_state``).
+    """
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    _check_gpu("q", q)
+    dt = q.dtype
+    _check_gpu("k", k, dt, q.shape)
+    _check_gpu("g", g, dt, q.shape)
+    _check_gpu("v", v, dt, (B, H, T, dv))
+    nseq = B
+    num_seqs = 0
+    if cu_seqlens is not None:
+        _check_gpu("cu_seqlens", cu_seqlens, torch.int32)
+        num_seqs = cu_seqlens.numel() - 1
+        nseq = num_seqs
+    if initial_state is not None:
+        _check_gpu("initial_state", initial_state, torch.float32, (nseq, H, dk, dv))
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=dt, device=q.device)
+    else:
+        _check_gpu("out", out, dt, (B, H, T, dv))
+    if final_state is None and output_final_state:
+        final_state = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif final_state is not None:
+        _check_gpu("final_state", final_state, torch.float32, (nseq, H, dk, dv))
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.gla_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(initial_state), _ptr(out),
+                               _ptr(final_state), _ptr(cu_seqlens), num_seqs, B, H, T, dk, dv,
+                               int(chunk_size), _dtype_code(q), ctypes.c_void_p(stream))
+    if rc != GLA_OK:
+        raise GLAError(rc, last_error())
+    return out, final_state
+
+
+def gla_recurrent_step(q, k, v, g, state, out=None):
+    """One decode step (C entry point ``gla_recurrent_step``): q, k, g [N, H, dk],
+    v [N, H, dv], state [N, H, dk, dv] float32 updated in place.  Returns o [N, H, dv]."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _check_gpu("q", q)
+    dt = q.dtype
+    _check_gpu("k", k, dt, q.shape)
+    _check_gpu("g", g, dt, q.shape)
+    _check_gpu("v", v, dt, (N, H, dv))
+    _check_gpu("state", state, torch.float32, (N, H, dk, dv))
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=dt, device=q.device)
+    else:
+        _check_gpu("out", out, dt, (N, H, dv))
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.gla_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(state), _ptr(out),
+                                    N, H, dk, dv, _dtype_code(q), ctypes.c_void_p(stream))
+    if rc != GLA_OK:
+        raise GLAError(rc, last_error())
+    return out

@@ -1,0 +1,130 @@
+"""The C ABI library: it loads, exports every function include/gla.h declares,
+and its host-side argument checks reject bad calls before any HIP call.  CPU
+only: no call here reaches a kernel (every argument set is invalid)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gla.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gla_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch  # noqa: F401  (torch first: the library binds to its HIP runtime)
+
+    from sub_quadratic_sequence_amd import gla
+
+    if not os.path.exists(gla.LIB_PATH):
+        pytest.skip("libgla.so not built (run __graft_entry__.build())")
+    return gla.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    assert names == ["gla_chunk_fwd", "gla_last_error", "gla_recurrent_step", "gla_status_string"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from sub_quadratic_sequence_amd import gla
+
+    out = subprocess.run(["nm", "-D", "--defined-only", gla.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    from sub_quadratic_sequence_amd import gla
+
+    assert gla.status_string(0) == "GLA_OK"
+    assert gla.status_string(1) == "GLA_ERR_INVALID_ARG"
+    assert gla.status_string(2) == "GLA_ERR_UNSUPPORTED"
+    assert gla.status_string(3) == "GLA_ERR_LAUNCH"
+    assert gla.status_string(99) == "GLA_UNKNOWN_STATUS"
+
+
+FAKE = 0x10000  # a 16-byte aligned address; never dereferenced (every call below is rejected)
+
+
+def _chunk(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, s0=None, o=FAKE, sT=None, cu=None, num_seqs=0, B=1,
+             H=2, T=64, dk=128, dv=128, C=64, dtype=0)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return lib.gla_chunk_fwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["s0"]), P(a["o"]),
+                             P(a["sT"]), P(a["cu"]), a["num_seqs"], a["B"], a["H"], a["T"],
+                             a["dk"], a["dv"], a["C"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), 1, "non-null"),
+    (dict(o=None), 1, "non-null"),
+    (dict(q=FAKE + 8), 1, "q is not 16-byte aligned"),
+    (dict(sT=FAKE + 4), 1, "final_state is not 16-byte aligned"),
+    (dict(B=0), 1, "must be positive"),
+    (dict(T=-1), 1, "must be positive"),
+    (dict(dtype=7), 1, "dtype"),
+    (dict(C=128), 2, "chunk_size"),
+    (dict(dk=96), 2, "dk=96"),
+    (dict(dk=128, dtype=1), 2, "dk=128"),
+    (dict(dv=96), 2, "dv=96"),
+    (dict(dv=1024), 2, "dv=1024"),
+    (dict(cu=FAKE, B=2, num_seqs=2), 1, "B == 1"),
+    (dict(cu=FAKE, num_seqs=0), 1, "num_seqs"),
+    (dict(B=4096, H=4096, T=4096), 1, "int32"),
+])
+def test_chunk_fwd_rejects(lib, kw, status, needle):
+    from sub_quadratic_sequence_amd import gla
+
+    rc = _chunk(lib, **kw)
+    assert rc == status
+    assert needle in gla.last_error()
+
+
+def test_chunk_fwd_zero_tokens_without_outputs_is_a_noop(lib):
+    # T == 0 and no final state: nothing to do, returns OK without touching the GPU
+    assert _chunk(lib, q=None, k=None, v=None, g=None, o=None, T=0) == 0
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(state=None), 1, "non-null"),
+    (dict(dk=96), 2, "dk=96"),
+    (dict(dv=512), 2, "dv=512"),
+    (dict(N=0), 1, "must be positive"),
+    (dict(o=FAKE + 2), 1, "o is not 16-byte aligned"),
+    (dict(dtype=-1), 1, "dtype"),
+])
+def test_recurrent_step_rejects(lib, kw, status, needle):
+    from sub_quadratic_sequence_amd import gla
+
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, state=FAKE, o=FAKE, N=4, H=2, dk=128, dv=128, dtype=0)
+    a.update(kw)
+    P = ctypes.c_void_p
+    rc = lib.gla_recurrent_step(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["state"]),
+                                P(a["o"]), a["N"], a["H"], a["dk"], a["dv"], a["dtype"], None)
+    assert rc == status
+    assert needle in gla.last_error()
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    from sub_quadratic_sequence_amd import gla
+
+    x = torch.zeros(1, 1, 64, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        gla.gla_chunk_fwd(x, x, x, x)
+    with pytest.raises(ValueError, match="GPU"):
+        gla.gla_recurrent_step(x[0], x[0], x[0], x[0], torch.zeros(1, 64, 64, 64))

@@ -1,0 +1,291 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the same
+seeded inputs.  Tolerances (per-unit max error over max |reference|, see
+parity.py): 2e-2 on the bf16 path, 1e-4 on the fp32 path.  Every test prints
+the case it is about to run before touching the GPU."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import TOL_BF16, TOL_F32, to64, unit_err_fixed, unit_err_varlen
+from sub_quadratic_sequence_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = min(16, os.cpu_count() or 1)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sub_quadratic_sequence_amd import gla
+
+    gla.load_library()
+    return torch.device("cuda:0")
+
+
+def say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _fwd(dev, d, s0=None, final=True, cu=None):
+    from sub_quadratic_sequence_amd import gla
+
+    args = [d[n].to(dev) for n in "qkvg"]
+    o, sf = gla.gla_chunk_fwd(*args, initial_state=None if s0 is None else s0.to(dev),
+                              output_final_state=final,
+                              cu_seqlens=None if cu is None else cu.to(dev))
+    torch.cuda.synchronize()
+    return o, sf
+
+
+def _check_fixed(d, o, sf, s0, tol, label):
+    o_ref, s_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], s0=s0, nthreads=NTHREADS)
+    e_o, e_s = unit_err_fixed(o, o_ref), unit_err_fixed(sf, s_ref)
+    print(f"{label}: O err {e_o:.3e}  S err {e_s:.3e}  (tol {tol})", flush=True)
+    assert np.all(np.isfinite(to64(o))) and np.all(np.isfinite(to64(sf)))
+    assert e_o <= tol and e_s <= tol, (e_o, e_s)
+
+
+# ------------------------------------------------------------------ the workloads
+def test_tiny_fp32(dev):
+    w = I.TINY_FP32
+    say(f"{w.name} seed={w.seed} gla_chunk_fwd")
+    d = I.chunk_inputs(w)
+    o, sf = _fwd(dev, d)
+    _check_fixed(d, o, sf, None, TOL_F32, w.name)
+
+
+def test_train_bf16_full(dev):
+    w = I.TRAIN_BF16
+    say(f"{w.name} seed={w.seed} gla_chunk_fwd (full size)")
+    d = I.chunk_inputs(w)
+    o, sf = _fwd(dev, d)
+    _check_fixed(d, o, sf, None, TOL_BF16, w.name)
+
+
+def test_long_bf16_full(dev):
+    w = I.LONG_BF16
+    say(f"{w.name} seed={w.seed} gla_chunk_fwd (full size, initial state)")
+    d = I.chunk_inputs(w)
+    o, sf = _fwd(dev, d, s0=d["s0"])
+    _check_fixed(d, o, sf, d["s0"], TOL_BF16, w.name)
+
+
+def test_varlen_strong_bf16_full(dev):
+    w = I.VARLEN_BF16
+    say(f"{w.name} seed={w.seed} gla_chunk_fwd (full size, packed, strong gates)")
+    d = I.chunk_inputs(w)
+    o, sf = _fwd(dev, d, cu=d["cu_seqlens"])
+    o_ref, s_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], cu_seqlens=d["cu_seqlens"],
+                                     nthreads=NTHREADS)
+    e_o = unit_err_varlen(o, o_ref, d["cu_seqlens"])
+    e_s = unit_err_fixed(sf, s_ref)
+    print(f"{w.name}: O err {e_o:.3e}  S err {e_s:.3e}", flush=True)
+    assert np.all(np.isfinite(to64(o)))
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+
+
+def test_decode_full(dev):
+    from sub_quadratic_sequence_amd import gla
+
+    w = I.DECODE_BF16
+    say(f"{w.name} seed={w.seed} gla_recurrent_step x{w.steps} (full size)")
+    d = I.decode_inputs(w)
+    st = d["s0"].to(dev).clone()
+    outs = []
+    for t in range(w.steps):
+        outs.append(gla.gla_recurrent_step(*(d[n][t].to(dev) for n in "qkvg"), st).float().cpu())
+    torch.cuda.synchronize()
+    # the oracle runs the same 64 tokens as one recurrence per (sequence, head)
+    q, k, v, g = (d[n].permute(1, 2, 0, 3).contiguous() for n in "qkvg")   # [N, H, steps, d]
+    o_ref, s_ref = oracle.recurrence(q, k, v, g, s0=d["s0"], nthreads=NTHREADS)
+    o_gpu = torch.stack(outs, 2)                                            # [N, H, steps, dv]
+    e_o, e_s = unit_err_fixed(o_gpu, o_ref), unit_err_fixed(st, s_ref)
+    print(f"{w.name}: O err {e_o:.3e}  S err {e_s:.3e}", flush=True)
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+
+
+# ------------------------------------------------------------------ fp32 path edge cases
+FP32_CASES = [
+    # (label, B, H, T, dv, gate, s0)
+    ("ragged_T200_s0", 1, 2, 200, 64, "weak", True),
+    ("T1", 2, 2, 1, 64, "weak", True),
+    ("T63", 1, 3, 63, 64, "weak", False),
+    ("T65_s0", 1, 2, 65, 64, "weak", True),
+    ("alpha1_s0", 2, 2, 256, 64, "zero", True),
+    ("strong_T300_s0", 1, 2, 300, 64, "strong", True),
+    ("dv192_B3H3_T130", 3, 3, 130, 192, "weak", True),
+    ("dv128_strong", 2, 1, 190, 128, "strong", False),
+]
+
+
+@pytest.mark.parametrize("label,B,H,T,dv,gate,s0", FP32_CASES, ids=[c[0] for c in FP32_CASES])
+def test_fp32_cases(dev, label, B, H, T, dv, gate, s0):
+    w = I.ChunkWorkload("fp32_edge", B=B, H=H, T=T, dk=64, dv=dv, dtype="f32", seed=101,
+                        k_scaled=True)
+    say(f"fp32 {label}: B={B} H={H} T={T} dk=64 dv={dv} gate={gate} s0={s0}")
+    d = I.chunk_inputs(w, gate=gate, s0=s0)
+    o, sf = _fwd(dev, d, s0=d["s0"])
+    _check_fixed(d, o, sf, d["s0"], TOL_F32, label)
+
+
+def test_fp32_extreme_gates_exact_diagonal(dev):
+    """Some channels decay by far more than 2^100 inside one 16-token sub-chunk
+    (and a few gates are -inf, alpha = 0): the diagonal score blocks are then
+    evaluated element by element."""
+    w = I.ChunkWorkload("fp32_extreme", B=1, H=2, T=192, dk=64, dv=64, dtype="f32", seed=7,
+                        k_scaled=True)
+    say("fp32 extreme gates: B=1 H=2 T=192 dk=64 dv=64, g down to -80 and -inf")
+    d = I.chunk_inputs(w, s0=True)
+    gen = torch.Generator().manual_seed(3)
+    mask = torch.rand(d["g"].shape, generator=gen) < 0.3
+    g = torch.where(mask, -80.0 * torch.rand(d["g"].shape, generator=gen), d["g"])
+    g[0, 0, 70, 5] = float("-inf")
+    d["g"] = g
+    o, sf = _fwd(dev, d, s0=d["s0"])
+    _check_fixed(d, o, sf, d["s0"], TOL_F32, "extreme")
+
+
+def test_fp32_varlen_with_empty_and_short(dev):
+    lengths = [5, 0, 64, 1, 130, 0, 77]
+    w = I.ChunkWorkload("fp32_varlen", B=1, H=2, T=0, dk=64, dv=64, dtype="f32", seed=11,
+                        k_scaled=True)
+    say(f"fp32 varlen lengths={lengths} with initial state")
+    d = I.chunk_inputs(w, lengths=lengths, s0=True)
+    o, sf = _fwd(dev, d, s0=d["s0"], cu=d["cu_seqlens"])
+    o_ref, s_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], s0=d["s0"],
+                                     cu_seqlens=d["cu_seqlens"])
+    e_o, e_s = unit_err_varlen(o, o_ref, d["cu_seqlens"]), unit_err_fixed(sf, s_ref)
+    print(f"varlen fp32: O err {e_o:.3e} S err {e_s:.3e}", flush=True)
+    assert e_o <= TOL_F32 and e_s <= TOL_F32
+    # empty sequences pass their initial state through unchanged
+    assert torch.equal(sf[1].cpu(), d["s0"][1]) and torch.equal(sf[5].cpu(), d["s0"][5])
+
+
+# ------------------------------------------------------------------ bf16 shapes
+BF16_CASES = [
+    ("dk64_dv64_T300", 2, 4, 300, 64, 64, "weak"),
+    ("dk128_dv192_T200", 1, 3, 200, 128, 192, "weak"),
+    ("dk128_dv512_T128", 1, 2, 128, 128, 512, "weak"),
+    ("dk128_strong_T257", 2, 2, 257, 128, 128, "strong"),
+]
+
+
+@pytest.mark.parametrize("label,B,H,T,dk,dv,gate", BF16_CASES, ids=[c[0] for c in BF16_CASES])
+def test_bf16_shapes(dev, label, B, H, T, dk, dv, gate):
+    w = I.ChunkWorkload("bf16_shape", B=B, H=H, T=T, dk=dk, dv=dv, dtype="bf16", seed=21)
+    say(f"bf16 {label}: B={B} H={H} T={T} dk={dk} dv={dv} gate={gate}, initial state")
+    d = I.chunk_inputs(w, gate=gate, s0=True)
+    o, sf = _fwd(dev, d, s0=d["s0"])
+    _check_fixed(d, o, sf, d["s0"], TOL_BF16, label)
+
+
+# ------------------------------------------------------------------ invariants
+def test_decode_fp32_small(dev):
+    from sub_quadratic_sequence_amd import gla
+
+    w = I.DecodeWorkload("dec_f32", N=5, H=3, dk=64, dv=128, steps=6, seed=9, dtype="f32")
+    say("gla_recurrent_step fp32 N=5 H=3 dk=64 dv=128 x6")
+    d = I.decode_inputs(w)
+    st = d["s0"].to(dev).clone()
+    s_ref = d["s0"].double().numpy()
+    for t in range(w.steps):
+        o = gla.gla_recurrent_step(*(d[n][t].to(dev) for n in "qkvg"), st)
+        o_ref, s_ref = oracle.decode_step(*(d[n][t] for n in "qkvg"), s_ref)
+        torch.cuda.synchronize()
+        assert unit_err_fixed(o, o_ref) <= TOL_F32
+    assert unit_err_fixed(st, s_ref) <= TOL_F32
+
+
+def test_decode_steps_equal_chunk_fwd(dev):
+    """64 decode steps and one chunked call over the same 64 tokens give the same
+    outputs and final state (fp32 path; both against each other)."""
+    from sub_quadratic_sequence_amd import gla
+
+    w = I.DecodeWorkload("dec_vs_chunk", N=3, H=2, dk=64, dv=64, steps=64, seed=13, dtype="f32")
+    say("decode x64 vs gla_chunk_fwd T=64, fp32, N=3 H=2 d=64")
+    d = I.decode_inputs(w)
+    st = d["s0"].to(dev).clone()
+    outs = [gla.gla_recurrent_step(*(d[n][t].to(dev) for n in "qkvg"), st) for t in range(64)]
+    o_dec = torch.stack(outs, 2)
+    q, k, v, g = (d[n].permute(1, 2, 0, 3).contiguous().to(dev) for n in "qkvg")
+    o_ch, s_ch = gla.gla_chunk_fwd(q, k, v, g, initial_state=d["s0"].to(dev), output_final_state=True)
+    torch.cuda.synchronize()
+    assert unit_err_fixed(o_dec, o_ch) <= 2e-4
+    assert unit_err_fixed(st, s_ch) <= 2e-4
+
+
+def test_split_call_composition(dev):
+    from sub_quadratic_sequence_amd import gla
+
+    w = I.TRAIN_BF16
+    say("split call: bf16 B=2 H=4 T=448 split at 192, state passed between calls")
+    d = I.chunk_inputs(w, B=2, H=4, T=448, s0=True)
+    args = [d[n].to(dev) for n in "qkvg"]
+    o, sf = gla.gla_chunk_fwd(*args, initial_state=d["s0"].to(dev), output_final_state=True)
+    a = [x[:, :, :192].contiguous() for x in args]
+    b = [x[:, :, 192:].contiguous() for x in args]
+    oa, sa = gla.gla_chunk_fwd(*a, initial_state=d["s0"].to(dev), output_final_state=True)
+    ob, sb = gla.gla_chunk_fwd(*b, initial_state=sa, output_final_state=True)
+    torch.cuda.synchronize()
+    assert unit_err_fixed(torch.cat([oa, ob], 2).float(), o.float()) <= TOL_BF16
+    assert unit_err_fixed(sb, sf) <= TOL_BF16
+
+
+def test_bitwise_deterministic(dev):
+    from sub_quadratic_sequence_amd import gla
+
+    say("determinism: bf16 B=2 H=4 T=320 d=128, two identical calls")
+    d = I.chunk_inputs(I.TRAIN_BF16, B=2, H=4, T=320, s0=True)
+    args = [d[n].to(dev) for n in "qkvg"]
+    s0 = d["s0"].to(dev)
+    o1, s1 = gla.gla_chunk_fwd(*args, initial_state=s0, output_final_state=True)
+    o2, s2 = gla.gla_chunk_fwd(*args, initial_state=s0, output_final_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_state_aliasing_in_place(dev):
+    from sub_quadratic_sequence_amd import gla
+
+    say("in place: final_state aliases initial_state, bf16 B=1 H=2 T=130")
+    d = I.chunk_inputs(I.TRAIN_BF16, B=1, H=2, T=130, s0=True)
+    args = [d[n].to(dev) for n in "qkvg"]
+    s0 = d["s0"].to(dev)
+    o1, s1 = gla.gla_chunk_fwd(*args, initial_state=s0.clone(), output_final_state=True)
+    st = s0.clone()
+    o2, s2 = gla.gla_chunk_fwd(*args, initial_state=st, final_state=st)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, st)
+
+
+def test_zero_tokens_passes_state(dev):
+    from sub_quadratic_sequence_amd import gla
+
+    say("T=0: final state equals initial state")
+    s0 = torch.randn(2, 3, 128, 128, device=dev)
+    e = torch.empty(2, 3, 0, 128, dtype=torch.bfloat16, device=dev)
+    o, sf = gla.gla_chunk_fwd(e, e, e, e, initial_state=s0, output_final_state=True)
+    o0, sz = gla.gla_chunk_fwd(e, e, e, e, output_final_state=True)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 3, 0, 128) and torch.equal(sf, s0) and not torch.any(sz)
+
+
+def test_nan_propagates(dev):
+    from sub_quadratic_sequence_amd import gla
+
+    say("NaN in v at token 70 of unit (0,1): NaN in column 3 of that unit from its chunk on")
+    d = I.chunk_inputs(I.TRAIN_BF16, B=1, H=2, T=192)
+    d["v"][0, 1, 70, 3] = float("nan")
+    o, sf = _fwd(dev, d)
+    o = o.float().cpu()
+    # the masked score (0) times NaN is NaN inside the 64-token chunk holding token 70,
+    # so earlier tokens of that chunk (64..69) may show it too; nothing before 64 may
+    assert torch.isfinite(o[0, 0]).all() and torch.isfinite(o[0, 1, :64]).all()
+    assert torch.isfinite(o[0, 1, :, [0, 1, 2, 4]]).all()
+    assert torch.isnan(o[0, 1, 70:, 3]).all()
+    assert torch.isnan(sf[0, 1]).any() and torch.isfinite(sf[0, 0]).all()
