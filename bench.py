@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunkwise GLA forward (and the decode step) on one MI355X.
+
+One step = one gla_chunk_fwd call over the training-shape batch B=8, H=16,
+T=2048, d_k=d_v=128, bf16 inputs, fp32 final state: all of the forward's
+stages run inside that call (gate cumsum, intra-chunk scores, P.V, inter term,
+state carry, varlen/tail handling).  Inputs are synthetic (seeded) and resident
+in HBM before timing starts.  The decode step (256 sequences x 16 heads,
+d=128, 64 consecutive steps) is timed in the same run and reported under
+"decode".  The fp64 CPU oracle is timed on the host on the same inputs.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GLA fwd tokens/s + TFLOP/s (% MFMA peak), B8 H16 T2048 d128 bf16"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "sub_quadratic_sequence_amd", "csrc", "chunk_fwd.hip")
+STEP_SRC = os.path.join(ROOT, "sub_quadratic_sequence_amd", "csrc", "recurrent_step.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def fwd_work(B, H, T, dk, dv, C, esz):
+    """Algorithmic FLOPs and bytes of one forward call (chunk form).
+    FLOPs per token and head: 2C(dk+dv) (scores and P.V over the chunk) +
+    4 dk dv (inter term and state update).  Bytes: q, k, g, v read once, o
+    written once, the fp32 final state written once."""
+    tokens_heads = B * H * T
+    flops = tokens_heads * (2 * C * (dk + dv) + 4 * dk * dv)
+    bytes_ = tokens_heads * esz * (3 * dk + 2 * dv) + B * H * dk * dv * 4
+    return flops, bytes_
+
+
+def decode_work(N, H, dk, dv, esz):
+    """Per decode step: 5 dk dv FLOPs per unit; bytes: the fp32 state read and
+    written (8 dk dv) plus q, k, g, v in and o out."""
+    units = N * H
+    return units * 5 * dk * dv, units * (8 * dk * dv + esz * (3 * dk + 2 * dv))
+
+
+def sha256(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic(name, src):
+    """HBM traffic per launch measured by rocprofv3 PMC counters, from the
+    committed summary, if it was taken on the current kernel source."""
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        line = line.strip()
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != sha256(src):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_launches(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        fn()
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) / steps, ev0.elapsed_time(ev1) / 1e3 / steps
+
+
+def bench_forward(args, torch, gla, inputs):
+    w = inputs.TRAIN_BF16
+    log(f"[bench] forward {w.name}: generating inputs")
+    d = inputs.chunk_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, g = (d[n].to(dev) for n in "qkvg")
+    o = torch.empty(w.B, w.H, w.T, w.dv, dtype=torch.bfloat16, device=dev)
+    sf = torch.empty(w.B, w.H, w.dk, w.dv, dtype=torch.float32, device=dev)
+
+    def step():
+        gla.gla_chunk_fwd(q, k, v, g, out=o, final_state=sf)
+
+    log(f"[bench] forward: {args.warmup} warmup + {args.steps} timed steps")
+    wall, gpu = time_launches(step, args.steps, args.warmup, torch)
+    flops, nbytes = fwd_work(w.B, w.H, w.T, w.dk, w.dv, 64, 2)
+    return dict(w=w, d=d, wall=wall, gpu=gpu, flops=flops, bytes=nbytes, tokens=w.B * w.T)
+
+
+def bench_decode(args, torch, gla, inputs):
+    w = inputs.DECODE_BF16
+    log(f"[bench] decode {w.name}: generating inputs")
+    d = inputs.decode_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, g = (d[n].to(dev) for n in "qkvg")
+    st = d["s0"].to(dev)
+    o = torch.empty(w.N, w.H, w.dv, dtype=torch.bfloat16, device=dev)
+    it = [0]
+
+    def step():
+        t = it[0] % w.steps
+        gla.gla_recurrent_step(q[t], k[t], v[t], g[t], st, out=o)
+        it[0] += 1
+
+    wall, gpu = time_launches(step, w.steps, min(args.warmup, w.steps), torch)
+    # cold variant: evict the state from the 256 MB last-level cache between steps
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    evs = []
+    for t in range(w.steps):
+        flush.fill_(t & 0xFF)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gla.gla_recurrent_step(q[t], k[t], v[t], g[t], st, out=o)
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    cold = sum(a.elapsed_time(b) for a, b in evs) / 1e3 / w.steps
+    flops, nbytes = decode_work(w.N, w.H, w.dk, w.dv, 2)
+    return dict(w=w, wall=wall, gpu=gpu, cold=cold, flops=flops, bytes=nbytes)
+
+
+def cpu_baseline(fwd, max_seconds=20.0):
+    """The fp64 oracle as it stands, on the host, on the forward workload's own
+    inputs: whole batch rows (sequences) are added until ~max_seconds of work."""
+    import oracle
+
+    w, d = fwd["w"], fwd["d"]
+    threads = min(16, os.cpu_count() or 1)
+    oracle.build(force=False)
+    done_tokens, elapsed, used, b = 0, 0.0, 0, 0
+    while b < w.B and elapsed < max_seconds:
+        sl = slice(b, b + 1)
+        t0 = time.perf_counter()
+        _, _, used = oracle.recurrence(d["q"][sl], d["k"][sl], d["v"][sl], d["g"][sl],
+                                       nthreads=threads, return_threads=True)
+        elapsed += time.perf_counter() - t0
+        done_tokens += w.T
+        b += 1
+    sample = (f"{b} of {w.B} sequences x {w.H} heads x {w.T} tokens of the same workload "
+              f"(fp64 token recurrence, OpenMP over heads)")
+    return {"value": done_tokens / elapsed, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": sample, "seconds": round(elapsed, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--only", choices=["fwd", "decode", "copy", "pmc"], default=None,
+                    help="profiling runs: launch only this part (copy = 512 MiB calibration "
+                         "copy; pmc = copy, then forward, then decode, a few launches each)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sub_quadratic_sequence_amd import gla, inputs
+
+    gla.load_library()
+    if args.only in ("copy", "pmc"):
+        src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] copy calibration: 5 x 512 MiB device-to-device copies done")
+        if args.only == "copy":
+            return
+        args.steps, args.warmup = 5, 1
+        bench_forward(args, torch, gla, inputs)
+        bench_decode(args, torch, gla, inputs)
+        log("[bench] pmc launches done")
+        return
+    if args.only == "decode":
+        dec = bench_decode(args, torch, gla, inputs)
+        log(f"[bench] decode warm {dec['gpu'] * 1e6:.1f} us/step, cold {dec['cold'] * 1e6:.1f} us/step")
+        return
+
+    fwd = bench_forward(args, torch, gla, inputs)
+    t = fwd["gpu"]
+    tflops = fwd["flops"] / t / 1e12
+    gbs = fwd["bytes"] / t / 1e9
+    log(f"[bench] forward: {t * 1e6:.1f} us/launch (events), {fwd['wall'] * 1e6:.1f} us/step (wall), "
+        f"{tflops:.1f} TFLOP/s, {gbs:.0f} GB/s")
+    if args.only == "fwd":
+        return
+    traffic = read_traffic("chunk_fwd_b8h16t2048d128_bf16_traffic.txt", KERNEL_SRC)
+    out = {
+        "metric": METRIC,
+        "value": fwd["tokens"] / fwd["wall"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": fwd["wall"] * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": fwd["w"].name, "B": 8, "H": 16, "T": 2048, "dk": 128, "dv": 128,
+                   "chunk": 64, "final_state": True, "initial_state": False},
+        "tflop_s": tflops,
+        "mfma_peak_frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "chunk_fwd_kernel<128, BF16>",
+                     "algorithmic_bytes_per_launch": fwd["bytes"],
+                     "algorithmic_flops_per_launch": fwd["flops"],
+                     "avg_launch_us": t * 1e6},
+    }
+    if not args.no_decode:
+        dec = bench_decode(args, torch, gla, inputs)
+        dgbs = dec["bytes"] / dec["gpu"] / 1e9
+        cgbs = dec["bytes"] / dec["cold"] / 1e9
+        log(f"[bench] decode: {dec['gpu'] * 1e6:.1f} us/step warm ({dgbs:.0f} GB/s), "
+            f"{dec['cold'] * 1e6:.1f} us/step cold ({cgbs:.0f} GB/s)")
+        out["decode"] = {
+            "workload": dec["w"].name, "tokens_per_s": dec["w"].N / dec["wall"],
+            "us_per_step": dec["gpu"] * 1e6, "us_per_step_cold_llc": dec["cold"] * 1e6,
+            "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dgbs / HBM_PEAK_GBS, "achieved_cold_llc": cgbs,
+                         "frac_cold_llc": cgbs / HBM_PEAK_GBS,
+                         "traffic": read_traffic("recurrent_step_n256h16d128_bf16_traffic.txt", STEP_SRC),
+                         "kernel": "recurrent_step_kernel<128, 128, BF16>",
+                         "algorithmic_bytes_per_launch": dec["bytes"]},
+        }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(fwd)
+        log(f"[bench] oracle: {out['cpu_baseline']['value']:.3g} tokens/s on "
+            f"{out['cpu_baseline']['cores']} threads")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,528 @@
+// Pipelined chunkwise GLA forward for gfx950 (MI355X), bf16 inputs, fp32 state.
+//
+// Same mathematics as chunk_fwd.hip (the chunk form of the page "Gated Linear
+// Attention (GLA): Mathematical Foundations ...", section "Mathematical
+// Formulation of Chunk Computations"), organised so that the gating work and
+// the matrix-core work of consecutive chunks overlap:
+//
+//  * one workgroup = 8 waves per (sequence, head, 64-column slice of d_v);
+//    waves 0-3 are producers, waves 4-7 consumers, one of each per SIMD.
+//  * producers turn chunk u+1's q, k, g, v into MFMA operand tiles in one LDS
+//    buffer while consumers run chunk u's contractions from the other buffer;
+//    a single workgroup barrier per chunk swaps them.
+//  * producer wave w owns key channels [w DK/4, (w+1) DK/4) of all 64 tokens:
+//    lane (tg, gq) holds tokens 4tg..4tg+3 x DK/16 channels, so the log2-gate
+//    cumulative sum is a serial sum over 4 tokens plus a 16-lane DPP scan.
+//  * consumer wave c owns state columns [16c, 16c+16) (all d_k rows) in MFMA
+//    accumulators and computes the transposed output tile O^T for those
+//    columns and all 64 queries.  The state rows are assigned to accumulator
+//    rows so that a lane's accumulator values for a 32-channel step are
+//    exactly the 8 contiguous channels its operand fragments use: the
+//    inter-chunk term takes S straight from the accumulators as an MFMA
+//    operand, without an LDS round trip.
+//
+// Numerics (decided per chunk and per producer wave, i.e. per 32-channel
+// slice, without cross-wave synchronisation):
+//  * fast slice (|Gamma_last| <= 60 in log2 units for all its channels):
+//    query operand Q 2^Gamma, key operand K 2^-Gamma, state keys K 2^-Gamma
+//    with S <- 2^Gamma_last (S + KT^T V).
+//  * safe slice: 16-token sub-chunk pivots B_p: query operand
+//    Q 2^(Gamma - B_p) (<= |Q|), key operand K 2^(B_{r+1} - Gamma) (<= |K|),
+//    per-(p, r) channel factors 2^(B_p - B_{r+1}) applied by the consumer,
+//    state keys K 2^(Gamma_last - Gamma) with S <- 2^Gamma_last S + KT^T V.
+//  * extreme slice (a 16-token decay beyond 2^100 in one of its channels): the
+//    diagonal 16x16 score blocks of that slice are summed element by element
+//    by the producer, exp2 of every gate difference, and added by consumers.
+#include "gla_device.h"
+#include "gla_kernels.h"
+
+namespace gla {
+
+namespace pipe {
+
+constexpr int C = 64;
+constexpr int DVT = 64;
+constexpr int PADE = 8;            // 16-byte row padding (bf16 elements)
+constexpr int PT = C + PADE;       // pitch of [channel | column][token] tiles
+constexpr float kFastLimit = 60.f;
+constexpr float kExtremeLimit = 100.f;
+
+template <int DK>
+struct Buf {
+  static constexpr int PQ = DK + PADE;
+  unsigned short q[C * PQ];        // query operand  [token][channel]
+  unsigned short k[C * PQ];        // key operand    [token][channel]
+  unsigned short kt[DK * PT];      // state keys     [channel][token]
+  unsigned short vt[DVT * PT];     // values         [column][token]
+  unsigned short diag[4][4][16][16];  // exact diagonal partials [slice][sub-chunk][i][j]
+  float w[7][DK];      // per-channel pair factors: 0-3 diagonal of sub-chunk p, 4 (2,0), 5 (3,1), 6 (3,0)
+  float bq[4][DK];     // inter-term factor per query sub-chunk
+  float pre[DK];       // S <- pre * S before the state update
+  float post[DK];      // S <- post * S after it
+  int flag[4];         // per producer wave: bit0 safe, bit1 extreme
+};
+
+// consumer state-row map: accumulator tile rb, row m -> key channel
+__device__ __forceinline__ int srow(int rb, int m) {
+  return 32 * (rb >> 1) + 8 * (m >> 2) + 4 * (rb & 1) + (m & 3);
+}
+
+}  // namespace pipe
+
+template <int DK>
+__global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm) {
+  using namespace pipe;
+  using BufT = Buf<DK>;
+  constexpr int PQ = BufT::PQ;
+  constexpr int CPL = DK / 16;   // producer: channels per lane
+  constexpr int WCH = DK / 4;    // producer: channels per wave
+  constexpr int KS = DK / 32;    // 32-channel contraction steps
+  constexpr int NRB = DK / 16;   // consumer: 16-row state tiles
+  constexpr int NWR = CPL / 2;   // 32-bit words per lane per token (q, k, g)
+
+  __shared__ __attribute__((aligned(16))) BufT bufs[2];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, m = lane & 15, gq = lane >> 4;
+  const bool producer = wave < 4;
+
+  // ---- work item ------------------------------------------------------------------
+  const int nblk = gridDim.x;
+  const int bid = blockIdx.x;
+  const int lin = prm.xcd_remap ? (bid & 7) * (nblk >> 3) + (bid >> 3) : bid;
+  const int unit = lin / prm.nvt, vt = lin - unit * prm.nvt;
+  const int n = unit / prm.H, h = unit - n * prm.H;
+  long bos, eos, rowbase;
+  if (prm.cu) {
+    bos = prm.cu[n];
+    eos = prm.cu[n + 1];
+    rowbase = (long)h * prm.T;
+  } else {
+    bos = 0;
+    eos = prm.T;
+    rowbase = ((long)n * prm.H + h) * prm.T;
+  }
+  const int DV = prm.DV;
+  const int vcol0 = vt * DVT;
+  const long sbase = (long)unit * DK * DV;
+  const int nch = (int)((eos - bos + C - 1) / C);
+
+  if (producer) {
+    // =========================== producer waves ===========================
+    const int w = wave;
+    const int tg = m;                      // tokens 4tg..4tg+3
+    const int ch0 = w * WCH + gq * CPL;    // first channel of this lane
+    const int sub = tg >> 2;               // 16-token sub-chunk
+    const int vc0 = w * 16 + gq * 4;       // first of 4 V columns
+    const unsigned short* qg = reinterpret_cast<const unsigned short*>(prm.q) + rowbase * DK + ch0;
+    const unsigned short* kg = reinterpret_cast<const unsigned short*>(prm.k) + rowbase * DK + ch0;
+    const unsigned short* gg = reinterpret_cast<const unsigned short*>(prm.g) + rowbase * DK + ch0;
+    const unsigned short* vg = reinterpret_cast<const unsigned short*>(prm.v) + rowbase * DV + vcol0 + vc0;
+
+    unsigned rq[4][NWR], rk[4][NWR], rg[4][NWR], rv[4][2];
+
+    auto prefetch = [&](int u) {
+      const long t0 = bos + (long)u * C;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const long t = t0 + 4 * tg + a;
+        if (t < eos) {
+          if constexpr (NWR == 4) {
+            const uint4 x = *reinterpret_cast<const uint4*>(qg + t * DK);
+            const uint4 y = *reinterpret_cast<const uint4*>(kg + t * DK);
+            const uint4 z = *reinterpret_cast<const uint4*>(gg + t * DK);
+            rq[a][0] = x.x; rq[a][1] = x.y; rq[a][2] = x.z; rq[a][3] = x.w;
+            rk[a][0] = y.x; rk[a][1] = y.y; rk[a][2] = y.z; rk[a][3] = y.w;
+            rg[a][0] = z.x; rg[a][1] = z.y; rg[a][2] = z.z; rg[a][3] = z.w;
+          } else {
+            const uint2 x = *reinterpret_cast<const uint2*>(qg + t * DK);
+            const uint2 y = *reinterpret_cast<const uint2*>(kg + t * DK);
+            const uint2 z = *reinterpret_cast<const uint2*>(gg + t * DK);
+            rq[a][0] = x.x; rq[a][1] = x.y;
+            rk[a][0] = y.x; rk[a][1] = y.y;
+            rg[a][0] = z.x; rg[a][1] = z.y;
+          }
+          const uint2 vv = *reinterpret_cast<const uint2*>(vg + t * DV);
+          rv[a][0] = vv.x;
+          rv[a][1] = vv.y;
+        } else {
+#pragma unroll
+          for (int i = 0; i < NWR; ++i) rq[a][i] = rk[a][i] = rg[a][i] = 0u;
+          rv[a][0] = rv[a][1] = 0u;
+        }
+      }
+    };
+
+    // bf16 element i (0..CPL-1) of a packed row fragment
+    auto el = [&](const unsigned (&r)[NWR], int i) -> float {
+      return (i & 1) ? __uint_as_float(r[i >> 1] & 0xffff0000u) : __uint_as_float(r[i >> 1] << 16);
+    };
+
+    auto produce = [&](BufT& B) {
+      float gam[4][CPL];   // Gamma (log2) relative to the chunk start
+      float B4[CPL];       // Gamma at the chunk's last row
+      bool fastw;
+      {
+        bool big = false;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          const float p0 = el(rg[0], i) * kLog2e;
+          const float p1 = p0 + el(rg[1], i) * kLog2e;
+          const float p2 = p1 + el(rg[2], i) * kLog2e;
+          const float p3 = p2 + el(rg[3], i) * kLog2e;
+          float inc = p3;                       // inclusive scan of lane totals over the row
+          inc += dpp<kRowShr1>(inc);
+          inc += dpp<kRowShr2>(inc);
+          inc += dpp<kRowShr4>(inc);
+          inc += dpp<kRowShr8>(inc);
+          const float ex = dpp<kRowShr1>(inc);  // exclusive prefix (0 in lane 0)
+          gam[0][i] = ex + p0;
+          gam[1][i] = ex + p1;
+          gam[2][i] = ex + p2;
+          gam[3][i] = ex + p3;
+          // Gamma_last: lane 15 of this 16-lane row
+          B4[i] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(inc), 0x1F0));
+          big |= !(fabsf(B4[i]) <= kFastLimit);
+        }
+        fastw = __ballot(big) == 0ull;
+      }
+      if (fastw) {
+        // ---- single pivot at the chunk start ----
+        float kh[4][CPL];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          float qe[CPL];
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) {
+            qe[i] = el(rq[a], i) * fast_exp2(gam[a][i]);
+            kh[a][i] = el(rk[a], i) * fast_exp2(-gam[a][i]);
+          }
+          const int row = 4 * tg + a;
+          lds_store_n<BF16, CPL>(B.q + row * PQ + ch0, qe);
+          lds_store_n<BF16, CPL>(B.k + row * PQ + ch0, kh[a]);
+        }
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+          store4<BF16>(B.kt + (ch0 + i) * PT + 4 * tg, kh[0][i], kh[1][i], kh[2][i], kh[3][i]);
+        if (tg == 0) {
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) {
+            const int c = ch0 + i;
+            B.pre[c] = 1.f;
+            B.post[c] = fast_exp2(B4[i]);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) B.bq[p][c] = 1.f;
+#pragma unroll
+            for (int e = 0; e < 7; ++e) B.w[e][c] = 1.f;
+          }
+        }
+        if (lane == 0) B.flag[w] = 0;
+      } else {
+        // ---- 16-token sub-chunk pivots (log2 gates floored at -256 so that an
+        //      alpha = 0 gate cannot produce inf - inf) ----
+        float loc[4][CPL], tot[CPL], Bp[CPL], s1v[CPL], s2v[CPL], b4[CPL];
+        bool ext = false;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          float pp[4];
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const float y = el(rg[a], i) * kLog2e;
+            pp[a] = (a ? pp[a - 1] : 0.f) + (y < -256.f ? -256.f : y);
+          }
+          float u4 = pp[3];
+          const float t1 = dpp<kRowShr1>(u4);
+          u4 += (tg & 3) >= 1 ? t1 : 0.f;
+          const float t2 = dpp<kRowShr2>(u4);
+          u4 += (tg & 3) >= 2 ? t2 : 0.f;
+          float ex = dpp<kRowShr1>(u4);
+          ex = (tg & 3) >= 1 ? ex : 0.f;
+#pragma unroll
+          for (int a = 0; a < 4; ++a) loc[a][i] = ex + pp[a];
+          const float tt = quad_bcast_c<3>(u4);
+          tot[i] = tt;
+          ext |= !(fabsf(tt) <= kExtremeLimit);
+        }
+        const bool extw = __ballot(ext) != 0ull;
+        if (extw) {
+          // exact diagonal partials, one (row a, key pair jj) at a time: sum over this
+          // lane's channels, then over the wave's four lane rows (its whole slice)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const int irow = (tg & 3) * 4 + a;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+              __builtin_amdgcn_sched_barrier(0);
+              float dd[2];
+#pragma unroll
+              for (int h2 = 0; h2 < 2; ++h2) {
+                const int j = 2 * jj + h2, src = j >> 2, b = j & 3;
+                float acc = 0.f;
+#pragma unroll
+                for (int i2 = 0; i2 < NWR; ++i2) {
+                  const unsigned kw = __builtin_bit_cast(unsigned, quad_bcast(__builtin_bit_cast(float, rk[b][i2]), src));
+                  const float l0 = quad_bcast(loc[b][2 * i2], src);
+                  const float l1 = quad_bcast(loc[b][2 * i2 + 1], src);
+                  acc += el(rq[a], 2 * i2) * __uint_as_float(kw << 16) * fast_exp2(loc[a][2 * i2] - l0);
+                  acc += el(rq[a], 2 * i2 + 1) * __uint_as_float(kw & 0xffff0000u) *
+                         fast_exp2(loc[a][2 * i2 + 1] - l1);
+                }
+                acc = j <= irow ? acc : 0.f;
+                acc += __shfl_xor(acc, 16);
+                acc += __shfl_xor(acc, 32);
+                dd[h2] = acc;
+              }
+              if (gq == 0)
+                *reinterpret_cast<unsigned*>(&B.diag[w][sub][irow][2 * jj]) = pack_bf16x2(dd[0], dd[1]);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // sub-chunk prefixes: s1 = total of sub-chunk p-1, s2 = of p-2, B_p = Gamma at
+        // the row before sub-chunk p, b4 = Gamma at the chunk's last row
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          const float tt = tot[i];
+          const float a1 = dpp<kRowShr4>(tt), a2 = dpp<kRowShr8>(tt), a3 = dpp<kRowShr12>(tt);
+          s1v[i] = a1;
+          s2v[i] = a2;
+          Bp[i] = (a1 + a2) + a3;
+          const float bn = Bp[i] + tt;
+          const float r4 = dpp<kRowRor4>(bn), r8 = dpp<kRowRor8>(bn), r12 = dpp<kRowRor12>(bn);
+          b4[i] = sub == 3 ? bn : sub == 0 ? r4 : sub == 1 ? r8 : r12;
+        }
+        float fke[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) fke[i] = fast_exp2(b4[i] - (Bp[i] + tot[i]));
+        float kte[4][CPL];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          float qh[CPL], kt[CPL];
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) {
+            qh[i] = el(rq[a], i) * fast_exp2(loc[a][i]);            // Q 2^(Gamma - B_p)
+            kt[i] = el(rk[a], i) * fast_exp2(tot[i] - loc[a][i]);   // K 2^(B_{p+1} - Gamma)
+            kte[a][i] = kt[i] * fke[i];                             // K 2^(Gamma_last - Gamma)
+          }
+          const int row = 4 * tg + a;
+          lds_store_n<BF16, CPL>(B.q + row * PQ + ch0, qh);
+          lds_store_n<BF16, CPL>(B.k + row * PQ + ch0, kt);
+        }
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+          store4<BF16>(B.kt + (ch0 + i) * PT + 4 * tg, kte[0][i], kte[1][i], kte[2][i], kte[3][i]);
+        if ((tg & 3) == 0) {
+          // one lane per (sub-chunk, channel group) writes the per-channel factors
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) {
+            const int c = ch0 + i;
+            B.bq[sub][c] = fast_exp2(Bp[i]);
+            // an extreme slice's diagonal blocks come from the exact partials alone
+            B.w[sub][c] = extw ? 0.f : fast_exp2(-tot[i]);
+            if (sub == 2) B.w[4][c] = fast_exp2(s1v[i]);
+            if (sub == 3) {
+              B.w[5][c] = fast_exp2(s1v[i]);
+              B.w[6][c] = fast_exp2(s1v[i] + s2v[i]);
+            }
+            if (sub == 0) {
+              B.pre[c] = fast_exp2(b4[i]);
+              B.post[c] = 1.f;
+            }
+          }
+        }
+        if (lane == 0) B.flag[w] = 1 | (extw ? 2 : 0);
+      }
+      // V as [column][token]: pair tokens (a, a+1) of one column in one word
+      {
+        unsigned* vt0 = reinterpret_cast<unsigned*>(B.vt);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int wi = c >> 1;
+          const unsigned sel = (c & 1) ? 0x07060302u : 0x05040100u;
+          const unsigned lo = __builtin_amdgcn_perm(rv[1][wi], rv[0][wi], sel);
+          const unsigned hi = __builtin_amdgcn_perm(rv[3][wi], rv[2][wi], sel);
+          *reinterpret_cast<uint2*>(vt0 + ((vc0 + c) * PT + 4 * tg) / 2) = uint2{lo, hi};
+        }
+      }
+    };
+
+    if (nch > 0) {
+      prefetch(0);
+      produce(bufs[0]);
+      if (nch > 1) prefetch(1);
+    }
+    __syncthreads();
+    for (int u = 0; u < nch; ++u) {
+      if (u + 1 < nch) {
+        produce(bufs[(u + 1) & 1]);
+        if (u + 2 < nch) prefetch(u + 2);
+      }
+      __syncthreads();
+    }
+  } else {
+    // =========================== consumer waves ===========================
+    const int cw = wave - 4;               // state / output columns [16cw, 16cw+16)
+    unsigned short* og = reinterpret_cast<unsigned short*>(prm.o) + rowbase * DV + vcol0;
+    f32x4 sacc[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int c = srow(rb, gq * 4 + s);
+        sacc[rb][s] = prm.s0 ? prm.s0[sbase + (long)c * DV + vcol0 + cw * 16 + m] : 0.f;
+      }
+    __syncthreads();
+    for (int u = 0; u < nch; ++u) {
+      const BufT& B = bufs[u & 1];
+      const int fl = B.flag[0] | B.flag[1] | B.flag[2] | B.flag[3];
+      const bool any_safe = (fl & 1) != 0;
+      const bool any_ext = (fl & 2) != 0;
+
+      // scaled copy of a query fragment by 8 per-channel factors
+      auto scaled = [&](const Frag<BF16>& f, const float* wrow, int ks) {
+        const float4 w0 = *reinterpret_cast<const float4*>(wrow + ks * 32 + gq * 8);
+        const float4 w1 = *reinterpret_cast<const float4*>(wrow + ks * 32 + gq * 8 + 4);
+        const uint4 r = __builtin_bit_cast(uint4, f.v);
+        float x[8];
+        x[0] = __uint_as_float(r.x << 16) * w0.x; x[1] = __uint_as_float(r.x & 0xffff0000u) * w0.y;
+        x[2] = __uint_as_float(r.y << 16) * w0.z; x[3] = __uint_as_float(r.y & 0xffff0000u) * w0.w;
+        x[4] = __uint_as_float(r.z << 16) * w1.x; x[5] = __uint_as_float(r.z & 0xffff0000u) * w1.y;
+        x[6] = __uint_as_float(r.w << 16) * w1.z; x[7] = __uint_as_float(r.w & 0xffff0000u) * w1.w;
+        Frag<BF16> o;
+        frag_from_f32(o, x);
+        return o;
+      };
+
+      // S_prev as the inter term's A operand: slots = channels 32ks+8gq..+7 (see srow)
+      Frag<BF16> sa[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const float sv[8] = {sacc[2 * ks][0],     sacc[2 * ks][1],     sacc[2 * ks][2],
+                             sacc[2 * ks][3],     sacc[2 * ks + 1][0], sacc[2 * ks + 1][1],
+                             sacc[2 * ks + 1][2], sacc[2 * ks + 1][3]};
+        frag_from_f32(sa[ks], sv);
+      }
+      // V^T rows of this wave's columns, tokens in the score accumulators' order
+      Frag<BF16> va[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const unsigned short* vrow = B.vt + (cw * 16 + m) * PT + ks * 32 + gq * 4;
+        frag_ld4x2(va[ks], vrow, vrow + 16);
+      }
+      Frag<BF16> kf[4][KS];   // key fragments of sub-chunk r, loaded when first needed
+      const long t0 = bos + (long)u * C;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        Frag<BF16> qf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          frag_ld8(kf[p][ks], B.k + (16 * p + m) * PQ + ks * 32 + gq * 8);
+          frag_ld8(qf[ks], B.q + (16 * p + m) * PQ + ks * 32 + gq * 8);
+        }
+        // scores P^T(r, p) = K_r Q_p^T, r <= p
+        f32x4 pacc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pacc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r <= p; ++r) {
+          const int widx = (p == r) ? p : (p == 2 && r == 0) ? 4 : (p == 3 && r == 1) ? 5 : (p == 3 && r == 0) ? 6 : -1;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            if (widx >= 0 && any_safe) {
+              const Frag<BF16> b = scaled(qf[ks], B.w[widx], ks);
+              mma(pacc[r], kf[r][ks], b);
+            } else {
+              mma(pacc[r], kf[r][ks], qf[ks]);
+            }
+          }
+        }
+        if (any_ext) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const int j = gq * 4 + s;
+            float e = 0.f;
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl)
+              if (B.flag[sl] & 2) e += bf16_bits_to_f32(B.diag[sl][p][m][j]);
+            pacc[p][s] += e;
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          if (gq * 4 + s > m) pacc[p][s] = 0.f;   // causal: key after query
+
+        // O^T(p) = V^T P^T + S_prev^T (Q 2^Gamma)^T
+        f32x4 oacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; 2 * ks <= p; ++ks) {
+          const float pv[8] = {pacc[2 * ks][0],     pacc[2 * ks][1],     pacc[2 * ks][2],
+                               pacc[2 * ks][3],     pacc[2 * ks + 1][0], pacc[2 * ks + 1][1],
+                               pacc[2 * ks + 1][2], pacc[2 * ks + 1][3]};
+          Frag<BF16> pb;
+          frag_from_f32(pb, pv);
+          mma(oacc, va[ks], pb);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (any_safe) {
+            const Frag<BF16> b = scaled(qf[ks], B.bq[p], ks);
+            mma(oacc, sa[ks], b);
+          } else {
+            mma(oacc, sa[ks], qf[ks]);
+          }
+        }
+        const long t = t0 + 16 * p + m;
+        if (t < eos)
+          store4<BF16>(og + t * DV + cw * 16 + gq * 4, oacc[0], oacc[1], oacc[2], oacc[3]);
+      }
+
+      // ---- state: S <- post * (pre * S + KT^T V) ----
+      if (any_safe) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const float4 f = *reinterpret_cast<const float4*>(&B.pre[srow(rb, gq * 4)]);
+          sacc[rb][0] *= f.x; sacc[rb][1] *= f.y; sacc[rb][2] *= f.z; sacc[rb][3] *= f.w;
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        Frag<BF16> vb;
+        frag_ld8(vb, B.vt + (cw * 16 + m) * PT + ks * 32 + gq * 8);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          Frag<BF16> ka;
+          frag_ld8(ka, B.kt + srow(rb, m) * PT + ks * 32 + gq * 8);
+          mma(sacc[rb], ka, vb);
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const float4 f = *reinterpret_cast<const float4*>(&B.post[srow(rb, gq * 4)]);
+        sacc[rb][0] *= f.x; sacc[rb][1] *= f.y; sacc[rb][2] *= f.z; sacc[rb][3] *= f.w;
+      }
+      __syncthreads();
+    }
+    if (prm.sT) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int c = srow(rb, gq * 4 + s);
+          prm.sT[sbase + (long)c * DV + vcol0 + cw * 16 + m] = sacc[rb][s];
+        }
+    }
+  }
+}
+
+int launch_chunk_fwd_pipe(const ChunkParams& prm, int dk, int nblocks, hipStream_t stream) {
+  if (dk == 128) {
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<128>), dim3(nblocks), dim3(512), 0, stream, prm);
+  } else if (dk == 64) {
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<64>), dim3(nblocks), dim3(512), 0, stream, prm);
+  } else {
+    return -2;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace gla

@@ -101,6 +101,17 @@ __device__ __forceinline__ void store8<F32>(float* p, const float* x) {
   *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
 }
 
+// Store N (4 or 8) consecutive elements.
+template <typename E, int N>
+__device__ __forceinline__ void lds_store_n(typename E::storage* p, const float* x) {
+  if constexpr (N == 8) {
+    store8<E>(p, x);
+  } else {
+    static_assert(N == 4, "store width");
+    store4<E>(p, x[0], x[1], x[2], x[3]);
+  }
+}
+
 // ---------------------------------------------------------------- MFMA operands
 // An "8-slot fragment" is what one lane contributes to a 16x16 tile over 32
 // contraction indices: for bf16 one v_mfma_f32_16x16x32_bf16 consumes it, for

@@ -35,6 +35,7 @@ struct StepParams {
 // Each returns 0 on success, -1 if the launch failed, -2 if no kernel exists
 // for the shape/dtype.
 int launch_chunk_fwd(const ChunkParams& prm, int dk, int dtype, int nblocks, hipStream_t stream);
+int launch_chunk_fwd_pipe(const ChunkParams& prm, int dk, int nblocks, hipStream_t stream);
 int launch_recurrent_step(const StepParams& prm, int units, int dk, int dv, int dtype,
                           hipStream_t stream);
 
