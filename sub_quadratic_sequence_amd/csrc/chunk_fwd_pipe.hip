@@ -33,6 +33,8 @@
 //  * extreme slice (a 16-token decay beyond 2^100 in one of its channels): the
 //    diagonal 16x16 score blocks of that slice are summed element by element
 //    by the producer, exp2 of every gate difference, and added by consumers.
+#include <type_traits>
+
 #include "gla_device.h"
 #include "gla_kernels.h"
 
@@ -61,6 +63,13 @@ struct Buf {
   float post[DK];      // S <- post * S after it
   int flag[4];         // per producer wave: bit0 safe, bit1 extreme
 };
+
+// Workgroup barrier that orders LDS only: it waits for this wave's LDS
+// operations but not for its outstanding global loads, so prefetches stay in
+// flight across it (a __syncthreads() fence would drain them every chunk).
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // consumer state-row map: accumulator tile rb, row m -> key channel
 __device__ __forceinline__ int srow(int rb, int m) {
@@ -109,6 +118,11 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
 
   if (producer) {
     // =========================== producer waves ===========================
+    // Lane (tg, gq) of producer wave w holds tokens 4tg..4tg+3 x key channels
+    // w*WCH + gq*CPL .. + CPL: the gate cumsum is a serial sum over 4 tokens
+    // plus a 16-lane DPP scan.  Each raw register group is reloaded with the
+    // next chunk's data as soon as this chunk has consumed it, so the loads
+    // overlap the rest of this chunk, the barrier and the next chunk's start.
     const int w = wave;
     const int tg = m;                      // tokens 4tg..4tg+3
     const int ch0 = w * WCH + gq * CPL;    // first channel of this lane
@@ -121,72 +135,97 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
 
     unsigned rq[4][NWR], rk[4][NWR], rg[4][NWR], rv[4][2];
 
-    auto prefetch = [&](int u) {
-      const long t0 = bos + (long)u * C;
+    // row t of chunk u, clamped into the sequence (rows past its end are re-reads
+    // of the last row, zeroed by mask_tail): loads never sit behind a branch
+    auto row = [&](int u, int a) __attribute__((always_inline)) -> long {
+      const long t = bos + (long)u * C + 4 * tg + a;
+      return t < eos ? t : eos - 1;
+    };
+    auto ld = [&](unsigned (&r)[NWR], const unsigned short* base) __attribute__((always_inline)) {
+      if constexpr (NWR == 4) {
+        const uint4 x = *reinterpret_cast<const uint4*>(base);
+        r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
+      } else {
+        const uint2 x = *reinterpret_cast<const uint2*>(base);
+        r[0] = x.x; r[1] = x.y;
+      }
+    };
+    auto load_v = [&](int u) __attribute__((always_inline)) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const long t = t0 + 4 * tg + a;
-        if (t < eos) {
-          if constexpr (NWR == 4) {
-            const uint4 x = *reinterpret_cast<const uint4*>(qg + t * DK);
-            const uint4 y = *reinterpret_cast<const uint4*>(kg + t * DK);
-            const uint4 z = *reinterpret_cast<const uint4*>(gg + t * DK);
-            rq[a][0] = x.x; rq[a][1] = x.y; rq[a][2] = x.z; rq[a][3] = x.w;
-            rk[a][0] = y.x; rk[a][1] = y.y; rk[a][2] = y.z; rk[a][3] = y.w;
-            rg[a][0] = z.x; rg[a][1] = z.y; rg[a][2] = z.z; rg[a][3] = z.w;
-          } else {
-            const uint2 x = *reinterpret_cast<const uint2*>(qg + t * DK);
-            const uint2 y = *reinterpret_cast<const uint2*>(kg + t * DK);
-            const uint2 z = *reinterpret_cast<const uint2*>(gg + t * DK);
-            rq[a][0] = x.x; rq[a][1] = x.y;
-            rk[a][0] = y.x; rk[a][1] = y.y;
-            rg[a][0] = z.x; rg[a][1] = z.y;
-          }
-          const uint2 vv = *reinterpret_cast<const uint2*>(vg + t * DV);
-          rv[a][0] = vv.x;
-          rv[a][1] = vv.y;
-        } else {
+        const uint2 x = *reinterpret_cast<const uint2*>(vg + row(u, a) * DV);
+        rv[a][0] = x.x; rv[a][1] = x.y;
+      }
+    };
+    auto load_g = [&](int u) __attribute__((always_inline)) {
 #pragma unroll
-          for (int i = 0; i < NWR; ++i) rq[a][i] = rk[a][i] = rg[a][i] = 0u;
-          rv[a][0] = rv[a][1] = 0u;
+      for (int a = 0; a < 4; ++a) ld(rg[a], gg + row(u, a) * DK);
+    };
+    auto load_qk = [&](int u, int a) __attribute__((always_inline)) {
+      ld(rq[a], qg + row(u, a) * DK);
+      ld(rk[a], kg + row(u, a) * DK);
+    };
+    auto mask_tail = [&](int u) __attribute__((always_inline)) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const bool ok = bos + (long)u * C + 4 * tg + a < eos;
+#pragma unroll
+        for (int i = 0; i < NWR; ++i) {
+          rq[a][i] = ok ? rq[a][i] : 0u;
+          rk[a][i] = ok ? rk[a][i] : 0u;
+          rg[a][i] = ok ? rg[a][i] : 0u;
         }
+        rv[a][0] = ok ? rv[a][0] : 0u;
+        rv[a][1] = ok ? rv[a][1] : 0u;
       }
     };
 
     // bf16 element i (0..CPL-1) of a packed row fragment
-    auto el = [&](const unsigned (&r)[NWR], int i) -> float {
+    auto el = [&](const unsigned (&r)[NWR], int i) __attribute__((always_inline)) -> float {
       return (i & 1) ? __uint_as_float(r[i >> 1] & 0xffff0000u) : __uint_as_float(r[i >> 1] << 16);
     };
 
-    auto produce = [&](BufT& B) {
-      float gam[4][CPL];   // Gamma (log2) relative to the chunk start
-      float B4[CPL];       // Gamma at the chunk's last row
-      bool fastw;
+    // produce chunk uc into B; un >= 0: reload the raw registers with chunk un
+    auto produce = [&](BufT& B, int uc, int un) __attribute__((always_inline)) {
+      if (uc == nch - 1) mask_tail(uc);   // only the last chunk can be partial
+      // V as [column][token]: pair tokens (a, a+1) of one column in one word
       {
-        bool big = false;
+        unsigned* vt0 = reinterpret_cast<unsigned*>(B.vt);
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-          const float p0 = el(rg[0], i) * kLog2e;
-          const float p1 = p0 + el(rg[1], i) * kLog2e;
-          const float p2 = p1 + el(rg[2], i) * kLog2e;
-          const float p3 = p2 + el(rg[3], i) * kLog2e;
-          float inc = p3;                       // inclusive scan of lane totals over the row
-          inc += dpp<kRowShr1>(inc);
-          inc += dpp<kRowShr2>(inc);
-          inc += dpp<kRowShr4>(inc);
-          inc += dpp<kRowShr8>(inc);
-          const float ex = dpp<kRowShr1>(inc);  // exclusive prefix (0 in lane 0)
-          gam[0][i] = ex + p0;
-          gam[1][i] = ex + p1;
-          gam[2][i] = ex + p2;
-          gam[3][i] = ex + p3;
-          // Gamma_last: lane 15 of this 16-lane row
-          B4[i] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(inc), 0x1F0));
-          big |= !(fabsf(B4[i]) <= kFastLimit);
+        for (int c = 0; c < 4; ++c) {
+          const int wi = c >> 1;
+          const unsigned sel = (c & 1) ? 0x07060302u : 0x05040100u;
+          const unsigned lo = __builtin_amdgcn_perm(rv[1][wi], rv[0][wi], sel);
+          const unsigned hi = __builtin_amdgcn_perm(rv[3][wi], rv[2][wi], sel);
+          *reinterpret_cast<uint2*>(vt0 + ((vc0 + c) * PT + 4 * tg) / 2) = uint2{lo, hi};
         }
-        fastw = __ballot(big) == 0ull;
       }
+      if (un >= 0) load_v(un);
+      float gam[4][CPL];   // Gamma (log2) relative to the chunk start
+      float inc[CPL];      // Gamma at this lane's last token
+      bool big = false;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const float p0 = el(rg[0], i) * kLog2e;
+        const float p1 = p0 + el(rg[1], i) * kLog2e;
+        const float p2 = p1 + el(rg[2], i) * kLog2e;
+        const float p3 = p2 + el(rg[3], i) * kLog2e;
+        float x = p3;                          // inclusive scan of lane totals over the row
+        x += dpp<kRowShr1>(x);
+        x += dpp<kRowShr2>(x);
+        x += dpp<kRowShr4>(x);
+        x += dpp<kRowShr8>(x);
+        inc[i] = x;
+        const float ex = x - p3;               // Gamma before this lane's first token
+        gam[0][i] = ex + p0;
+        gam[1][i] = ex + p1;
+        gam[2][i] = ex + p2;
+        gam[3][i] = x;
+        big |= !(fabsf(x) <= kFastLimit);      // |Gamma| grows along the chunk
+      }
+      const bool fastw = __ballot(big) == 0ull;
       if (fastw) {
+        if (un >= 0) load_g(un);
         // ---- single pivot at the chunk start ----
         float kh[4][CPL];
 #pragma unroll
@@ -197,19 +236,20 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
             qe[i] = el(rq[a], i) * fast_exp2(gam[a][i]);
             kh[a][i] = el(rk[a], i) * fast_exp2(-gam[a][i]);
           }
-          const int row = 4 * tg + a;
-          lds_store_n<BF16, CPL>(B.q + row * PQ + ch0, qe);
-          lds_store_n<BF16, CPL>(B.k + row * PQ + ch0, kh[a]);
+          if (un >= 0) load_qk(un, a);
+          const int rw = 4 * tg + a;
+          lds_store_n<BF16, CPL>(B.q + rw * PQ + ch0, qe);
+          lds_store_n<BF16, CPL>(B.k + rw * PQ + ch0, kh[a]);
         }
 #pragma unroll
         for (int i = 0; i < CPL; ++i)
           store4<BF16>(B.kt + (ch0 + i) * PT + 4 * tg, kh[0][i], kh[1][i], kh[2][i], kh[3][i]);
-        if (tg == 0) {
+        if (tg == 15) {   // this lane's last token is the chunk's last row
 #pragma unroll
           for (int i = 0; i < CPL; ++i) {
             const int c = ch0 + i;
             B.pre[c] = 1.f;
-            B.post[c] = fast_exp2(B4[i]);
+            B.post[c] = fast_exp2(inc[i]);
 #pragma unroll
             for (int p = 0; p < 4; ++p) B.bq[p][c] = 1.f;
 #pragma unroll
@@ -218,8 +258,8 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         }
         if (lane == 0) B.flag[w] = 0;
       } else {
-        // ---- 16-token sub-chunk pivots (log2 gates floored at -256 so that an
-        //      alpha = 0 gate cannot produce inf - inf) ----
+        // ---- 16-token sub-chunk pivots; log2 gates floored at -256 so that an
+        //      alpha = 0 gate cannot produce inf - inf ----
         float loc[4][CPL], tot[CPL], Bp[CPL], s1v[CPL], s2v[CPL], b4[CPL];
         bool ext = false;
 #pragma unroll
@@ -235,8 +275,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
           u4 += (tg & 3) >= 1 ? t1 : 0.f;
           const float t2 = dpp<kRowShr2>(u4);
           u4 += (tg & 3) >= 2 ? t2 : 0.f;
-          float ex = dpp<kRowShr1>(u4);
-          ex = (tg & 3) >= 1 ? ex : 0.f;
+          const float ex = u4 - pp[3];
 #pragma unroll
           for (int a = 0; a < 4; ++a) loc[a][i] = ex + pp[a];
           const float tt = quad_bcast_c<3>(u4);
@@ -304,9 +343,9 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
             kt[i] = el(rk[a], i) * fast_exp2(tot[i] - loc[a][i]);   // K 2^(B_{p+1} - Gamma)
             kte[a][i] = kt[i] * fke[i];                             // K 2^(Gamma_last - Gamma)
           }
-          const int row = 4 * tg + a;
-          lds_store_n<BF16, CPL>(B.q + row * PQ + ch0, qh);
-          lds_store_n<BF16, CPL>(B.k + row * PQ + ch0, kt);
+          const int rw = 4 * tg + a;
+          lds_store_n<BF16, CPL>(B.q + rw * PQ + ch0, qh);
+          lds_store_n<BF16, CPL>(B.k + rw * PQ + ch0, kt);
         }
 #pragma unroll
         for (int i = 0; i < CPL; ++i)
@@ -331,33 +370,25 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
           }
         }
         if (lane == 0) B.flag[w] = 1 | (extw ? 2 : 0);
-      }
-      // V as [column][token]: pair tokens (a, a+1) of one column in one word
-      {
-        unsigned* vt0 = reinterpret_cast<unsigned*>(B.vt);
+        // the rarer safe path reloads everything at its end (fewer live registers)
+        if (un >= 0) {
+          load_g(un);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int wi = c >> 1;
-          const unsigned sel = (c & 1) ? 0x07060302u : 0x05040100u;
-          const unsigned lo = __builtin_amdgcn_perm(rv[1][wi], rv[0][wi], sel);
-          const unsigned hi = __builtin_amdgcn_perm(rv[3][wi], rv[2][wi], sel);
-          *reinterpret_cast<uint2*>(vt0 + ((vc0 + c) * PT + 4 * tg) / 2) = uint2{lo, hi};
+          for (int a = 0; a < 4; ++a) load_qk(un, a);
         }
       }
     };
 
+    // step i produces chunk i while the consumers use chunk i-1
     if (nch > 0) {
-      prefetch(0);
-      produce(bufs[0]);
-      if (nch > 1) prefetch(1);
+      load_v(0);
+      load_g(0);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) load_qk(0, a);
     }
-    __syncthreads();
-    for (int u = 0; u < nch; ++u) {
-      if (u + 1 < nch) {
-        produce(bufs[(u + 1) & 1]);
-        if (u + 2 < nch) prefetch(u + 2);
-      }
-      __syncthreads();
+    for (int i = 0; i <= nch; ++i) {
+      if (i < nch) produce(bufs[i & 1], i, i + 1 < nch ? i + 1 : -1);
+      barrier_lds();
     }
   } else {
     // =========================== consumer waves ===========================
@@ -371,15 +402,12 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         const int c = srow(rb, gq * 4 + s);
         sacc[rb][s] = prm.s0 ? prm.s0[sbase + (long)c * DV + vcol0 + cw * 16 + m] : 0.f;
       }
-    __syncthreads();
-    for (int u = 0; u < nch; ++u) {
-      const BufT& B = bufs[u & 1];
-      const int fl = B.flag[0] | B.flag[1] | B.flag[2] | B.flag[3];
-      const bool any_safe = (fl & 1) != 0;
-      const bool any_ext = (fl & 2) != 0;
-
+    // one chunk of contractions; SAFE / EXT are compile-time so the body is branch-free
+    auto consume = [&](const BufT& B, int u, auto safe_tag, auto ext_tag) __attribute__((always_inline)) {
+      constexpr bool SAFE = decltype(safe_tag)::value;
+      constexpr bool EXT = decltype(ext_tag)::value;
       // scaled copy of a query fragment by 8 per-channel factors
-      auto scaled = [&](const Frag<BF16>& f, const float* wrow, int ks) {
+      auto scaled = [&](const Frag<BF16>& f, const float* wrow, int ks) __attribute__((always_inline)) {
         const float4 w0 = *reinterpret_cast<const float4*>(wrow + ks * 32 + gq * 8);
         const float4 w1 = *reinterpret_cast<const float4*>(wrow + ks * 32 + gq * 8 + 4);
         const uint4 r = __builtin_bit_cast(uint4, f.v);
@@ -392,7 +420,6 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         frag_from_f32(o, x);
         return o;
       };
-
       // S_prev as the inter term's A operand: slots = channels 32ks+8gq..+7 (see srow)
       Frag<BF16> sa[KS];
 #pragma unroll
@@ -410,7 +437,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         frag_ld4x2(va[ks], vrow, vrow + 16);
       }
       Frag<BF16> kf[4][KS];   // key fragments of sub-chunk r, loaded when first needed
-      const long t0 = bos + (long)u * C;
+      f32x4 oacc[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         Frag<BF16> qf[KS];
@@ -428,7 +455,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
           const int widx = (p == r) ? p : (p == 2 && r == 0) ? 4 : (p == 3 && r == 1) ? 5 : (p == 3 && r == 0) ? 6 : -1;
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            if (widx >= 0 && any_safe) {
+            if (SAFE && widx >= 0) {
               const Frag<BF16> b = scaled(qf[ks], B.w[widx], ks);
               mma(pacc[r], kf[r][ks], b);
             } else {
@@ -436,23 +463,22 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
             }
           }
         }
-        if (any_ext) {
+        if constexpr (EXT) {
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             const int j = gq * 4 + s;
             float e = 0.f;
 #pragma unroll
             for (int sl = 0; sl < 4; ++sl)
-              if (B.flag[sl] & 2) e += bf16_bits_to_f32(B.diag[sl][p][m][j]);
+              e += (B.flag[sl] & 2) ? bf16_bits_to_f32(B.diag[sl][p][m][j]) : 0.f;
             pacc[p][s] += e;
           }
         }
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          if (gq * 4 + s > m) pacc[p][s] = 0.f;   // causal: key after query
+        for (int s = 0; s < 4; ++s) pacc[p][s] = (gq * 4 + s > m) ? 0.f : pacc[p][s];  // causal
 
         // O^T(p) = V^T P^T + S_prev^T (Q 2^Gamma)^T
-        f32x4 oacc = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 o1 = f32x4{0.f, 0.f, 0.f, 0.f}, o2 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; 2 * ks <= p; ++ks) {
           const float pv[8] = {pacc[2 * ks][0],     pacc[2 * ks][1],     pacc[2 * ks][2],
@@ -460,24 +486,29 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
                                pacc[2 * ks + 1][2], pacc[2 * ks + 1][3]};
           Frag<BF16> pb;
           frag_from_f32(pb, pv);
-          mma(oacc, va[ks], pb);
+          mma(o1, va[ks], pb);
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          if (any_safe) {
+          if constexpr (SAFE) {
             const Frag<BF16> b = scaled(qf[ks], B.bq[p], ks);
-            mma(oacc, sa[ks], b);
+            mma(o2, sa[ks], b);
           } else {
-            mma(oacc, sa[ks], qf[ks]);
+            mma(o2, sa[ks], qf[ks]);
           }
         }
+        oacc[p] = o1 + o2;
+      }
+      const long t0 = bos + (long)u * C;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
         const long t = t0 + 16 * p + m;
         if (t < eos)
-          store4<BF16>(og + t * DV + cw * 16 + gq * 4, oacc[0], oacc[1], oacc[2], oacc[3]);
+          store4<BF16>(og + t * DV + cw * 16 + gq * 4, oacc[p][0], oacc[p][1], oacc[p][2], oacc[p][3]);
       }
 
       // ---- state: S <- post * (pre * S + KT^T V) ----
-      if (any_safe) {
+      if constexpr (SAFE) {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
           const float4 f = *reinterpret_cast<const float4*>(&B.pre[srow(rb, gq * 4)]);
@@ -500,7 +531,22 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         const float4 f = *reinterpret_cast<const float4*>(&B.post[srow(rb, gq * 4)]);
         sacc[rb][0] *= f.x; sacc[rb][1] *= f.y; sacc[rb][2] *= f.z; sacc[rb][3] *= f.w;
       }
-      __syncthreads();
+    };
+    using T_ = std::integral_constant<bool, true>;
+    using F_ = std::integral_constant<bool, false>;
+    for (int i = 0; i <= nch; ++i) {
+      if (i > 0) {
+        const int u = i - 1;
+        const BufT& B = bufs[u & 1];
+        const int fl = B.flag[0] | B.flag[1] | B.flag[2] | B.flag[3];
+        if (fl == 0)
+          consume(B, u, F_{}, F_{});
+        else if ((fl & 2) == 0)
+          consume(B, u, T_{}, F_{});
+        else
+          consume(B, u, T_{}, T_{});
+      }
+      barrier_lds();
     }
     if (prm.sT) {
 #pragma unroll

@@ -150,6 +150,40 @@ def test_fp32_extreme_gates_exact_diagonal(dev):
     _check_fixed(d, o, sf, d["s0"], TOL_F32, "extreme")
 
 
+@pytest.mark.parametrize("dk", [128, 64])
+def test_bf16_extreme_gates_exact_diagonal(dev, dk):
+    """bf16 path with gates that decay by more than 2^100 inside a 16-token
+    sub-chunk (and alpha = 0 tokens): exact diagonal partials."""
+    w = I.ChunkWorkload("bf16_extreme", B=2, H=2, T=200, dk=dk, dv=128, dtype="bf16", seed=17,
+                        k_scaled=True)
+    say(f"bf16 extreme gates: B=2 H=2 T=200 dk={dk} dv=128, g down to -80 and -inf")
+    d = I.chunk_inputs(w, s0=True)
+    gen = torch.Generator().manual_seed(5)
+    g = d["g"].float()
+    mask = torch.rand(g.shape, generator=gen) < 0.3
+    g = torch.where(mask, -80.0 * torch.rand(g.shape, generator=gen), g)
+    g[0, 1, 100, 7] = float("-inf")
+    g[1, 0, 10:20, :] = float("-inf")
+    d["g"] = g.to(torch.bfloat16)
+    o, sf = _fwd(dev, d, s0=d["s0"])
+    _check_fixed(d, o, sf, d["s0"], TOL_BF16, f"bf16 extreme dk={dk}")
+
+
+def test_bf16_mixed_fast_and_safe_slices(dev):
+    """Strong gates on some key channels only: within one chunk some 32-channel
+    slices take the single-pivot form and others the sub-chunk pivots."""
+    w = I.ChunkWorkload("bf16_mixed", B=1, H=3, T=256, dk=128, dv=128, dtype="bf16", seed=23)
+    say("bf16 mixed gates: strong on channels 32..63 and 100..101, weak elsewhere")
+    d = I.chunk_inputs(w, s0=True)
+    strong = I.chunk_inputs(w, gate="strong", s0=True)["g"]
+    g = d["g"].clone()
+    g[..., 32:64] = strong[..., 32:64]
+    g[..., 100:102] = strong[..., 100:102]
+    d["g"] = g
+    o, sf = _fwd(dev, d, s0=d["s0"])
+    _check_fixed(d, o, sf, d["s0"], TOL_BF16, "bf16 mixed")
+
+
 def test_fp32_varlen_with_empty_and_short(dev):
     lengths = [5, 0, 64, 1, 130, 0, 77]
     w = I.ChunkWorkload("fp32_varlen", B=1, H=2, T=0, dk=64, dv=64, dtype="f32", seed=11,
