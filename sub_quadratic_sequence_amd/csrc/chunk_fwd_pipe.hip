@@ -48,6 +48,7 @@ constexpr int PADE = 8;            // 16-byte row padding (bf16 elements)
 constexpr int PT = C + PADE;       // pitch of [channel | column][token] tiles
 constexpr float kFastLimit = 60.f;
 constexpr float kExtremeLimit = 100.f;
+constexpr int kBufferFlags = 0x00020000;   // gfx9 buffer descriptor word 3: raw 32-bit dwords
 
 template <int DK>
 struct Buf {
@@ -120,74 +121,93 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     // =========================== producer waves ===========================
     // Lane (tg, gq) of producer wave w holds tokens 4tg..4tg+3 x key channels
     // w*WCH + gq*CPL .. + CPL: the gate cumsum is a serial sum over 4 tokens
-    // plus a 16-lane DPP scan.  Each raw register group is reloaded with the
-    // next chunk's data as soon as this chunk has consumed it, so the loads
-    // overlap the rest of this chunk, the barrier and the next chunk's start.
+    // plus a 16-lane DPP scan.  Each group of raw registers (v, g, then q and
+    // k) is reloaded with the next chunk's data as soon as this chunk no longer
+    // needs it, early in the chunk: the raw q and k words first move to this
+    // lane's own slots of the operand tiles B.q / B.k (no other lane touches
+    // them) and are read back from there when the operands overwrite them.
     const int w = wave;
     const int tg = m;                      // tokens 4tg..4tg+3
     const int ch0 = w * WCH + gq * CPL;    // first channel of this lane
     const int sub = tg >> 2;               // 16-token sub-chunk
     const int vc0 = w * 16 + gq * 4;       // first of 4 V columns
-    const unsigned short* qg = reinterpret_cast<const unsigned short*>(prm.q) + rowbase * DK + ch0;
-    const unsigned short* kg = reinterpret_cast<const unsigned short*>(prm.k) + rowbase * DK + ch0;
-    const unsigned short* gg = reinterpret_cast<const unsigned short*>(prm.g) + rowbase * DK + ch0;
-    const unsigned short* vg = reinterpret_cast<const unsigned short*>(prm.v) + rowbase * DV + vcol0 + vc0;
+    // Raw buffer loads over the sequence's rows: a read past its last row
+    // returns zeros (the buffer's record count ends there), which is exactly
+    // the padding of a partial last chunk (q = k = v = 0, log-gate 0).  Offsets
+    // are byte offsets held whole in the VGPR operand.
+    const long r0 = rowbase + bos;
+    const int qk_rec = (int)(unsigned)((eos - bos) * DK * 2);   // < 2^32 (host-checked sizes)
+    const int v_rec = (int)(unsigned)((eos - bos) * DV * 2);
+    const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(static_cast<const void*>(static_cast<const unsigned short*>(prm.q) + r0 * DK)),
+        (short)0, qk_rec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(static_cast<const void*>(static_cast<const unsigned short*>(prm.k) + r0 * DK)),
+        (short)0, qk_rec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rs_g = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(static_cast<const void*>(static_cast<const unsigned short*>(prm.g) + r0 * DK)),
+        (short)0, qk_rec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(static_cast<const void*>(static_cast<const unsigned short*>(prm.v) + r0 * DV)),
+        (short)0, v_rec, kBufferFlags);
+    const unsigned qk_lane = ((4 * tg) * DK + ch0) * 2u;          // token 4tg, channel ch0
+    const unsigned v_lane = ((4 * tg) * DV + vcol0 + vc0) * 2u;   // token 4tg, column vcol0 + vc0
 
     unsigned rq[4][NWR], rk[4][NWR], rg[4][NWR], rv[4][2];
 
-    // row t of chunk u, clamped into the sequence (rows past its end are re-reads
-    // of the last row, zeroed by mask_tail): loads never sit behind a branch
-    auto row = [&](int u, int a) __attribute__((always_inline)) -> long {
-      const long t = bos + (long)u * C + 4 * tg + a;
-      return t < eos ? t : eos - 1;
-    };
-    auto ld = [&](unsigned (&r)[NWR], const unsigned short* base) __attribute__((always_inline)) {
+    auto ld = [&](unsigned (&r)[NWR], __amdgpu_buffer_rsrc_t rs, unsigned off) __attribute__((always_inline)) {
       if constexpr (NWR == 4) {
-        const uint4 x = *reinterpret_cast<const uint4*>(base);
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+        r[0] = x[0]; r[1] = x[1]; r[2] = x[2]; r[3] = x[3];
+      } else {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, 0);
+        r[0] = x[0]; r[1] = x[1];
+      }
+    };
+    auto lds_ld = [&](unsigned (&r)[NWR], const unsigned short* p) __attribute__((always_inline)) {
+      if constexpr (NWR == 4) {
+        const uint4 x = *reinterpret_cast<const uint4*>(p);
         r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
       } else {
-        const uint2 x = *reinterpret_cast<const uint2*>(base);
+        const uint2 x = *reinterpret_cast<const uint2*>(p);
         r[0] = x.x; r[1] = x.y;
       }
+    };
+    auto st = [&](unsigned short* p, const unsigned (&r)[NWR]) __attribute__((always_inline)) {
+      if constexpr (NWR == 4)
+        *reinterpret_cast<uint4*>(p) = uint4{r[0], r[1], r[2], r[3]};
+      else
+        *reinterpret_cast<uint2*>(p) = uint2{r[0], r[1]};
     };
     auto load_v = [&](int u) __attribute__((always_inline)) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const uint2 x = *reinterpret_cast<const uint2*>(vg + row(u, a) * DV);
-        rv[a][0] = x.x; rv[a][1] = x.y;
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs_v, (int)(v_lane + (unsigned)(u * C + a) * DV * 2u), 0, 0);
+        rv[a][0] = x[0]; rv[a][1] = x[1];
       }
     };
     auto load_g = [&](int u) __attribute__((always_inline)) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) ld(rg[a], gg + row(u, a) * DK);
+      for (int a = 0; a < 4; ++a) ld(rg[a], rs_g, qk_lane + (unsigned)(u * C + a) * DK * 2u);
     };
-    auto load_qk = [&](int u, int a) __attribute__((always_inline)) {
-      ld(rq[a], qg + row(u, a) * DK);
-      ld(rk[a], kg + row(u, a) * DK);
-    };
-    auto mask_tail = [&](int u) __attribute__((always_inline)) {
+    auto load_qk = [&](int u) __attribute__((always_inline)) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const bool ok = bos + (long)u * C + 4 * tg + a < eos;
-#pragma unroll
-        for (int i = 0; i < NWR; ++i) {
-          rq[a][i] = ok ? rq[a][i] : 0u;
-          rk[a][i] = ok ? rk[a][i] : 0u;
-          rg[a][i] = ok ? rg[a][i] : 0u;
-        }
-        rv[a][0] = ok ? rv[a][0] : 0u;
-        rv[a][1] = ok ? rv[a][1] : 0u;
+        ld(rq[a], rs_q, qk_lane + (unsigned)(u * C + a) * DK * 2u);
+        ld(rk[a], rs_k, qk_lane + (unsigned)(u * C + a) * DK * 2u);
       }
     };
-
     // bf16 element i (0..CPL-1) of a packed row fragment
     auto el = [&](const unsigned (&r)[NWR], int i) __attribute__((always_inline)) -> float {
       return (i & 1) ? __uint_as_float(r[i >> 1] & 0xffff0000u) : __uint_as_float(r[i >> 1] << 16);
     };
+    // this lane's slot for token a in a [token][channel] operand tile
+    auto slot = [&](unsigned short* tile, int a) __attribute__((always_inline)) -> unsigned short* {
+      return tile + (4 * tg + a) * PQ + ch0;
+    };
 
-    // produce chunk uc into B; un >= 0: reload the raw registers with chunk un
+    // produce chunk uc into B and start loading chunk un (a valid chunk index)
     auto produce = [&](BufT& B, int uc, int un) __attribute__((always_inline)) {
-      if (uc == nch - 1) mask_tail(uc);   // only the last chunk can be partial
       // V as [column][token]: pair tokens (a, a+1) of one column in one word
       {
         unsigned* vt0 = reinterpret_cast<unsigned*>(B.vt);
@@ -200,46 +220,56 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
           *reinterpret_cast<uint2*>(vt0 + ((vc0 + c) * PT + 4 * tg) / 2) = uint2{lo, hi};
         }
       }
-      if (un >= 0) load_v(un);
-      float gam[4][CPL];   // Gamma (log2) relative to the chunk start
-      float inc[CPL];      // Gamma at this lane's last token
+      __builtin_amdgcn_sched_barrier(0);
+      load_v(un);
+      // log2 gates, floored at -256 so that an alpha = 0 gate cannot produce
+      // inf - inf (a chunk holding such a gate is never a fast one, so the floor
+      // only acts on the safe path); pp = inclusive prefix over this lane's 4
+      // tokens, inc = inclusive prefix over the chunk at this lane's last token
+      float pp[4][CPL], inc[CPL];
       bool big = false;
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
-        const float p0 = el(rg[0], i) * kLog2e;
-        const float p1 = p0 + el(rg[1], i) * kLog2e;
-        const float p2 = p1 + el(rg[2], i) * kLog2e;
-        const float p3 = p2 + el(rg[3], i) * kLog2e;
-        float x = p3;                          // inclusive scan of lane totals over the row
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const float y = fmaxf(el(rg[a], i) * kLog2e, -256.f);
+          pp[a][i] = a ? pp[a - 1][i] + y : y;
+        }
+        float x = pp[3][i];
         x += dpp<kRowShr1>(x);
         x += dpp<kRowShr2>(x);
         x += dpp<kRowShr4>(x);
         x += dpp<kRowShr8>(x);
         inc[i] = x;
-        const float ex = x - p3;               // Gamma before this lane's first token
-        gam[0][i] = ex + p0;
-        gam[1][i] = ex + p1;
-        gam[2][i] = ex + p2;
-        gam[3][i] = x;
         big |= !(fabsf(x) <= kFastLimit);      // |Gamma| grows along the chunk
       }
+      __builtin_amdgcn_sched_barrier(0);
+      load_g(un);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        st(slot(B.q, a), rq[a]);
+        st(slot(B.k, a), rk[a]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      load_qk(un);
       const bool fastw = __ballot(big) == 0ull;
       if (fastw) {
-        if (un >= 0) load_g(un);
         // ---- single pivot at the chunk start ----
         float kh[4][CPL];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
+          unsigned xq[NWR], xk[NWR];
+          lds_ld(xq, slot(B.q, a));
+          lds_ld(xk, slot(B.k, a));
           float qe[CPL];
 #pragma unroll
           for (int i = 0; i < CPL; ++i) {
-            qe[i] = el(rq[a], i) * fast_exp2(gam[a][i]);
-            kh[a][i] = el(rk[a], i) * fast_exp2(-gam[a][i]);
+            const float gm = (inc[i] - pp[3][i]) + pp[a][i];   // Gamma of token 4tg+a
+            qe[i] = el(xq, i) * fast_exp2(gm);
+            kh[a][i] = el(xk, i) * fast_exp2(-gm);
           }
-          if (un >= 0) load_qk(un, a);
-          const int rw = 4 * tg + a;
-          lds_store_n<BF16, CPL>(B.q + rw * PQ + ch0, qe);
-          lds_store_n<BF16, CPL>(B.k + rw * PQ + ch0, kh[a]);
+          lds_store_n<BF16, CPL>(slot(B.q, a), qe);
+          lds_store_n<BF16, CPL>(slot(B.k, a), kh[a]);
         }
 #pragma unroll
         for (int i = 0; i < CPL; ++i)
@@ -258,34 +288,81 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         }
         if (lane == 0) B.flag[w] = 0;
       } else {
-        // ---- 16-token sub-chunk pivots; log2 gates floored at -256 so that an
-        //      alpha = 0 gate cannot produce inf - inf ----
-        float loc[4][CPL], tot[CPL], Bp[CPL], s1v[CPL], s2v[CPL], b4[CPL];
+        // ---- 16-token sub-chunk pivots ----
+        // loc = Gamma relative to the start of the token's sub-chunk, tot = the
+        // sub-chunk's total: a 4-lane scan of the lane totals within each quad
+        float loc[4][CPL], tot[CPL];
         bool ext = false;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-          float pp[4];
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const float y = el(rg[a], i) * kLog2e;
-            pp[a] = (a ? pp[a - 1] : 0.f) + (y < -256.f ? -256.f : y);
-          }
-          float u4 = pp[3];
+          float u4 = pp[3][i];
           const float t1 = dpp<kRowShr1>(u4);
           u4 += (tg & 3) >= 1 ? t1 : 0.f;
           const float t2 = dpp<kRowShr2>(u4);
           u4 += (tg & 3) >= 2 ? t2 : 0.f;
-          const float ex = u4 - pp[3];
+          const float ex = u4 - pp[3][i];
 #pragma unroll
-          for (int a = 0; a < 4; ++a) loc[a][i] = ex + pp[a];
+          for (int a = 0; a < 4; ++a) loc[a][i] = ex + pp[a][i];
           const float tt = quad_bcast_c<3>(u4);
           tot[i] = tt;
           ext |= !(fabsf(tt) <= kExtremeLimit);
         }
         const bool extw = __ballot(ext) != 0ull;
+        // sub-chunk prefixes: s1 = total of sub-chunk p-1, s2 = of p-2, B_p = Gamma at
+        // the row before sub-chunk p, b4 = Gamma at the chunk's last row; identical in
+        // the four lanes of a quad, so each lane writes CPL/4 channels' factors
+        float fke[CPL];
+        {
+          float s1v[CPL], s2v[CPL], Bp[CPL], b4[CPL];
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) {
+            const float tt = tot[i];
+            const float a1 = dpp<kRowShr4>(tt), a2 = dpp<kRowShr8>(tt), a3 = dpp<kRowShr12>(tt);
+            s1v[i] = a1;
+            s2v[i] = a2;
+            Bp[i] = (a1 + a2) + a3;
+            const float bn = Bp[i] + tt;
+            const float r4 = dpp<kRowRor4>(bn), r8 = dpp<kRowRor8>(bn), r12 = dpp<kRowRor12>(bn);
+            b4[i] = sub == 3 ? bn : sub == 0 ? r4 : sub == 1 ? r8 : r12;
+            fke[i] = fast_exp2(b4[i] - bn);   // 2^(Gamma_last - B_{p+1})
+          }
+          constexpr int NPL = CPL / 4;
+          const int qd = tg & 3;
+          auto pick = [&](const float (&x)[CPL], int j) __attribute__((always_inline)) -> float {
+            return qd == 0 ? x[j] : qd == 1 ? x[NPL + j] : qd == 2 ? x[2 * NPL + j] : x[3 * NPL + j];
+          };
+#pragma unroll
+          for (int j = 0; j < NPL; ++j) {
+            const int c = ch0 + qd * NPL + j;
+            const float s1 = pick(s1v, j);
+            const float ebq = fast_exp2(pick(Bp, j));
+            // an extreme slice's diagonal blocks come from the exact partials alone
+            const float ew = extw ? 0.f : fast_exp2(-pick(tot, j));
+            const float e1 = fast_exp2(s1);
+            const float e12 = fast_exp2(s1 + pick(s2v, j));
+            const float epre = fast_exp2(pick(b4, j));
+            B.bq[sub][c] = ebq;
+            B.w[sub][c] = ew;
+            if (sub == 2) B.w[4][c] = e1;
+            if (sub == 3) {
+              B.w[5][c] = e1;
+              B.w[6][c] = e12;
+            }
+            if (sub == 0) {
+              B.pre[c] = epre;
+              B.post[c] = 1.f;
+            }
+          }
+        }
         if (extw) {
           // exact diagonal partials, one (row a, key pair jj) at a time: sum over this
           // lane's channels, then over the wave's four lane rows (its whole slice)
+          unsigned sq[4][NWR], sk[4][NWR];
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            lds_ld(sq[a], slot(B.q, a));
+            lds_ld(sk[a], slot(B.k, a));
+          }
 #pragma unroll
           for (int a = 0; a < 4; ++a) {
             const int irow = (tg & 3) * 4 + a;
@@ -299,11 +376,11 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
                 float acc = 0.f;
 #pragma unroll
                 for (int i2 = 0; i2 < NWR; ++i2) {
-                  const unsigned kw = __builtin_bit_cast(unsigned, quad_bcast(__builtin_bit_cast(float, rk[b][i2]), src));
+                  const unsigned kw = __builtin_bit_cast(unsigned, quad_bcast(__builtin_bit_cast(float, sk[b][i2]), src));
                   const float l0 = quad_bcast(loc[b][2 * i2], src);
                   const float l1 = quad_bcast(loc[b][2 * i2 + 1], src);
-                  acc += el(rq[a], 2 * i2) * __uint_as_float(kw << 16) * fast_exp2(loc[a][2 * i2] - l0);
-                  acc += el(rq[a], 2 * i2 + 1) * __uint_as_float(kw & 0xffff0000u) *
+                  acc += el(sq[a], 2 * i2) * __uint_as_float(kw << 16) * fast_exp2(loc[a][2 * i2] - l0);
+                  acc += el(sq[a], 2 * i2 + 1) * __uint_as_float(kw & 0xffff0000u) *
                          fast_exp2(loc[a][2 * i2 + 1] - l1);
                 }
                 acc = j <= irow ? acc : 0.f;
@@ -317,77 +394,39 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-        // sub-chunk prefixes: s1 = total of sub-chunk p-1, s2 = of p-2, B_p = Gamma at
-        // the row before sub-chunk p, b4 = Gamma at the chunk's last row
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-          const float tt = tot[i];
-          const float a1 = dpp<kRowShr4>(tt), a2 = dpp<kRowShr8>(tt), a3 = dpp<kRowShr12>(tt);
-          s1v[i] = a1;
-          s2v[i] = a2;
-          Bp[i] = (a1 + a2) + a3;
-          const float bn = Bp[i] + tt;
-          const float r4 = dpp<kRowRor4>(bn), r8 = dpp<kRowRor8>(bn), r12 = dpp<kRowRor12>(bn);
-          b4[i] = sub == 3 ? bn : sub == 0 ? r4 : sub == 1 ? r8 : r12;
-        }
-        float fke[CPL];
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) fke[i] = fast_exp2(b4[i] - (Bp[i] + tot[i]));
         float kte[4][CPL];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
+          unsigned xq[NWR], xk[NWR];
+          lds_ld(xq, slot(B.q, a));
+          lds_ld(xk, slot(B.k, a));
           float qh[CPL], kt[CPL];
 #pragma unroll
           for (int i = 0; i < CPL; ++i) {
-            qh[i] = el(rq[a], i) * fast_exp2(loc[a][i]);            // Q 2^(Gamma - B_p)
-            kt[i] = el(rk[a], i) * fast_exp2(tot[i] - loc[a][i]);   // K 2^(B_{p+1} - Gamma)
-            kte[a][i] = kt[i] * fke[i];                             // K 2^(Gamma_last - Gamma)
+            qh[i] = el(xq, i) * fast_exp2(loc[a][i]);            // Q 2^(Gamma - B_p)
+            kt[i] = el(xk, i) * fast_exp2(tot[i] - loc[a][i]);   // K 2^(B_{p+1} - Gamma)
+            kte[a][i] = kt[i] * fke[i];                          // K 2^(Gamma_last - Gamma)
           }
-          const int rw = 4 * tg + a;
-          lds_store_n<BF16, CPL>(B.q + rw * PQ + ch0, qh);
-          lds_store_n<BF16, CPL>(B.k + rw * PQ + ch0, kt);
+          lds_store_n<BF16, CPL>(slot(B.q, a), qh);
+          lds_store_n<BF16, CPL>(slot(B.k, a), kt);
         }
 #pragma unroll
         for (int i = 0; i < CPL; ++i)
           store4<BF16>(B.kt + (ch0 + i) * PT + 4 * tg, kte[0][i], kte[1][i], kte[2][i], kte[3][i]);
-        if ((tg & 3) == 0) {
-          // one lane per (sub-chunk, channel group) writes the per-channel factors
-#pragma unroll
-          for (int i = 0; i < CPL; ++i) {
-            const int c = ch0 + i;
-            B.bq[sub][c] = fast_exp2(Bp[i]);
-            // an extreme slice's diagonal blocks come from the exact partials alone
-            B.w[sub][c] = extw ? 0.f : fast_exp2(-tot[i]);
-            if (sub == 2) B.w[4][c] = fast_exp2(s1v[i]);
-            if (sub == 3) {
-              B.w[5][c] = fast_exp2(s1v[i]);
-              B.w[6][c] = fast_exp2(s1v[i] + s2v[i]);
-            }
-            if (sub == 0) {
-              B.pre[c] = fast_exp2(b4[i]);
-              B.post[c] = 1.f;
-            }
-          }
-        }
         if (lane == 0) B.flag[w] = 1 | (extw ? 2 : 0);
-        // the rarer safe path reloads everything at its end (fewer live registers)
-        if (un >= 0) {
-          load_g(un);
-#pragma unroll
-          for (int a = 0; a < 4; ++a) load_qk(un, a);
-        }
       }
     };
 
-    // step i produces chunk i while the consumers use chunk i-1
+    // step i produces chunk i into bufs[i & 1] while the consumers use chunk i-1;
+    // the look-ahead index is clamped, so the last step re-reads the last chunk
+    // and no load sits behind a branch
     if (nch > 0) {
       load_v(0);
       load_g(0);
-#pragma unroll
-      for (int a = 0; a < 4; ++a) load_qk(0, a);
+      load_qk(0);
     }
     for (int i = 0; i <= nch; ++i) {
-      if (i < nch) produce(bufs[i & 1], i, i + 1 < nch ? i + 1 : -1);
+      if (i < nch) produce(bufs[i & 1], i, i + 1 < nch ? i + 1 : i);
       barrier_lds();
     }
   } else {
