@@ -44,19 +44,55 @@ namespace pipe {
 
 constexpr int C = 64;
 constexpr int DVT = 64;
-constexpr int PADE = 8;            // 16-byte row padding (bf16 elements)
-constexpr int PT = C + PADE;       // pitch of [channel | column][token] tiles
 constexpr float kFastLimit = 60.f;
 constexpr float kExtremeLimit = 100.f;
 constexpr int kBufferFlags = 0x00020000;   // gfx9 buffer descriptor word 3: raw 32-bit dwords
 
+// LDS tile layouts.  Rows are stored densely and the 16-byte units of a row
+// are permuted by XOR with a linear function of the row index, so that both
+// the producers' row-wise writes and the consumers' MFMA fragment reads reach
+// all LDS banks without conflicts (the maps were chosen by measuring every
+// access pattern of this kernel on gfx950).  A linear map lets an address
+// split into a per-lane part and a compile-time part: swz(a ^ b) =
+// swz(a) ^ swz(b) for row bits that do not overlap.
+//
+// [token][channel] tiles (query / key operands), DK = 128: 64 rows of 256 B,
+// unit u of row r at ((u ^ tok_swz(r)) & 15).  DK = 64 uses 16-byte padded
+// rows instead.
+__device__ __forceinline__ constexpr int tok_swz(int r) {
+  return ((r & 1) ? 2 : 0) ^ ((r & 2) ? 1 : 0) ^ ((r & 4) ? 6 : 0) ^ ((r & 8) ? 15 : 0) ^
+         ((r & 16) ? 13 : 0) ^ ((r & 32) ? 10 : 0);
+}
+// [channel | column][token] tiles (state keys, values): rows of 64 tokens =
+// 128 B, 16-byte unit u of row r at ((u ^ tr_swz(r)) & 7).
+__device__ __forceinline__ constexpr int tr_swz(int r) {
+  return ((r & 1) ? 5 : 0) ^ ((r & 2) ? 1 : 0) ^ ((r & 4) ? 7 : 0) ^ ((r & 8) ? 3 : 0) ^
+         ((r & 16) ? 6 : 0) ^ ((r & 64) ? 3 : 0);
+}
+
+template <int DK>
+struct TokTile {
+  static constexpr bool kSwz = DK == 128;
+  static constexpr int kPitch = kSwz ? DK : DK + 8;   // elements per row
+  // element offset of 8-byte half `h` of 16-byte unit u in row r, with the row's
+  // swizzle given separately (sw = tok_swz(r) or its split parts XORed)
+  __device__ static __forceinline__ int off(int r, int u, int sw, int h = 0) {
+    return r * kPitch + (kSwz ? ((u ^ sw) & 15) : u) * 8 + h * 4;
+  }
+  __device__ static __forceinline__ int swz(int r) { return kSwz ? tok_swz(r) : 0; }
+};
+constexpr int TRP = C;   // [channel | column][token] row pitch (elements)
+__device__ __forceinline__ int tr_off(int r, int u, int sw, int h = 0) {
+  return r * TRP + ((u ^ sw) & 7) * 8 + h * 4;
+}
+
 template <int DK>
 struct Buf {
-  static constexpr int PQ = DK + PADE;
+  static constexpr int PQ = TokTile<DK>::kPitch;
   unsigned short q[C * PQ];        // query operand  [token][channel]
   unsigned short k[C * PQ];        // key operand    [token][channel]
-  unsigned short kt[DK * PT];      // state keys     [channel][token]
-  unsigned short vt[DVT * PT];     // values         [column][token]
+  unsigned short kt[DK * TRP];     // state keys     [channel][token]
+  unsigned short vt[DVT * TRP];    // values         [column][token]
   unsigned short diag[4][4][16][16];  // exact diagonal partials [slice][sub-chunk][i][j]
   float w[7][DK];      // per-channel pair factors: 0-3 diagonal of sub-chunk p, 4 (2,0), 5 (3,1), 6 (3,0)
   float bq[4][DK];     // inter-term factor per query sub-chunk
@@ -71,6 +107,11 @@ struct Buf {
 __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+
+// Hides x's value from the optimiser at this point, so that addresses derived
+// from it are recomputed inside the chunk loop (1 VALU op per LDS access)
+// instead of being hoisted into dozens of live registers.
+__device__ __forceinline__ void launder(int& x) { asm volatile("" : "+v"(x)); }
 
 // consumer state-row map: accumulator tile rb, row m -> key channel
 __device__ __forceinline__ int srow(int rb, int m) {
@@ -201,23 +242,35 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     auto el = [&](const unsigned (&r)[NWR], int i) __attribute__((always_inline)) -> float {
       return (i & 1) ? __uint_as_float(r[i >> 1] & 0xffff0000u) : __uint_as_float(r[i >> 1] << 16);
     };
-    // this lane's slot for token a in a [token][channel] operand tile
+    // this lane's slot for token a in a [token][channel] operand tile: row 4tg+a,
+    // 16-byte unit (ch0 / 8) (DK = 128) or 8-byte half of unit ch0 / 8 (DK = 64)
+    int p_sw = TokTile<DK>::swz(4 * tg);
     auto slot = [&](unsigned short* tile, int a) __attribute__((always_inline)) -> unsigned short* {
-      return tile + (4 * tg + a) * PQ + ch0;
+      return tile + TokTile<DK>::off(4 * tg + a, ch0 >> 3, p_sw ^ TokTile<DK>::swz(a), (ch0 >> 2) & 1);
+    };
+    // [channel][token] slot of channel ch0 + i (kt) / column vc0 + c (vt), tokens 4tg..4tg+3
+    int kt_sw = tr_swz(ch0), vt_sw = tr_swz(vc0);
+    auto kt_slot = [&](unsigned short* tile, int i) __attribute__((always_inline)) -> unsigned short* {
+      return tile + tr_off(ch0 + i, tg >> 1, kt_sw ^ tr_swz(i), tg & 1);
+    };
+    auto vt_slot = [&](unsigned short* tile, int c) __attribute__((always_inline)) -> unsigned short* {
+      return tile + tr_off(vc0 + c, tg >> 1, vt_sw ^ tr_swz(c), tg & 1);
     };
 
     // produce chunk uc into B and start loading chunk un (a valid chunk index)
     auto produce = [&](BufT& B, int uc, int un) __attribute__((always_inline)) {
+      launder(p_sw);
+      launder(kt_sw);
+      launder(vt_sw);
       // V as [column][token]: pair tokens (a, a+1) of one column in one word
       {
-        unsigned* vt0 = reinterpret_cast<unsigned*>(B.vt);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int wi = c >> 1;
           const unsigned sel = (c & 1) ? 0x07060302u : 0x05040100u;
           const unsigned lo = __builtin_amdgcn_perm(rv[1][wi], rv[0][wi], sel);
           const unsigned hi = __builtin_amdgcn_perm(rv[3][wi], rv[2][wi], sel);
-          *reinterpret_cast<uint2*>(vt0 + ((vc0 + c) * PT + 4 * tg) / 2) = uint2{lo, hi};
+          *reinterpret_cast<uint2*>(vt_slot(B.vt, c)) = uint2{lo, hi};
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -273,7 +326,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         }
 #pragma unroll
         for (int i = 0; i < CPL; ++i)
-          store4<BF16>(B.kt + (ch0 + i) * PT + 4 * tg, kh[0][i], kh[1][i], kh[2][i], kh[3][i]);
+          store4<BF16>(kt_slot(B.kt, i), kh[0][i], kh[1][i], kh[2][i], kh[3][i]);
         if (tg == 15) {   // this lane's last token is the chunk's last row
 #pragma unroll
           for (int i = 0; i < CPL; ++i) {
@@ -412,7 +465,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         }
 #pragma unroll
         for (int i = 0; i < CPL; ++i)
-          store4<BF16>(B.kt + (ch0 + i) * PT + 4 * tg, kte[0][i], kte[1][i], kte[2][i], kte[3][i]);
+          store4<BF16>(kt_slot(B.kt, i), kte[0][i], kte[1][i], kte[2][i], kte[3][i]);
         if (lane == 0) B.flag[w] = 1 | (extw ? 2 : 0);
       }
     };
@@ -432,6 +485,10 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
   } else {
     // =========================== consumer waves ===========================
     const int cw = wave - 4;               // state / output columns [16cw, 16cw+16)
+    const int vrow = cw * 16 + m;          // this lane's row of the values tile
+    int vrow_sw = tr_swz(vrow);
+    int c_sw = TokTile<DK>::swz(m);        // rows 16p + m of the operand tiles
+    int ka_sw = tr_swz(srow(0, m));        // rows srow(rb, m) of the state-key tile
     unsigned short* og = reinterpret_cast<unsigned short*>(prm.o) + rowbase * DV + vcol0;
     f32x4 sacc[NRB];
 #pragma unroll
@@ -443,6 +500,9 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       }
     // one chunk of contractions; SAFE / EXT are compile-time so the body is branch-free
     auto consume = [&](const BufT& B, int u, auto safe_tag, auto ext_tag) __attribute__((always_inline)) {
+      launder(vrow_sw);
+      launder(c_sw);
+      launder(ka_sw);
       constexpr bool SAFE = decltype(safe_tag)::value;
       constexpr bool EXT = decltype(ext_tag)::value;
       // scaled copy of a query fragment by 8 per-channel factors
@@ -472,8 +532,10 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       Frag<BF16> va[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const unsigned short* vrow = B.vt + (cw * 16 + m) * PT + ks * 32 + gq * 4;
-        frag_ld4x2(va[ks], vrow, vrow + 16);
+        // tokens 32ks + 4gq .. +3 and the same 16 tokens later
+        const int u = 4 * ks + (gq >> 1);
+        frag_ld4x2(va[ks], B.vt + tr_off(vrow, u, vrow_sw, gq & 1),
+                   B.vt + tr_off(vrow, u + 2, vrow_sw, gq & 1));
       }
       Frag<BF16> kf[4][KS];   // key fragments of sub-chunk r, loaded when first needed
       f32x4 oacc[4];
@@ -482,8 +544,9 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         Frag<BF16> qf[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          frag_ld8(kf[p][ks], B.k + (16 * p + m) * PQ + ks * 32 + gq * 8);
-          frag_ld8(qf[ks], B.q + (16 * p + m) * PQ + ks * 32 + gq * 8);
+          const int o = TokTile<DK>::off(16 * p + m, 4 * ks + gq, c_sw ^ TokTile<DK>::swz(16 * p));
+          frag_ld8(kf[p][ks], B.k + o);
+          frag_ld8(qf[ks], B.q + o);
         }
         // scores P^T(r, p) = K_r Q_p^T, r <= p
         f32x4 pacc[4];
@@ -557,11 +620,11 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         Frag<BF16> vb;
-        frag_ld8(vb, B.vt + (cw * 16 + m) * PT + ks * 32 + gq * 8);
+        frag_ld8(vb, B.vt + tr_off(vrow, 4 * ks + gq, vrow_sw));
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
           Frag<BF16> ka;
-          frag_ld8(ka, B.kt + srow(rb, m) * PT + ks * 32 + gq * 8);
+          frag_ld8(ka, B.kt + tr_off(srow(rb, m), 4 * ks + gq, ka_sw ^ tr_swz(srow(rb, 0))));
           mma(sacc[rb], ka, vb);
         }
       }
