@@ -108,10 +108,19 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// N (4 or 8) consecutive floats to 16-byte aligned shared memory.
+template <int N>
+__device__ __forceinline__ void store_f32(float* p, const float* x) {
+  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  if constexpr (N == 8) *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
+
 // Hides x's value from the optimiser at this point, so that addresses derived
 // from it are recomputed inside the chunk loop (1 VALU op per LDS access)
 // instead of being hoisted into dozens of live registers.
 __device__ __forceinline__ void launder(int& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void launder(unsigned& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void launder(float& x) { asm volatile("" : "+v"(x)); }
 
 // consumer state-row map: accumulator tile rb, row m -> key channel
 __device__ __forceinline__ int srow(int rb, int m) {
@@ -257,8 +266,10 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       return tile + tr_off(vc0 + c, tg >> 1, vt_sw ^ tr_swz(c), tg & 1);
     };
 
-    // produce chunk uc into B and start loading chunk un (a valid chunk index)
-    auto produce = [&](BufT& B, int uc, int un) __attribute__((always_inline)) {
+    // which LDS buffers hold all-ones safe-path factors for this wave's slice
+    int ones = 0;
+    // produce chunk uc into B = bufs[bi] and start loading chunk un (a valid chunk index)
+    auto produce = [&](BufT& B, int bi, int un) __attribute__((always_inline)) {
       launder(p_sw);
       launder(kt_sw);
       launder(vt_sw);
@@ -275,26 +286,44 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       }
       __builtin_amdgcn_sched_barrier(0);
       load_v(un);
-      // log2 gates, floored at -256 so that an alpha = 0 gate cannot produce
-      // inf - inf (a chunk holding such a gate is never a fast one, so the floor
-      // only acts on the safe path); pp = inclusive prefix over this lane's 4
-      // tokens, inc = inclusive prefix over the chunk at this lane's last token
+      // log2 gates: pp = inclusive prefix over this lane's 4 tokens, inc =
+      // inclusive prefix over the chunk at this lane's last token (a 16-lane
+      // DPP scan of the lane totals).  Gates are <= 0, so |Gamma| is largest
+      // at the chunk's last row; the chunk is a fast one for this wave when
+      // every |Gamma| of its slice stays within 2^kFastLimit.  A -inf gate
+      // (alpha = 0) makes Gamma infinite and the chunk a safe one.
       float pp[4][CPL], inc[CPL];
-      bool big = false;
+      float mx = 0.f;
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
+        pp[0][i] = el(rg[0], i) * kLog2e;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const float y = fmaxf(el(rg[a], i) * kLog2e, -256.f);
-          pp[a][i] = a ? pp[a - 1][i] + y : y;
-        }
+        for (int a = 1; a < 4; ++a) pp[a][i] = fmaf(el(rg[a], i), kLog2e, pp[a - 1][i]);
         float x = pp[3][i];
         x += dpp<kRowShr1>(x);
         x += dpp<kRowShr2>(x);
         x += dpp<kRowShr4>(x);
         x += dpp<kRowShr8>(x);
         inc[i] = x;
-        big |= !(fabsf(x) <= kFastLimit);      // |Gamma| grows along the chunk
+        mx = fmaxf(mx, fabsf(x));
+      }
+      const bool fastw = __ballot(!(mx <= kFastLimit)) == 0ull;
+      if (!fastw) {
+        // the safe path works from gates floored at -256 (log2), so that an
+        // alpha = 0 gate cannot produce inf - inf (laundering keeps the
+        // compiler from speculating this rare work into the fast path)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int j = 0; j < NWR; ++j) launder(rg[a][j]);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const float y = fmaxf(el(rg[a], i) * kLog2e, -256.f);
+            pp[a][i] = a ? pp[a - 1][i] + y : y;
+          }
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       load_g(un);
@@ -305,45 +334,69 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       }
       __builtin_amdgcn_sched_barrier(0);
       load_qk(un);
-      const bool fastw = __ballot(big) == 0ull;
       if (fastw) {
         // ---- single pivot at the chunk start ----
-        float kh[4][CPL];
+        float ex[CPL];   // Gamma before this lane's first token
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) ex[i] = inc[i] - pp[3][i];
+        unsigned kw[4][NWR];   // packed key operand words, token a
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           unsigned xq[NWR], xk[NWR];
           lds_ld(xq, slot(B.q, a));
           lds_ld(xk, slot(B.k, a));
-          float qe[CPL];
+          float qe[CPL], ke[CPL];
 #pragma unroll
           for (int i = 0; i < CPL; ++i) {
-            const float gm = (inc[i] - pp[3][i]) + pp[a][i];   // Gamma of token 4tg+a
+            const float gm = ex[i] + pp[a][i];   // Gamma of token 4tg+a
             qe[i] = el(xq, i) * fast_exp2(gm);
-            kh[a][i] = el(xk, i) * fast_exp2(-gm);
+            ke[i] = el(xk, i) * fast_exp2(-gm);
           }
+#pragma unroll
+          for (int j = 0; j < NWR; ++j) kw[a][j] = pack_bf16x2(ke[2 * j], ke[2 * j + 1]);
           lds_store_n<BF16, CPL>(slot(B.q, a), qe);
-          lds_store_n<BF16, CPL>(slot(B.k, a), kh[a]);
+          st(slot(B.k, a), kw[a]);
         }
+        // state keys = the same bf16 values, [channel][token]: channel 2j (2j+1)
+        // is the low (high) half of word j of the four token rows
 #pragma unroll
-        for (int i = 0; i < CPL; ++i)
-          store4<BF16>(kt_slot(B.kt, i), kh[0][i], kh[1][i], kh[2][i], kh[3][i]);
-        if (tg == 15) {   // this lane's last token is the chunk's last row
+        for (int j = 0; j < NWR; ++j) {
 #pragma unroll
-          for (int i = 0; i < CPL; ++i) {
-            const int c = ch0 + i;
-            B.pre[c] = 1.f;
-            B.post[c] = fast_exp2(inc[i]);
-#pragma unroll
-            for (int p = 0; p < 4; ++p) B.bq[p][c] = 1.f;
-#pragma unroll
-            for (int e = 0; e < 7; ++e) B.w[e][c] = 1.f;
+          for (int hb = 0; hb < 2; ++hb) {
+            const unsigned sel = hb ? 0x07060302u : 0x05040100u;
+            const unsigned lo = __builtin_amdgcn_perm(kw[1][j], kw[0][j], sel);
+            const unsigned hi = __builtin_amdgcn_perm(kw[3][j], kw[2][j], sel);
+            *reinterpret_cast<uint2*>(kt_slot(B.kt, 2 * j + hb)) = uint2{lo, hi};
           }
         }
+        if (tg == 15) {   // this lane's last token is the chunk's last row
+          float e[CPL];
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) e[i] = fast_exp2(inc[i]);
+          store_f32<CPL>(&B.post[ch0], e);
+          // the safe-path factors of this slice are ones; they stay so in this
+          // buffer until a safe chunk overwrites them
+          if (!(ones & (1 << bi))) {
+            float one[CPL];
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) one[i] = 1.f;
+            store_f32<CPL>(&B.pre[ch0], one);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) store_f32<CPL>(&B.bq[p][ch0], one);
+#pragma unroll
+            for (int e2 = 0; e2 < 7; ++e2) store_f32<CPL>(&B.w[e2][ch0], one);
+          }
+        }
+        ones |= 1 << bi;
         if (lane == 0) B.flag[w] = 0;
       } else {
         // ---- 16-token sub-chunk pivots ----
         // loc = Gamma relative to the start of the token's sub-chunk, tot = the
         // sub-chunk's total: a 4-lane scan of the lane totals within each quad
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) launder(pp[a][i]);
         float loc[4][CPL], tot[CPL];
         bool ext = false;
 #pragma unroll
@@ -467,6 +520,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         for (int i = 0; i < CPL; ++i)
           store4<BF16>(kt_slot(B.kt, i), kte[0][i], kte[1][i], kte[2][i], kte[3][i]);
         if (lane == 0) B.flag[w] = 1 | (extw ? 2 : 0);
+        ones &= ~(1 << bi);
       }
     };
 
@@ -479,7 +533,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       load_qk(0);
     }
     for (int i = 0; i <= nch; ++i) {
-      if (i < nch) produce(bufs[i & 1], i, i + 1 < nch ? i + 1 : i);
+      if (i < nch) produce(bufs[i & 1], i & 1, i + 1 < nch ? i + 1 : i);
       barrier_lds();
     }
   } else {

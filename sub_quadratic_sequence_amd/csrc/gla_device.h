@@ -175,10 +175,11 @@ __device__ __forceinline__ void mma(f32x4& acc, const Frag<F32>& a, const Frag<F
 
 // ---------------------------------------------------------------- lane moves
 // DPP moves inside a row of 16 lanes.  Lanes whose source falls outside the
-// row read 0.
+// row read 0 (bound_ctrl), which lets the compiler fold the move into the
+// instruction that consumes it.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118,
               kRowShr12 = 0x11C;
