@@ -77,7 +77,15 @@ def read_traffic(name, src):
         return None
 
 
-def time_launches(fn, steps, warmup, torch):
+def time_launches(fn, steps, warmup, torch, preroll_s=0.0):
+    """Untimed: fn() repeated for preroll_s seconds (the GPU leaves its idle
+    clocks), then `warmup` calls.  Timed: exactly `steps` calls, bracketed by
+    device synchronisation, on the wall clock and with HIP events on the
+    current stream (the stream the kernels are launched on)."""
+    t_end = time.perf_counter() + preroll_s
+    while time.perf_counter() < t_end:
+        fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -105,8 +113,8 @@ def bench_forward(args, torch, gla, inputs):
     def step():
         gla.gla_chunk_fwd(q, k, v, g, out=o, final_state=sf)
 
-    log(f"[bench] forward: {args.warmup} warmup + {args.steps} timed steps")
-    wall, gpu = time_launches(step, args.steps, args.warmup, torch)
+    log(f"[bench] forward: {args.preroll:.1f} s pre-roll, {args.warmup} warmup + {args.steps} timed steps")
+    wall, gpu = time_launches(step, args.steps, args.warmup, torch, args.preroll)
     flops, nbytes = fwd_work(w.B, w.H, w.T, w.dk, w.dv, 64, 2)
     return dict(w=w, d=d, wall=wall, gpu=gpu, flops=flops, bytes=nbytes, tokens=w.B * w.T)
 
@@ -173,8 +181,11 @@ def cpu_baseline(fwd, min_seconds=12.0, max_passes=64):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--preroll", type=float, default=1.0,
+                    help="seconds of untimed calls before the warm-up steps, so that the GPU "
+                         "runs at its working clocks when timing starts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only", choices=["fwd", "decode", "copy", "pmc"], default=None,
@@ -202,7 +213,7 @@ def main():
         log("[bench] copy calibration: 5 x 512 MiB device-to-device copies done")
         if args.only == "copy":
             return
-        args.steps, args.warmup = 5, 1
+        args.steps, args.warmup, args.preroll = 5, 1, 0.0
         bench_forward(args, torch, gla, inputs)
         bench_decode(args, torch, gla, inputs)
         log("[bench] pmc launches done")
@@ -228,6 +239,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "preroll_s": args.preroll,
         "ms_per_step": fwd["wall"] * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
