@@ -22,8 +22,9 @@
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent) owned
- *     by the caller; the library keeps no pointer after the call returns,
- *     allocates no device memory and needs no workspace.
+ *     by the caller; the library keeps no pointer after the call returns and
+ *     allocates no device memory.  Only gla_chunk_fwd_ws takes a workspace,
+ *     which the caller allocates.
  *   - Layouts are row-major, last index fastest, densely packed, and every
  *     tensor pointer must be 16-byte aligned.
  *   - dtype selects the element type of q, k, v, g and o: GLA_BF16 (bfloat16)
@@ -43,6 +44,7 @@
 #ifndef GLA_H_
 #define GLA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -83,6 +85,46 @@ int gla_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                   const float* initial_state, void* o, float* final_state,
                   const int32_t* cu_seqlens, int num_seqs, int B, int H, int T,
                   int dk, int dv, int chunk_size, int dtype, void* stream);
+
+/*
+ * Device workspace, in bytes, that gla_chunk_fwd_ws needs for this shape; 0 when
+ * the call would not split its sequences (then the workspace may be NULL).
+ * Arguments as for gla_chunk_fwd (num_seqs > 0 means packed sequences, which
+ * are never split).  Invalid shapes give 0; gla_chunk_fwd_ws reports them.
+ */
+size_t gla_chunk_fwd_workspace_size(int num_seqs, int B, int H, int T, int dk, int dv,
+                                    int chunk_size, int dtype);
+
+/*
+ * gla_chunk_fwd with a sequence split for inputs whose (sequence, head, 64-column
+ * slice) work items do not fill the device: each sequence is cut into segments
+ * of whole 64-token chunks, at least 512 tokens long, so that there are about
+ * as many work items as compute units.  The recurrence is linear in the state
+ * with a diagonal transition, so over one segment S_end = diag(a) S_start +
+ * S_zero, with a = exp(sum of the segment's g) and S_zero the state reached
+ * from zero (page "Gated Linear Attention (GLA) ...", section "The Gated
+ * Recurrent Update", unrolled over the segment).  The call runs three kernels
+ * on the stream: S_zero and a for every segment in parallel; a scan over the
+ * segments giving every incoming state and the final states; the forward pass
+ * of every segment from its incoming state.  Results equal gla_chunk_fwd's up
+ * to rounding.
+ *
+ *   workspace       device buffer of at least gla_chunk_fwd_workspace_size(...)
+ *                   bytes, 256-byte aligned, owned by the caller; its contents
+ *                   are scratch, used until the call's kernels complete (the
+ *                   caller must not reuse it before that on another stream).
+ *                   May be NULL when that size is 0.
+ *   workspace_bytes its size.
+ *
+ * Other arguments, layouts and errors as for gla_chunk_fwd; a missing, small or
+ * misaligned workspace gives GLA_ERR_INVALID_ARG.  Packed sequences, fp32 and
+ * shapes that already fill the device run unsplit, exactly as gla_chunk_fwd.
+ */
+int gla_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* g,
+                     const float* initial_state, void* o, float* final_state,
+                     const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk,
+                     int dv, int chunk_size, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 /*
  * One recurrent decode step for N sequences x H heads, in place on the state.

@@ -507,7 +507,7 @@ static int launch(const ChunkParams& prm, int nblocks, hipStream_t stream) {
 
 int launch_chunk_fwd(const ChunkParams& prm, int dk, int dtype, int nblocks, hipStream_t stream) {
   // bf16: the pipelined producer/consumer kernel; fp32: the single-phase kernel above
-  if (dtype == 0) return launch_chunk_fwd_pipe(prm, dk, nblocks, stream);
+  if (dtype == 0) return launch_chunk_fwd_pipe(prm, dk, false, nblocks, stream);
   if (dtype == 1 && dk == 64) return launch<64, F32>(prm, nblocks, stream);
   return -2;
 }

@@ -129,9 +129,13 @@ __device__ __forceinline__ int srow(int rb, int m) {
 
 }  // namespace pipe
 
-template <int DK>
+// MODE kFull: the forward pass (outputs, and the final state of unsplit sequences).
+// MODE kStateOnly: the state a segment reaches from S = 0 and the segment's total
+// gate decay, for the sequence split (no queries read, no outputs written).
+template <int DK, int MODE>
 __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm) {
   using namespace pipe;
+  constexpr bool FULL = MODE == kFull;
   using BufT = Buf<DK>;
   constexpr int PQ = BufT::PQ;
   constexpr int CPL = DK / 16;   // producer: channels per lane
@@ -150,7 +154,8 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
   const int nblk = gridDim.x;
   const int bid = blockIdx.x;
   const int lin = prm.xcd_remap ? (bid & 7) * (nblk >> 3) + (bid >> 3) : bid;
-  const int unit = lin / prm.nvt, vt = lin - unit * prm.nvt;
+  const int item = lin / prm.nvt, vt = lin - item * prm.nvt;   // item = (unit, segment)
+  const int unit = item / prm.nseg, seg = item - unit * prm.nseg;
   const int n = unit / prm.H, h = unit - n * prm.H;
   long bos, eos, rowbase;
   if (prm.cu) {
@@ -158,14 +163,26 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     eos = prm.cu[n + 1];
     rowbase = (long)h * prm.T;
   } else {
-    bos = 0;
-    eos = prm.T;
+    bos = (long)seg * prm.seg_len;
+    eos = bos + prm.seg_len < prm.T ? bos + prm.seg_len : prm.T;
     rowbase = ((long)n * prm.H + h) * prm.T;
   }
   const int DV = prm.DV;
   const int vcol0 = vt * DVT;
-  const long sbase = (long)unit * DK * DV;
   const int nch = (int)((eos - bos + C - 1) / C);
+  // state in and out of this work item ([DK][DV] fp32, this slice's columns used)
+  const float* s_in;
+  float* s_out;
+  if constexpr (!FULL) {
+    s_in = nullptr;
+    s_out = prm.seg_state + (long)item * DK * DV;
+  } else if (prm.nseg > 1) {
+    s_in = prm.seg_state + (long)item * DK * DV;   // the segment's incoming state
+    s_out = nullptr;
+  } else {
+    s_in = prm.s0 ? prm.s0 + (long)unit * DK * DV : nullptr;
+    s_out = prm.sT ? prm.sT + (long)unit * DK * DV : nullptr;
+  }
 
   if (producer) {
     // =========================== producer waves ===========================
@@ -243,7 +260,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     auto load_qk = [&](int u) __attribute__((always_inline)) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        ld(rq[a], rs_q, qk_lane + (unsigned)(u * C + a) * DK * 2u);
+        if constexpr (FULL) ld(rq[a], rs_q, qk_lane + (unsigned)(u * C + a) * DK * 2u);
         ld(rk[a], rs_k, qk_lane + (unsigned)(u * C + a) * DK * 2u);
       }
     };
@@ -268,6 +285,11 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
 
     // which LDS buffers hold all-ones safe-path factors for this wave's slice
     int ones = 0;
+    // state-only pass: the segment's log2 gate total of this lane's channels (its
+    // tg == 15 lanes hold the chunk-last-row values)
+    float dsum[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) dsum[i] = 0.f;
     // produce chunk uc into B = bufs[bi] and start loading chunk un (a valid chunk index)
     auto produce = [&](BufT& B, int bi, int un) __attribute__((always_inline)) {
       launder(p_sw);
@@ -329,7 +351,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       load_g(un);
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        st(slot(B.q, a), rq[a]);
+        if constexpr (FULL) st(slot(B.q, a), rq[a]);
         st(slot(B.k, a), rk[a]);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -343,19 +365,21 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           unsigned xq[NWR], xk[NWR];
-          lds_ld(xq, slot(B.q, a));
+          if constexpr (FULL) lds_ld(xq, slot(B.q, a));
           lds_ld(xk, slot(B.k, a));
           float qe[CPL], ke[CPL];
 #pragma unroll
           for (int i = 0; i < CPL; ++i) {
             const float gm = ex[i] + pp[a][i];   // Gamma of token 4tg+a
-            qe[i] = el(xq, i) * fast_exp2(gm);
+            if constexpr (FULL) qe[i] = el(xq, i) * fast_exp2(gm);
             ke[i] = el(xk, i) * fast_exp2(-gm);
           }
 #pragma unroll
           for (int j = 0; j < NWR; ++j) kw[a][j] = pack_bf16x2(ke[2 * j], ke[2 * j + 1]);
-          lds_store_n<BF16, CPL>(slot(B.q, a), qe);
-          st(slot(B.k, a), kw[a]);
+          if constexpr (FULL) {
+            lds_store_n<BF16, CPL>(slot(B.q, a), qe);
+            st(slot(B.k, a), kw[a]);
+          }
         }
         // state keys = the same bf16 values, [channel][token]: channel 2j (2j+1)
         // is the low (high) half of word j of the four token rows
@@ -372,7 +396,10 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         if (tg == 15) {   // this lane's last token is the chunk's last row
           float e[CPL];
 #pragma unroll
-          for (int i = 0; i < CPL; ++i) e[i] = fast_exp2(inc[i]);
+          for (int i = 0; i < CPL; ++i) {
+            e[i] = fast_exp2(inc[i]);
+            if constexpr (!FULL) dsum[i] += inc[i];
+          }
           store_f32<CPL>(&B.post[ch0], e);
           // the safe-path factors of this slice are ones; they stay so in this
           // buffer until a safe chunk overwrites them
@@ -431,6 +458,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
             const float r4 = dpp<kRowRor4>(bn), r8 = dpp<kRowRor8>(bn), r12 = dpp<kRowRor12>(bn);
             b4[i] = sub == 3 ? bn : sub == 0 ? r4 : sub == 1 ? r8 : r12;
             fke[i] = fast_exp2(b4[i] - bn);   // 2^(Gamma_last - B_{p+1})
+            if constexpr (!FULL) dsum[i] += b4[i];
           }
           constexpr int NPL = CPL / 4;
           const int qd = tg & 3;
@@ -460,7 +488,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
             }
           }
         }
-        if (extw) {
+        if (FULL && extw) {
           // exact diagonal partials, one (row a, key pair jj) at a time: sum over this
           // lane's channels, then over the wave's four lane rows (its whole slice)
           unsigned sq[4][NWR], sk[4][NWR];
@@ -504,17 +532,19 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           unsigned xq[NWR], xk[NWR];
-          lds_ld(xq, slot(B.q, a));
+          if constexpr (FULL) lds_ld(xq, slot(B.q, a));
           lds_ld(xk, slot(B.k, a));
           float qh[CPL], kt[CPL];
 #pragma unroll
           for (int i = 0; i < CPL; ++i) {
-            qh[i] = el(xq, i) * fast_exp2(loc[a][i]);            // Q 2^(Gamma - B_p)
+            if constexpr (FULL) qh[i] = el(xq, i) * fast_exp2(loc[a][i]);   // Q 2^(Gamma - B_p)
             kt[i] = el(xk, i) * fast_exp2(tot[i] - loc[a][i]);   // K 2^(B_{p+1} - Gamma)
             kte[a][i] = kt[i] * fke[i];                          // K 2^(Gamma_last - Gamma)
           }
-          lds_store_n<BF16, CPL>(slot(B.q, a), qh);
-          lds_store_n<BF16, CPL>(slot(B.k, a), kt);
+          if constexpr (FULL) {
+            lds_store_n<BF16, CPL>(slot(B.q, a), qh);
+            lds_store_n<BF16, CPL>(slot(B.k, a), kt);
+          }
         }
 #pragma unroll
         for (int i = 0; i < CPL; ++i)
@@ -536,6 +566,17 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       if (i < nch) produce(bufs[i & 1], i & 1, i + 1 < nch ? i + 1 : i);
       barrier_lds();
     }
+    if constexpr (!FULL) {
+      // the segment's decay exp(sum of g) per key channel, once per (unit, segment)
+      if (vt == 0 && tg == 15) {
+        float e[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) e[i] = fast_exp2(dsum[i]);
+        float* dst = prm.seg_decay + (long)item * DK + ch0;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) dst[i] = e[i];
+      }
+    }
   } else {
     // =========================== consumer waves ===========================
     const int cw = wave - 4;               // state / output columns [16cw, 16cw+16)
@@ -550,7 +591,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int c = srow(rb, gq * 4 + s);
-        sacc[rb][s] = prm.s0 ? prm.s0[sbase + (long)c * DV + vcol0 + cw * 16 + m] : 0.f;
+        sacc[rb][s] = s_in ? s_in[(long)c * DV + vcol0 + cw * 16 + m] : 0.f;
       }
     // one chunk of contractions; SAFE / EXT are compile-time so the body is branch-free
     auto consume = [&](const BufT& B, int u, auto safe_tag, auto ext_tag) __attribute__((always_inline)) {
@@ -573,94 +614,96 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         frag_from_f32(o, x);
         return o;
       };
-      // S_prev as the inter term's A operand: slots = channels 32ks+8gq..+7 (see srow)
-      Frag<BF16> sa[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const float sv[8] = {sacc[2 * ks][0],     sacc[2 * ks][1],     sacc[2 * ks][2],
-                             sacc[2 * ks][3],     sacc[2 * ks + 1][0], sacc[2 * ks + 1][1],
-                             sacc[2 * ks + 1][2], sacc[2 * ks + 1][3]};
-        frag_from_f32(sa[ks], sv);
-      }
-      // V^T rows of this wave's columns, tokens in the score accumulators' order
-      Frag<BF16> va[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        // tokens 32ks + 4gq .. +3 and the same 16 tokens later
-        const int u = 4 * ks + (gq >> 1);
-        frag_ld4x2(va[ks], B.vt + tr_off(vrow, u, vrow_sw, gq & 1),
-                   B.vt + tr_off(vrow, u + 2, vrow_sw, gq & 1));
-      }
-      Frag<BF16> kf[4][KS];   // key fragments of sub-chunk r, loaded when first needed
-      f32x4 oacc[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        Frag<BF16> qf[KS];
+      if constexpr (FULL) {   // outputs of this chunk (the state-only pass has none)
+        // S_prev as the inter term's A operand: slots = channels 32ks+8gq..+7 (see srow)
+        Frag<BF16> sa[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const int o = TokTile<DK>::off(16 * p + m, 4 * ks + gq, c_sw ^ TokTile<DK>::swz(16 * p));
-          frag_ld8(kf[p][ks], B.k + o);
-          frag_ld8(qf[ks], B.q + o);
+          const float sv[8] = {sacc[2 * ks][0],     sacc[2 * ks][1],     sacc[2 * ks][2],
+                               sacc[2 * ks][3],     sacc[2 * ks + 1][0], sacc[2 * ks + 1][1],
+                               sacc[2 * ks + 1][2], sacc[2 * ks + 1][3]};
+          frag_from_f32(sa[ks], sv);
         }
-        // scores P^T(r, p) = K_r Q_p^T, r <= p
-        f32x4 pacc[4];
+        // V^T rows of this wave's columns, tokens in the score accumulators' order
+        Frag<BF16> va[2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pacc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < 2; ++ks) {
+          // tokens 32ks + 4gq .. +3 and the same 16 tokens later
+          const int u = 4 * ks + (gq >> 1);
+          frag_ld4x2(va[ks], B.vt + tr_off(vrow, u, vrow_sw, gq & 1),
+                     B.vt + tr_off(vrow, u + 2, vrow_sw, gq & 1));
+        }
+        Frag<BF16> kf[4][KS];   // key fragments of sub-chunk r, loaded when first needed
+        f32x4 oacc[4];
 #pragma unroll
-        for (int r = 0; r <= p; ++r) {
-          const int widx = (p == r) ? p : (p == 2 && r == 0) ? 4 : (p == 3 && r == 1) ? 5 : (p == 3 && r == 0) ? 6 : -1;
+        for (int p = 0; p < 4; ++p) {
+          Frag<BF16> qf[KS];
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            if (SAFE && widx >= 0) {
-              const Frag<BF16> b = scaled(qf[ks], B.w[widx], ks);
-              mma(pacc[r], kf[r][ks], b);
-            } else {
-              mma(pacc[r], kf[r][ks], qf[ks]);
+            const int o = TokTile<DK>::off(16 * p + m, 4 * ks + gq, c_sw ^ TokTile<DK>::swz(16 * p));
+            frag_ld8(kf[p][ks], B.k + o);
+            frag_ld8(qf[ks], B.q + o);
+          }
+          // scores P^T(r, p) = K_r Q_p^T, r <= p
+          f32x4 pacc[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pacc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int r = 0; r <= p; ++r) {
+            const int widx = (p == r) ? p : (p == 2 && r == 0) ? 4 : (p == 3 && r == 1) ? 5 : (p == 3 && r == 0) ? 6 : -1;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              if (SAFE && widx >= 0) {
+                const Frag<BF16> b = scaled(qf[ks], B.w[widx], ks);
+                mma(pacc[r], kf[r][ks], b);
+              } else {
+                mma(pacc[r], kf[r][ks], qf[ks]);
+              }
             }
           }
-        }
-        if constexpr (EXT) {
+          if constexpr (EXT) {
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const int j = gq * 4 + s;
-            float e = 0.f;
+            for (int s = 0; s < 4; ++s) {
+              const int j = gq * 4 + s;
+              float e = 0.f;
 #pragma unroll
-            for (int sl = 0; sl < 4; ++sl)
-              e += (B.flag[sl] & 2) ? bf16_bits_to_f32(B.diag[sl][p][m][j]) : 0.f;
-            pacc[p][s] += e;
+              for (int sl = 0; sl < 4; ++sl)
+                e += (B.flag[sl] & 2) ? bf16_bits_to_f32(B.diag[sl][p][m][j]) : 0.f;
+              pacc[p][s] += e;
+            }
           }
-        }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) pacc[p][s] = (gq * 4 + s > m) ? 0.f : pacc[p][s];  // causal
+          for (int s = 0; s < 4; ++s) pacc[p][s] = (gq * 4 + s > m) ? 0.f : pacc[p][s];  // causal
 
-        // O^T(p) = V^T P^T + S_prev^T (Q 2^Gamma)^T
-        f32x4 o1 = f32x4{0.f, 0.f, 0.f, 0.f}, o2 = f32x4{0.f, 0.f, 0.f, 0.f};
+          // O^T(p) = V^T P^T + S_prev^T (Q 2^Gamma)^T
+          f32x4 o1 = f32x4{0.f, 0.f, 0.f, 0.f}, o2 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; 2 * ks <= p; ++ks) {
-          const float pv[8] = {pacc[2 * ks][0],     pacc[2 * ks][1],     pacc[2 * ks][2],
-                               pacc[2 * ks][3],     pacc[2 * ks + 1][0], pacc[2 * ks + 1][1],
-                               pacc[2 * ks + 1][2], pacc[2 * ks + 1][3]};
-          Frag<BF16> pb;
-          frag_from_f32(pb, pv);
-          mma(o1, va[ks], pb);
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          if constexpr (SAFE) {
-            const Frag<BF16> b = scaled(qf[ks], B.bq[p], ks);
-            mma(o2, sa[ks], b);
-          } else {
-            mma(o2, sa[ks], qf[ks]);
+          for (int ks = 0; 2 * ks <= p; ++ks) {
+            const float pv[8] = {pacc[2 * ks][0],     pacc[2 * ks][1],     pacc[2 * ks][2],
+                                 pacc[2 * ks][3],     pacc[2 * ks + 1][0], pacc[2 * ks + 1][1],
+                                 pacc[2 * ks + 1][2], pacc[2 * ks + 1][3]};
+            Frag<BF16> pb;
+            frag_from_f32(pb, pv);
+            mma(o1, va[ks], pb);
           }
-        }
-        oacc[p] = o1 + o2;
-      }
-      const long t0 = bos + (long)u * C;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const long t = t0 + 16 * p + m;
-        if (t < eos)
-          store4<BF16>(og + t * DV + cw * 16 + gq * 4, oacc[p][0], oacc[p][1], oacc[p][2], oacc[p][3]);
+          for (int ks = 0; ks < KS; ++ks) {
+            if constexpr (SAFE) {
+              const Frag<BF16> b = scaled(qf[ks], B.bq[p], ks);
+              mma(o2, sa[ks], b);
+            } else {
+              mma(o2, sa[ks], qf[ks]);
+            }
+          }
+          oacc[p] = o1 + o2;
+        }
+        const long t0 = bos + (long)u * C;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const long t = t0 + 16 * p + m;
+          if (t < eos)
+            store4<BF16>(og + t * DV + cw * 16 + gq * 4, oacc[p][0], oacc[p][1], oacc[p][2], oacc[p][3]);
+        }
       }
 
       // ---- state: S <- post * (pre * S + KT^T V) ----
@@ -704,23 +747,28 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       }
       barrier_lds();
     }
-    if (prm.sT) {
+    if (s_out) {
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const int c = srow(rb, gq * 4 + s);
-          prm.sT[sbase + (long)c * DV + vcol0 + cw * 16 + m] = sacc[rb][s];
+          s_out[(long)c * DV + vcol0 + cw * 16 + m] = sacc[rb][s];
         }
     }
   }
 }
 
-int launch_chunk_fwd_pipe(const ChunkParams& prm, int dk, int nblocks, hipStream_t stream) {
-  if (dk == 128) {
-    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<128>), dim3(nblocks), dim3(512), 0, stream, prm);
+int launch_chunk_fwd_pipe(const ChunkParams& prm, int dk, bool state_only, int nblocks,
+                          hipStream_t stream) {
+  if (dk == 128 && !state_only) {
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<128, kFull>), dim3(nblocks), dim3(512), 0, stream, prm);
+  } else if (dk == 128) {
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<128, kStateOnly>), dim3(nblocks), dim3(512), 0, stream, prm);
+  } else if (dk == 64 && !state_only) {
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<64, kFull>), dim3(nblocks), dim3(512), 0, stream, prm);
   } else if (dk == 64) {
-    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<64>), dim3(nblocks), dim3(512), 0, stream, prm);
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<64, kStateOnly>), dim3(nblocks), dim3(512), 0, stream, prm);
   } else {
     return -2;
   }

@@ -44,51 +44,57 @@ const char* gla_status_string(int status) {
 
 const char* gla_last_error(void) { return g_last_error; }
 
-int gla_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
-                  const float* initial_state, void* o, float* final_state,
-                  const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk,
-                  int dv, int chunk_size, int dtype, void* stream) {
-  g_last_error[0] = '\0';
+}  // extern "C"
+
+namespace {
+
+// Host-side validation shared by the forward entry points; fills prm (unsplit)
+// and the launch shape.  Returns GLA_OK, or an error status with the message set.
+int check_chunk_args(const char* fn, const void* q, const void* k, const void* v, const void* g,
+                     const float* initial_state, void* o, float* final_state,
+                     const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk, int dv,
+                     int chunk_size, int dtype, gla::ChunkParams& prm, long long& units,
+                     bool& nothing_to_do) {
+  nothing_to_do = false;
   if (dtype != GLA_BF16 && dtype != GLA_F32)
-    return fail(GLA_ERR_INVALID_ARG, "gla_chunk_fwd: dtype %d is not GLA_BF16 or GLA_F32", dtype);
+    return fail(GLA_ERR_INVALID_ARG, "%s: dtype %d is not GLA_BF16 or GLA_F32", fn, dtype);
   if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0)
-    return fail(GLA_ERR_INVALID_ARG, "gla_chunk_fwd: B=%d H=%d T=%d dk=%d dv=%d must be positive (T >= 0)",
+    return fail(GLA_ERR_INVALID_ARG, "%s: B=%d H=%d T=%d dk=%d dv=%d must be positive (T >= 0)", fn,
                 B, H, T, dk, dv);
   if (chunk_size != 64)
-    return fail(GLA_ERR_UNSUPPORTED, "gla_chunk_fwd: chunk_size %d (only 64 is implemented)", chunk_size);
+    return fail(GLA_ERR_UNSUPPORTED, "%s: chunk_size %d (only 64 is implemented)", fn, chunk_size);
   if (dtype == GLA_BF16 ? (dk != 64 && dk != 128) : dk != 64)
-    return fail(GLA_ERR_UNSUPPORTED, "gla_chunk_fwd: dk=%d is not implemented for %s", dk,
+    return fail(GLA_ERR_UNSUPPORTED, "%s: dk=%d is not implemented for %s", fn, dk,
                 dtype == GLA_BF16 ? "GLA_BF16 (64 or 128)" : "GLA_F32 (64)");
   if (dv % 64 != 0 || dv > 512)
-    return fail(GLA_ERR_UNSUPPORTED, "gla_chunk_fwd: dv=%d must be a multiple of 64 up to 512", dv);
+    return fail(GLA_ERR_UNSUPPORTED, "%s: dv=%d must be a multiple of 64 up to 512", fn, dv);
   int nseq = B;
   if (cu_seqlens) {
     if (B != 1)
-      return fail(GLA_ERR_INVALID_ARG, "gla_chunk_fwd: packed sequences (cu_seqlens) need B == 1, got %d", B);
+      return fail(GLA_ERR_INVALID_ARG, "%s: packed sequences (cu_seqlens) need B == 1, got %d", fn, B);
     if (num_seqs <= 0)
-      return fail(GLA_ERR_INVALID_ARG, "gla_chunk_fwd: num_seqs=%d must be positive with cu_seqlens",
+      return fail(GLA_ERR_INVALID_ARG, "%s: num_seqs=%d must be positive with cu_seqlens", fn,
                   num_seqs);
     nseq = num_seqs;
   }
   if (!fits_i32((long long)B * H * T) || !fits_i32((long long)B * H * T * dv) ||
       !fits_i32((long long)B * H * T * dk) || !fits_i32((long long)nseq * H * dk * dv))
-    return fail(GLA_ERR_INVALID_ARG, "gla_chunk_fwd: tensor sizes exceed int32 indexing");
+    return fail(GLA_ERR_INVALID_ARG, "%s: tensor sizes exceed int32 indexing", fn);
   const bool any_tokens = (long long)B * H * T > 0;
   if (any_tokens && (!q || !k || !v || !g || !o))
-    return fail(GLA_ERR_INVALID_ARG, "gla_chunk_fwd: q, k, v, g and o must be non-null");
+    return fail(GLA_ERR_INVALID_ARG, "%s: q, k, v, g and o must be non-null", fn);
   const void* ptrs[] = {q, k, v, g, o, initial_state, final_state, cu_seqlens};
   const char* names[] = {"q", "k", "v", "g", "o", "initial_state", "final_state", "cu_seqlens"};
   for (int i = 0; i < 8; ++i)
     if (ptrs[i] && !aligned16(ptrs[i]))
-      return fail(GLA_ERR_INVALID_ARG, "gla_chunk_fwd: %s is not 16-byte aligned", names[i]);
-  const long long units = (long long)nseq * H;
+      return fail(GLA_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, names[i]);
+  units = (long long)nseq * H;
   const int nvt = dv / 64;
   const long long nblocks = units * nvt;
   if (!fits_i32(nblocks) || nblocks == 0)
-    return fail(GLA_ERR_INVALID_ARG, "gla_chunk_fwd: %lld work items", nblocks);
-  if (!any_tokens && !final_state) return GLA_OK;  // nothing to compute or write
+    return fail(GLA_ERR_INVALID_ARG, "%s: %lld work items", fn, nblocks);
+  if (!any_tokens && !final_state) nothing_to_do = true;
 
-  gla::ChunkParams prm;
   prm.q = q;
   prm.k = k;
   prm.v = v;
@@ -102,13 +108,140 @@ int gla_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
   prm.DV = dv;
   prm.nvt = nvt;
   prm.xcd_remap = (nblocks % 8 == 0) ? 1 : 0;
-  const int rc = gla::launch_chunk_fwd(prm, dk, dtype, (int)nblocks,
-                                       reinterpret_cast<hipStream_t>(stream));
-  if (rc == -2) return fail(GLA_ERR_UNSUPPORTED, "gla_chunk_fwd: no kernel for dk=%d dtype=%d", dk, dtype);
-  if (rc != 0)
-    return fail(GLA_ERR_LAUNCH, "gla_chunk_fwd: kernel launch failed: %s",
-                hipGetErrorString(hipGetLastError()));
+  prm.nseg = 1;
+  prm.seg_len = T;
+  prm.seg_state = nullptr;
+  prm.seg_decay = nullptr;
   return GLA_OK;
+}
+
+int launch_status(const char* fn, int rc, int dk, int dtype) {
+  if (rc == -2) return fail(GLA_ERR_UNSUPPORTED, "%s: no kernel for dk=%d dtype=%d", fn, dk, dtype);
+  if (rc != 0)
+    return fail(GLA_ERR_LAUNCH, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+  return GLA_OK;
+}
+
+// Compute units of the current device (256 on MI355X; that value if no device answers).
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+// Sequence split: fixed-length bf16 inputs whose work items do not fill the
+// device are cut into segments of at least kMinSegChunks chunks, about enough to
+// give every compute unit one work item.  Returns the segment count (1 = none)
+// and the segment length in tokens.
+constexpr int kMinSegChunks = 8;
+
+int split_plan(bool varlen, int dtype, long long items, int T, int& seg_len) {
+  seg_len = T;
+  if (varlen || dtype != GLA_BF16 || T <= 0) return 1;
+  const int ncu = device_cus();
+  if (items >= ncu) return 1;
+  const int nch = (T + 63) / 64;
+  long long want = (ncu + items - 1) / items;
+  const long long by_len = nch / kMinSegChunks;
+  long long nseg = want < by_len ? want : by_len;
+  if (nseg < 2) return 1;
+  const int seg_chunks = (int)((nch + nseg - 1) / nseg);
+  seg_len = seg_chunks * 64;
+  return (T + seg_len - 1) / seg_len;
+}
+
+size_t split_bytes(long long units, int nseg, int dk, int dv) {
+  const size_t st = (size_t)units * nseg * dk * dv * sizeof(float);
+  const size_t dec = (size_t)units * nseg * dk * sizeof(float);
+  return ((st + 255) / 256) * 256 + ((dec + 255) / 256) * 256;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gla_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
+                  const float* initial_state, void* o, float* final_state,
+                  const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk,
+                  int dv, int chunk_size, int dtype, void* stream) {
+  g_last_error[0] = '\0';
+  gla::ChunkParams prm;
+  long long units = 0;
+  bool nothing = false;
+  const int st = check_chunk_args("gla_chunk_fwd", q, k, v, g, initial_state, o, final_state,
+                                  cu_seqlens, num_seqs, B, H, T, dk, dv, chunk_size, dtype, prm,
+                                  units, nothing);
+  if (st != GLA_OK || nothing) return st;
+  const int rc = gla::launch_chunk_fwd(prm, dk, dtype, (int)(units * prm.nvt),
+                                       reinterpret_cast<hipStream_t>(stream));
+  return launch_status("gla_chunk_fwd", rc, dk, dtype);
+}
+
+size_t gla_chunk_fwd_workspace_size(int num_seqs, int B, int H, int T, int dk, int dv,
+                                    int chunk_size, int dtype) {
+  if (B <= 0 || H <= 0 || T <= 0 || dk <= 0 || dv <= 0 || chunk_size != 64) return 0;
+  if (dv % 64 != 0) return 0;
+  const long long units = (long long)B * H;
+  int seg_len = 0;
+  const int nseg = split_plan(num_seqs > 0, dtype, units * (dv / 64), T, seg_len);
+  return nseg > 1 ? split_bytes(units, nseg, dk, dv) : 0;
+}
+
+int gla_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* g,
+                     const float* initial_state, void* o, float* final_state,
+                     const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk,
+                     int dv, int chunk_size, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  gla::ChunkParams prm;
+  long long units = 0;
+  bool nothing = false;
+  const int st = check_chunk_args("gla_chunk_fwd_ws", q, k, v, g, initial_state, o, final_state,
+                                  cu_seqlens, num_seqs, B, H, T, dk, dv, chunk_size, dtype, prm,
+                                  units, nothing);
+  if (st != GLA_OK || nothing) return st;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int seg_len = T;
+  const int nseg = split_plan(cu_seqlens != nullptr, dtype, units * prm.nvt, T, seg_len);
+  if (nseg == 1) {
+    const int rc = gla::launch_chunk_fwd(prm, dk, dtype, (int)(units * prm.nvt), s);
+    return launch_status("gla_chunk_fwd_ws", rc, dk, dtype);
+  }
+  const size_t need = split_bytes(units, nseg, dk, dv);
+  if (!workspace || workspace_bytes < need)
+    return fail(GLA_ERR_INVALID_ARG, "gla_chunk_fwd_ws: workspace of %zu bytes given, %zu needed",
+                workspace ? workspace_bytes : (size_t)0, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(GLA_ERR_INVALID_ARG, "gla_chunk_fwd_ws: workspace is not 256-byte aligned");
+  const long long nblocks = units * nseg * prm.nvt;
+  if (!fits_i32(nblocks))
+    return fail(GLA_ERR_INVALID_ARG, "gla_chunk_fwd_ws: %lld work items", nblocks);
+  char* ws = static_cast<char*>(workspace);
+  const size_t st_bytes = ((size_t)units * nseg * dk * dv * sizeof(float) + 255) / 256 * 256;
+  prm.nseg = nseg;
+  prm.seg_len = seg_len;
+  prm.seg_state = reinterpret_cast<float*>(ws);
+  prm.seg_decay = reinterpret_cast<float*>(ws + st_bytes);
+  prm.xcd_remap = (nblocks % 8 == 0) ? 1 : 0;
+  // 1. each segment's state from zero and its total decay
+  int rc = gla::launch_chunk_fwd_pipe(prm, dk, true, (int)nblocks, s);
+  if (rc != 0) return launch_status("gla_chunk_fwd_ws", rc, dk, dtype);
+  // 2. incoming state of every segment, and the final states
+  gla::SegScanParams sp;
+  sp.s0 = initial_state;
+  sp.sT = final_state;
+  sp.seg_state = prm.seg_state;
+  sp.seg_decay = prm.seg_decay;
+  sp.dk = dk;
+  sp.dv = dv;
+  sp.nseg = nseg;
+  rc = gla::launch_seg_scan(sp, (int)units, s);
+  if (rc != 0) return launch_status("gla_chunk_fwd_ws", rc, dk, dtype);
+  // 3. the forward pass of every segment from its incoming state
+  rc = gla::launch_chunk_fwd_pipe(prm, dk, false, (int)nblocks, s);
+  return launch_status("gla_chunk_fwd_ws", rc, dk, dtype);
 }
 
 int gla_recurrent_step(const void* q, const void* k, const void* v, const void* g, float* state,

@@ -20,6 +20,26 @@ struct ChunkParams {
   int DV;
   int nvt;           // DV / 64 column slices
   int xcd_remap;     // 1: consecutive work items share an XCD (grid size % 8 == 0)
+  // Sequence split (fixed-length inputs only; nseg = 1 and seg_len = T otherwise):
+  // each sequence is cut into nseg segments of seg_len tokens (a multiple of 64,
+  // the last one shorter), and a work item is one (sequence, head, segment, slice).
+  int nseg;
+  int seg_len;
+  float* seg_state;  // [units][nseg][dk][dv] fp32: a segment's state from zero, then its incoming state
+  float* seg_decay;  // [units][nseg][dk] fp32: exp of the segment's summed log-gates
+};
+
+// Kernel modes of the pipelined forward.
+constexpr int kFull = 0;       // outputs (and the final state of unsplit sequences)
+constexpr int kStateOnly = 1;  // a segment's state from zero and its total decay
+
+// Arguments of the segment scan of the sequence split.
+struct SegScanParams {
+  const float* s0;   // [units][dk][dv] or null (zeros)
+  float* sT;         // [units][dk][dv] or null; may alias s0
+  float* seg_state;  // in: states from zero; out: incoming states
+  const float* seg_decay;
+  int dk, dv, nseg;
 };
 
 // Arguments of the decode step kernel.
@@ -35,7 +55,9 @@ struct StepParams {
 // Each returns 0 on success, -1 if the launch failed, -2 if no kernel exists
 // for the shape/dtype.
 int launch_chunk_fwd(const ChunkParams& prm, int dk, int dtype, int nblocks, hipStream_t stream);
-int launch_chunk_fwd_pipe(const ChunkParams& prm, int dk, int nblocks, hipStream_t stream);
+int launch_chunk_fwd_pipe(const ChunkParams& prm, int dk, bool state_only, int nblocks,
+                          hipStream_t stream);
+int launch_seg_scan(const SegScanParams& prm, int units, hipStream_t stream);
 int launch_recurrent_step(const StepParams& prm, int units, int dk, int dv, int dtype,
                           hipStream_t stream);
 

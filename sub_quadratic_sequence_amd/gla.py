@@ -39,6 +39,11 @@ def load_library():
         P, I = ctypes.c_void_p, ctypes.c_int
         lib.gla_chunk_fwd.restype = I
         lib.gla_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P]
+        lib.gla_chunk_fwd_workspace_size.restype = ctypes.c_size_t
+        lib.gla_chunk_fwd_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
+        lib.gla_chunk_fwd_ws.restype = I
+        lib.gla_chunk_fwd_ws.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P,
+                                         ctypes.c_size_t, P]
         lib.gla_recurrent_step.restype = I
         lib.gla_recurrent_step.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
         lib.gla_status_string.restype = ctypes.c_char_p
@@ -82,15 +87,30 @@ def _check_gpu(name, t, dtype=None, shape=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+def workspace_size(q, v, cu_seqlens=None, chunk_size: int = 64) -> int:
+    """Bytes of workspace the sequence-split forward needs for these inputs (0: none)."""
+    B, H, T, dk = q.shape
+    num_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    return int(load_library().gla_chunk_fwd_workspace_size(num_seqs, B, H, T, dk, v.shape[-1],
+                                                           int(chunk_size), _dtype_code(q)))
+
+
 def gla_chunk_fwd(q, k, v, g, initial_state=None, output_final_state=False, cu_seqlens=None,
-                  chunk_size: int = 64, out=None, final_state=None):
-    """Chunkwise GLA forward (C entry point ``gla_chunk_fwd``).
+                  chunk_size: int = 64, out=None, final_state=None, split: bool = True,
+                  workspace=None):
+    """Chunkwise GLA forward.
 
     q, k, g: [B, H, T, dk]; v: [B, H, T, dv] (bfloat16 or float32, same dtype);
     initial_state: [Nseq, H, dk, dv] float32 or None; cu_seqlens: int32 [Nseq+1]
     on the GPU for packed sequences (B == 1).  Returns ``(o, final_state)``;
     ``final_state`` is None unless ``output_final_state`` (or ``final_state``
     is passed, which may alias ``initial_state``).
+
+    With ``split`` (the default) the call goes through ``gla_chunk_fwd_ws``,
+    which cuts long sequences into segments when the inputs have too few
+    (sequence, head) units to fill the device; the workspace it needs is a
+    torch allocation (or ``workspace``, a uint8 GPU tensor).  ``split=False``
+    calls ``gla_chunk_fwd``, which never splits.
     """
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -118,9 +138,22 @@ def gla_chunk_fwd(q, k, v, g, initial_state=None, output_final_state=False, cu_s
     lib = load_library()
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        rc = lib.gla_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(initial_state), _ptr(out),
-                               _ptr(final_state), _ptr(cu_seqlens), num_seqs, B, H, T, dk, dv,
-                               int(chunk_size), _dtype_code(q), ctypes.c_void_p(stream))
+        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(initial_state), _ptr(out),
+                _ptr(final_state), _ptr(cu_seqlens), num_seqs, B, H, T, dk, dv, int(chunk_size),
+                _dtype_code(q))
+        if split:
+            need = workspace_size(q, v, cu_seqlens, chunk_size)
+            if need and workspace is None:
+                workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+            ws_ptr, ws_bytes = None, 0
+            if workspace is not None:
+                _check_gpu("workspace", workspace, torch.uint8)
+                base = workspace.data_ptr()
+                off = (-base) % 256
+                ws_ptr, ws_bytes = ctypes.c_void_p(base + off), max(0, workspace.numel() - off)
+            rc = lib.gla_chunk_fwd_ws(*args, ws_ptr, ws_bytes, ctypes.c_void_p(stream))
+        else:
+            rc = lib.gla_chunk_fwd(*args, ctypes.c_void_p(stream))
     if rc != GLA_OK:
         raise GLAError(rc, last_error())
     return out, final_state

@@ -31,7 +31,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    assert names == ["gla_chunk_fwd", "gla_last_error", "gla_recurrent_step", "gla_status_string"]
+    assert names == ["gla_chunk_fwd", "gla_chunk_fwd_workspace_size", "gla_chunk_fwd_ws",
+                     "gla_last_error", "gla_recurrent_step", "gla_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -128,3 +129,28 @@ def test_binding_refuses_cpu_tensors():
         gla.gla_chunk_fwd(x, x, x, x)
     with pytest.raises(ValueError, match="GPU"):
         gla.gla_recurrent_step(x[0], x[0], x[0], x[0], torch.zeros(1, 64, 64, 64))
+
+
+def test_workspace_size_only_for_few_long_fixed_length_sequences(lib):
+    # long context, 16 units x 2 slices: split; training shape (256 work items),
+    # packed sequences and fp32: no split
+    assert lib.gla_chunk_fwd_workspace_size(0, 1, 16, 65536, 128, 128, 64, 0) > 0
+    assert lib.gla_chunk_fwd_workspace_size(0, 8, 16, 2048, 128, 128, 64, 0) == 0
+    assert lib.gla_chunk_fwd_workspace_size(16, 1, 16, 33000, 128, 256, 64, 0) == 0
+    assert lib.gla_chunk_fwd_workspace_size(0, 1, 16, 65536, 64, 64, 64, 1) == 0
+    assert lib.gla_chunk_fwd_workspace_size(0, 1, 16, 600, 128, 128, 64, 0) == 0   # too short
+
+
+@pytest.mark.parametrize("ws,nbytes,needle", [
+    (None, 0, "workspace of 0 bytes"),
+    (FAKE, 1024, "needed"),
+    (FAKE + 16, 1 << 30, "256-byte aligned"),
+])
+def test_chunk_fwd_ws_rejects_workspace(lib, ws, nbytes, needle):
+    from sub_quadratic_sequence_amd import gla
+
+    P = ctypes.c_void_p
+    rc = lib.gla_chunk_fwd_ws(P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, P(FAKE), None, None, 0,
+                              1, 16, 65536, 128, 128, 64, 0, P(ws) if ws else None, nbytes, None)
+    assert rc == 1
+    assert needle in gla.last_error()

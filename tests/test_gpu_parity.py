@@ -323,3 +323,66 @@ def test_nan_propagates(dev):
     assert torch.isfinite(o[0, 1, :, [0, 1, 2, 4]]).all()
     assert torch.isnan(o[0, 1, 70:, 3]).all()
     assert torch.isnan(sf[0, 1]).any() and torch.isfinite(sf[0, 0]).all()
+
+
+# ------------------------------------------------------------------ sequence split
+SPLIT_CASES = [
+    # (label, B, H, T, dk, dv, gate, s0)
+    ("weak_s0_T5000", 1, 2, 5000, 128, 128, "weak", True),
+    ("strong_dv256_T3000", 1, 2, 3000, 128, 256, "strong", True),
+    ("dk64_T2500", 2, 1, 2500, 64, 64, "weak", True),
+    ("ragged_T1025", 1, 1, 1025, 128, 128, "weak", False),
+]
+
+
+@pytest.mark.parametrize("label,B,H,T,dk,dv,gate,s0", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_sequence_split_matches_oracle(dev, label, B, H, T, dk, dv, gate, s0):
+    """Few units and long sequences: gla_chunk_fwd_ws cuts the sequences into
+    segments (state pass, segment scan, forward from the incoming states).  The
+    result matches the oracle and the unsplit call."""
+    from sub_quadratic_sequence_amd import gla
+
+    w = I.ChunkWorkload("split", B=B, H=H, T=T, dk=dk, dv=dv, dtype="bf16", seed=31)
+    say(f"sequence split {label}: B={B} H={H} T={T} dk={dk} dv={dv} gate={gate} s0={s0}")
+    d = I.chunk_inputs(w, gate=gate, s0=s0)
+    args = [d[n].to(dev) for n in "qkvg"]
+    assert gla.workspace_size(args[0], args[2]) > 0   # the split is taken
+    s0_dev = None if d["s0"] is None else d["s0"].to(dev)
+    o, sf = gla.gla_chunk_fwd(*args, initial_state=s0_dev, output_final_state=True)
+    o1, s1 = gla.gla_chunk_fwd(*args, initial_state=s0_dev, output_final_state=True, split=False)
+    torch.cuda.synchronize()
+    _check_fixed(d, o, sf, d["s0"], TOL_BF16, f"split {label}")
+    assert unit_err_fixed(o.float(), o1.float()) <= TOL_BF16
+    assert unit_err_fixed(sf, s1) <= TOL_BF16
+
+
+def test_sequence_split_extreme_gates(dev):
+    """alpha = 0 tokens and 16-token decays beyond 2^100 inside split segments:
+    a segment's total decay underflows to zero and its state restarts."""
+    w = I.ChunkWorkload("split_extreme", B=1, H=2, T=2100, dk=128, dv=128, dtype="bf16", seed=37,
+                        k_scaled=True)
+    say("sequence split, extreme gates: B=1 H=2 T=2100, g down to -80 and -inf")
+    d = I.chunk_inputs(w, s0=True)
+    gen = torch.Generator().manual_seed(41)
+    g = d["g"].float()
+    mask = torch.rand(g.shape, generator=gen) < 0.05
+    g = torch.where(mask, -80.0 * torch.rand(g.shape, generator=gen), g)
+    g[0, 1, 900, :] = float("-inf")
+    g[0, 0, 1500:1510, 3] = float("-inf")
+    d["g"] = g.to(torch.bfloat16)
+    o, sf = _fwd(dev, d, s0=d["s0"])
+    _check_fixed(d, o, sf, d["s0"], TOL_BF16, "split extreme")
+
+
+def test_sequence_split_in_place_and_deterministic(dev):
+    from sub_quadratic_sequence_amd import gla
+
+    say("sequence split: final_state aliasing initial_state, and two identical calls")
+    d = I.chunk_inputs(I.LONG_BF16, B=1, H=2, T=4100, s0=True)
+    args = [d[n].to(dev) for n in "qkvg"]
+    s0 = d["s0"].to(dev)
+    o1, s1 = gla.gla_chunk_fwd(*args, initial_state=s0.clone(), output_final_state=True)
+    st = s0.clone()
+    o2, _ = gla.gla_chunk_fwd(*args, initial_state=st, final_state=st)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, st)
