@@ -148,8 +148,49 @@ def bench_decode(args, torch, gla, inputs):
         evs.append((e0, e1))
     torch.cuda.synchronize()
     cold = sum(a.elapsed_time(b) for a, b in evs) / 1e3 / w.steps
+    # reference for a read-modify-write stream of the state's size: a device copy of
+    # the same number of bytes (read once, written once), after the same eviction
+    src = torch.empty_like(st)
+    cps = []
+    for t in range(8):
+        flush.fill_(t & 0xFF)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        st.copy_(src)
+        e1.record()
+        cps.append((e0, e1))
+    torch.cuda.synchronize()
+    copy_t = sum(a.elapsed_time(b) for a, b in cps) / 1e3 / len(cps)
+    copy_gbs = 2 * st.numel() * 4 / copy_t / 1e9
+    del src, flush
     flops, nbytes = decode_work(w.N, w.H, w.dk, w.dv, 2)
-    return dict(w=w, wall=wall, gpu=gpu, cold=cold, flops=flops, bytes=nbytes)
+    return dict(w=w, wall=wall, gpu=gpu, cold=cold, flops=flops, bytes=nbytes, copy_gbs=copy_gbs)
+
+
+def bench_long(args, torch, gla, inputs):
+    """The long-context workload (B1 H16 T65536 d128, initial state): 32 work
+    items for the whole device unless the sequences are split into segments
+    (gla_chunk_fwd_ws), so both paths are timed."""
+    w = inputs.LONG_BF16
+    log(f"[bench] long context {w.name}: generating inputs")
+    d = inputs.chunk_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, g = (d[n].to(dev) for n in "qkvg")
+    s0 = d["s0"].to(dev)
+    o = torch.empty(w.B, w.H, w.T, w.dv, dtype=torch.bfloat16, device=dev)
+    sf = torch.empty(w.B, w.H, w.dk, w.dv, dtype=torch.float32, device=dev)
+    ws = torch.empty(gla.workspace_size(q, v) + 256, dtype=torch.uint8, device=dev)
+    res = {}
+    for split in (True, False):
+        def step():
+            gla.gla_chunk_fwd(q, k, v, g, initial_state=s0, out=o, final_state=sf, split=split,
+                              workspace=ws)
+        _, t = time_launches(step, 10, 2, torch, 0.3)
+        res[split] = t
+    flops, nbytes = fwd_work(w.B, w.H, w.T, w.dk, w.dv, 64, 2)
+    nbytes += w.B * w.H * w.dk * w.dv * 4          # the initial state is read too
+    return dict(w=w, split=res[True], unsplit=res[False], flops=flops, bytes=nbytes)
 
 
 def cpu_baseline(fwd, min_seconds=12.0, max_passes=64):
@@ -188,6 +229,7 @@ def main():
                          "runs at its working clocks when timing starts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-long", action="store_true", help="skip the long-context leg")
     ap.add_argument("--only", choices=["fwd", "decode", "copy", "pmc"], default=None,
                     help="profiling runs: launch only this part (copy = 512 MiB calibration "
                          "copy; pmc = copy, then forward, then decode, a few launches each)")
@@ -269,9 +311,24 @@ def main():
             "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": dgbs / HBM_PEAK_GBS, "achieved_cold_llc": cgbs,
                          "frac_cold_llc": cgbs / HBM_PEAK_GBS,
+                         "device_copy_same_bytes_cold_gbs": dec["copy_gbs"],
                          "traffic": read_traffic("recurrent_step_n256h16d128_bf16_traffic.txt", STEP_SRC),
                          "kernel": "gla::recurrent_step_kernel<128, 128, BF16>",
                          "algorithmic_bytes_per_launch": dec["bytes"]},
+        }
+    if not args.no_long:
+        lg = bench_long(args, torch, gla, inputs)
+        gbs = lg["bytes"] / lg["split"] / 1e9
+        log(f"[bench] long context: {lg['split'] * 1e6:.1f} us split, {lg['unsplit'] * 1e6:.1f} us unsplit "
+            f"({gbs:.0f} GB/s split)")
+        out["long_context"] = {
+            "workload": lg["w"].name, "us_per_call_split": lg["split"] * 1e6,
+            "us_per_call_unsplit": lg["unsplit"] * 1e6,
+            "tokens_per_s": lg["w"].B * lg["w"].T / lg["split"],
+            "tflop_s": lg["flops"] / lg["split"] / 1e12,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": lg["bytes"],
+                         "note": "three kernels per call: segment state pass, segment scan, forward"},
         }
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
