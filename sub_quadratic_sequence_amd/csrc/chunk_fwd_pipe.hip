@@ -362,17 +362,22 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
 #pragma unroll
         for (int i = 0; i < CPL; ++i) ex[i] = inc[i] - pp[3][i];
         unsigned kw[4][NWR];   // packed key operand words, token a
+        // all four rows read back before any is overwritten, so that one LDS
+        // round trip covers them
+        unsigned xq[4][NWR], xk[4][NWR];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          unsigned xq[NWR], xk[NWR];
-          if constexpr (FULL) lds_ld(xq, slot(B.q, a));
-          lds_ld(xk, slot(B.k, a));
+          if constexpr (FULL) lds_ld(xq[a], slot(B.q, a));
+          lds_ld(xk[a], slot(B.k, a));
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
           float qe[CPL], ke[CPL];
 #pragma unroll
           for (int i = 0; i < CPL; ++i) {
             const float gm = ex[i] + pp[a][i];   // Gamma of token 4tg+a
-            if constexpr (FULL) qe[i] = el(xq, i) * fast_exp2(gm);
-            ke[i] = el(xk, i) * fast_exp2(-gm);
+            if constexpr (FULL) qe[i] = el(xq[a], i) * fast_exp2(gm);
+            ke[i] = el(xk[a], i) * fast_exp2(-gm);
           }
 #pragma unroll
           for (int j = 0; j < NWR; ++j) kw[a][j] = pack_bf16x2(ke[2 * j], ke[2 * j + 1]);
@@ -529,16 +534,19 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
           __builtin_amdgcn_sched_barrier(0);
         }
         float kte[4][CPL];
+        unsigned xq[4][NWR], xk[4][NWR];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          unsigned xq[NWR], xk[NWR];
-          if constexpr (FULL) lds_ld(xq, slot(B.q, a));
-          lds_ld(xk, slot(B.k, a));
+          if constexpr (FULL) lds_ld(xq[a], slot(B.q, a));
+          lds_ld(xk[a], slot(B.k, a));
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
           float qh[CPL], kt[CPL];
 #pragma unroll
           for (int i = 0; i < CPL; ++i) {
-            if constexpr (FULL) qh[i] = el(xq, i) * fast_exp2(loc[a][i]);   // Q 2^(Gamma - B_p)
-            kt[i] = el(xk, i) * fast_exp2(tot[i] - loc[a][i]);   // K 2^(B_{p+1} - Gamma)
+            if constexpr (FULL) qh[i] = el(xq[a], i) * fast_exp2(loc[a][i]);   // Q 2^(Gamma - B_p)
+            kt[i] = el(xk[a], i) * fast_exp2(tot[i] - loc[a][i]);   // K 2^(B_{p+1} - Gamma)
             kte[a][i] = kt[i] * fke[i];                          // K 2^(Gamma_last - Gamma)
           }
           if constexpr (FULL) {
@@ -707,6 +715,19 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       }
 
       // ---- state: S <- post * (pre * S + KT^T V) ----
+      // every operand is read first (the output phase's registers are free by now),
+      // so the 2 NRB products issue back to back
+      Frag<BF16> vb[2], ka[2][NRB];
+      float4 fpost[NRB];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        frag_ld8(vb[ks], B.vt + tr_off(vrow, 4 * ks + gq, vrow_sw));
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          frag_ld8(ka[ks][rb], B.kt + tr_off(srow(rb, m), 4 * ks + gq, ka_sw ^ tr_swz(srow(rb, 0))));
+      }
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) fpost[rb] = *reinterpret_cast<const float4*>(&B.post[srow(rb, gq * 4)]);
       if constexpr (SAFE) {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
@@ -715,19 +736,12 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         }
       }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        Frag<BF16> vb;
-        frag_ld8(vb, B.vt + tr_off(vrow, 4 * ks + gq, vrow_sw));
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          Frag<BF16> ka;
-          frag_ld8(ka, B.kt + tr_off(srow(rb, m), 4 * ks + gq, ka_sw ^ tr_swz(srow(rb, 0))));
-          mma(sacc[rb], ka, vb);
-        }
-      }
+        for (int rb = 0; rb < NRB; ++rb) mma(sacc[rb], ka[ks][rb], vb[ks]);
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
-        const float4 f = *reinterpret_cast<const float4*>(&B.post[srow(rb, gq * 4)]);
+        const float4 f = fpost[rb];
         sacc[rb][0] *= f.x; sacc[rb][1] *= f.y; sacc[rb][2] *= f.z; sacc[rb][3] *= f.w;
       }
     };
