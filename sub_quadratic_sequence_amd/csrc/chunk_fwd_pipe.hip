@@ -87,7 +87,7 @@ __device__ __forceinline__ int tr_off(int r, int u, int sw, int h = 0) {
 }
 
 template <int DK>
-struct Buf {
+struct alignas(256) Buf {
   static constexpr int PQ = TokTile<DK>::kPitch;
   unsigned short q[C * PQ];        // query operand  [token][channel]
   unsigned short k[C * PQ];        // key operand    [token][channel]
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
   constexpr int NRB = DK / 16;   // consumer: 16-row state tiles
   constexpr int NWR = CPL / 2;   // 32-bit words per lane per token (q, k, g)
 
-  __shared__ __attribute__((aligned(16))) BufT bufs[2];
+  __shared__ __attribute__((aligned(256))) BufT bufs[2];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, m = lane & 15, gq = lane >> 4;
@@ -589,9 +589,21 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     // =========================== consumer waves ===========================
     const int cw = wave - 4;               // state / output columns [16cw, 16cw+16)
     const int vrow = cw * 16 + m;          // this lane's row of the values tile
-    int vrow_sw = tr_swz(vrow);
-    int c_sw = TokTile<DK>::swz(m);        // rows 16p + m of the operand tiles
-    int ka_sw = tr_swz(srow(0, m));        // rows srow(rb, m) of the state-key tile
+    // Per-lane byte offsets of the operand fragments inside a buffer.  With the
+    // swizzled layouts a fragment's offset is (lane part) XOR (compile-time part)
+    // plus a compile-time row offset: the XOR touches only bits 4-6 (4-7 for the
+    // 256-byte token rows), which the buffer base (a multiple of 256) and the row
+    // offsets leave clear, so each read costs one v_xor and an immediate offset.
+    constexpr unsigned kQ = offsetof(BufT, q), kK = offsetof(BufT, k), kKT = offsetof(BufT, kt),
+                       kVT = offsetof(BufT, vt);
+    static_assert(kQ % 256 == 0 && kK % 256 == 0 && kKT % 256 == 0 && kVT % 256 == 0 &&
+                  sizeof(BufT) % 256 == 0, "fragment offsets assume 256-byte aligned tiles");
+    const unsigned lb_qk = TokTile<DK>::kSwz
+                               ? (unsigned)(m * 256 + ((gq ^ TokTile<DK>::swz(m)) << 4))
+                               : (unsigned)(m * TokTile<DK>::kPitch * 2 + gq * 16);
+    const unsigned lb_kt = (unsigned)(srow(0, m) * 128 + (((gq ^ tr_swz(srow(0, m))) & 7) << 4));
+    const unsigned lb_vb = (unsigned)(vrow * 128 + (((gq ^ tr_swz(vrow)) & 7) << 4));
+    const unsigned lb_va = (unsigned)(vrow * 128 + ((((gq >> 1) ^ tr_swz(vrow)) & 7) << 4) + (gq & 1) * 8);
     unsigned short* og = reinterpret_cast<unsigned short*>(prm.o) + rowbase * DV + vcol0;
     f32x4 sacc[NRB];
 #pragma unroll
@@ -603,10 +615,22 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       }
     // one chunk of contractions; SAFE / EXT are compile-time so the body is branch-free
     auto consume = [&](const BufT& B, int u, auto safe_tag, auto ext_tag) __attribute__((always_inline)) {
-      launder(vrow_sw);
-      launder(c_sw);
-      launder(ka_sw);
-      constexpr bool SAFE = decltype(safe_tag)::value;
+      const unsigned bb = (unsigned)(reinterpret_cast<const char*>(&B) - reinterpret_cast<const char*>(bufs));
+      unsigned b_qk = lb_qk + bb, b_kt = lb_kt + bb + kKT, b_vb = lb_vb + bb + kVT, b_va = lb_va + bb + kVT;
+      launder(b_qk);
+      launder(b_kt);
+      launder(b_vb);
+      launder(b_va);
+      const char* lds = reinterpret_cast<const char*>(bufs);
+      // fragment (p, ks) of a [token][channel] tile at byte offset tile_off
+      auto tok_frag = [&](Frag<BF16>& f, unsigned tile_off, int p, int ks) __attribute__((always_inline)) {
+        unsigned a;
+        if constexpr (TokTile<DK>::kSwz)
+          a = (b_qk ^ ((unsigned)((4 * ks) ^ tok_swz(16 * p)) << 4)) + tile_off + p * 16 * 256;
+        else
+          a = b_qk + tile_off + p * 16 * TokTile<DK>::kPitch * 2 + ks * 64;
+        f.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(lds + a));
+      };      constexpr bool SAFE = decltype(safe_tag)::value;
       constexpr bool EXT = decltype(ext_tag)::value;
       // scaled copy of a query fragment by 8 per-channel factors
       auto scaled = [&](const Frag<BF16>& f, const float* wrow, int ks) __attribute__((always_inline)) {
@@ -637,9 +661,9 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           // tokens 32ks + 4gq .. +3 and the same 16 tokens later
-          const int u = 4 * ks + (gq >> 1);
-          frag_ld4x2(va[ks], B.vt + tr_off(vrow, u, vrow_sw, gq & 1),
-                     B.vt + tr_off(vrow, u + 2, vrow_sw, gq & 1));
+          const uint2 lo = *reinterpret_cast<const uint2*>(lds + (b_va ^ ((unsigned)(4 * ks) << 4)));
+          const uint2 hi = *reinterpret_cast<const uint2*>(lds + (b_va ^ ((unsigned)(4 * ks + 2) << 4)));
+          va[ks].v = __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
         }
         Frag<BF16> kf[4][KS];   // key fragments of sub-chunk r, loaded when first needed
         f32x4 oacc[4];
@@ -648,9 +672,8 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
           Frag<BF16> qf[KS];
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            const int o = TokTile<DK>::off(16 * p + m, 4 * ks + gq, c_sw ^ TokTile<DK>::swz(16 * p));
-            frag_ld8(kf[p][ks], B.k + o);
-            frag_ld8(qf[ks], B.q + o);
+            tok_frag(kf[p][ks], kK, p, ks);
+            tok_frag(qf[ks], kQ, p, ks);
           }
           // scores P^T(r, p) = K_r Q_p^T, r <= p
           f32x4 pacc[4];
@@ -721,10 +744,12 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       float4 fpost[NRB];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        frag_ld8(vb[ks], B.vt + tr_off(vrow, 4 * ks + gq, vrow_sw));
+        vb[ks].v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(lds + (b_vb ^ ((unsigned)(4 * ks) << 4))));
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-          frag_ld8(ka[ks][rb], B.kt + tr_off(srow(rb, m), 4 * ks + gq, ka_sw ^ tr_swz(srow(rb, 0))));
+        for (int rb = 0; rb < NRB; ++rb) {
+          const unsigned a = (b_kt ^ ((unsigned)(((4 * ks) ^ tr_swz(srow(rb, 0))) & 7) << 4)) + srow(rb, 0) * 128;
+          ka[ks][rb].v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(lds + a));
+        }
       }
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) fpost[rb] = *reinterpret_cast<const float4*>(&B.post[srow(rb, gq * 4)]);
