@@ -188,11 +188,9 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     // =========================== producer waves ===========================
     // Lane (tg, gq) of producer wave w holds tokens 4tg..4tg+3 x key channels
     // w*WCH + gq*CPL .. + CPL: the gate cumsum is a serial sum over 4 tokens
-    // plus a 16-lane DPP scan.  Each group of raw registers (v, g, then q and
-    // k) is reloaded with the next chunk's data as soon as this chunk no longer
-    // needs it, early in the chunk: the raw q and k words first move to this
-    // lane's own slots of the operand tiles B.q / B.k (no other lane touches
-    // them) and are read back from there when the operands overwrite them.
+    // plus a 16-lane DPP scan.  Each group of raw registers is reloaded with
+    // the next chunk's data as soon as this chunk no longer needs it: v after
+    // the value tile is written, g after the gate scan, q and k at the end.
     const int w = wave;
     const int tg = m;                      // tokens 4tg..4tg+3
     const int ch0 = w * WCH + gq * CPL;    // first channel of this lane
@@ -229,15 +227,6 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       } else {
         const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, 0);
         r[0] = x[0]; r[1] = x[1];
-      }
-    };
-    auto lds_ld = [&](unsigned (&r)[NWR], const unsigned short* p) __attribute__((always_inline)) {
-      if constexpr (NWR == 4) {
-        const uint4 x = *reinterpret_cast<const uint4*>(p);
-        r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
-      } else {
-        const uint2 x = *reinterpret_cast<const uint2*>(p);
-        r[0] = x.x; r[1] = x.y;
       }
     };
     auto st = [&](unsigned short* p, const unsigned (&r)[NWR]) __attribute__((always_inline)) {
@@ -349,35 +338,20 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       }
       __builtin_amdgcn_sched_barrier(0);
       load_g(un);
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        if constexpr (FULL) st(slot(B.q, a), rq[a]);
-        st(slot(B.k, a), rk[a]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      load_qk(un);
       if (fastw) {
         // ---- single pivot at the chunk start ----
         float ex[CPL];   // Gamma before this lane's first token
 #pragma unroll
         for (int i = 0; i < CPL; ++i) ex[i] = inc[i] - pp[3][i];
         unsigned kw[4][NWR];   // packed key operand words, token a
-        // all four rows read back before any is overwritten, so that one LDS
-        // round trip covers them
-        unsigned xq[4][NWR], xk[4][NWR];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          if constexpr (FULL) lds_ld(xq[a], slot(B.q, a));
-          lds_ld(xk[a], slot(B.k, a));
-        }
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           float qe[CPL], ke[CPL];
 #pragma unroll
           for (int i = 0; i < CPL; ++i) {
             const float gm = ex[i] + pp[a][i];   // Gamma of token 4tg+a
-            if constexpr (FULL) qe[i] = el(xq[a], i) * fast_exp2(gm);
-            ke[i] = el(xk[a], i) * fast_exp2(-gm);
+            if constexpr (FULL) qe[i] = el(rq[a], i) * fast_exp2(gm);
+            ke[i] = el(rk[a], i) * fast_exp2(-gm);
           }
 #pragma unroll
           for (int j = 0; j < NWR; ++j) kw[a][j] = pack_bf16x2(ke[2 * j], ke[2 * j + 1]);
@@ -496,12 +470,6 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         if (FULL && extw) {
           // exact diagonal partials, one (row a, key pair jj) at a time: sum over this
           // lane's channels, then over the wave's four lane rows (its whole slice)
-          unsigned sq[4][NWR], sk[4][NWR];
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            lds_ld(sq[a], slot(B.q, a));
-            lds_ld(sk[a], slot(B.k, a));
-          }
 #pragma unroll
           for (int a = 0; a < 4; ++a) {
             const int irow = (tg & 3) * 4 + a;
@@ -515,11 +483,11 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
                 float acc = 0.f;
 #pragma unroll
                 for (int i2 = 0; i2 < NWR; ++i2) {
-                  const unsigned kw = __builtin_bit_cast(unsigned, quad_bcast(__builtin_bit_cast(float, sk[b][i2]), src));
+                  const unsigned kw = __builtin_bit_cast(unsigned, quad_bcast(__builtin_bit_cast(float, rk[b][i2]), src));
                   const float l0 = quad_bcast(loc[b][2 * i2], src);
                   const float l1 = quad_bcast(loc[b][2 * i2 + 1], src);
-                  acc += el(sq[a], 2 * i2) * __uint_as_float(kw << 16) * fast_exp2(loc[a][2 * i2] - l0);
-                  acc += el(sq[a], 2 * i2 + 1) * __uint_as_float(kw & 0xffff0000u) *
+                  acc += el(rq[a], 2 * i2) * __uint_as_float(kw << 16) * fast_exp2(loc[a][2 * i2] - l0);
+                  acc += el(rq[a], 2 * i2 + 1) * __uint_as_float(kw & 0xffff0000u) *
                          fast_exp2(loc[a][2 * i2 + 1] - l1);
                 }
                 acc = j <= irow ? acc : 0.f;
@@ -534,19 +502,13 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
           __builtin_amdgcn_sched_barrier(0);
         }
         float kte[4][CPL];
-        unsigned xq[4][NWR], xk[4][NWR];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          if constexpr (FULL) lds_ld(xq[a], slot(B.q, a));
-          lds_ld(xk[a], slot(B.k, a));
-        }
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           float qh[CPL], kt[CPL];
 #pragma unroll
           for (int i = 0; i < CPL; ++i) {
-            if constexpr (FULL) qh[i] = el(xq[a], i) * fast_exp2(loc[a][i]);   // Q 2^(Gamma - B_p)
-            kt[i] = el(xk[a], i) * fast_exp2(tot[i] - loc[a][i]);   // K 2^(B_{p+1} - Gamma)
+            if constexpr (FULL) qh[i] = el(rq[a], i) * fast_exp2(loc[a][i]);   // Q 2^(Gamma - B_p)
+            kt[i] = el(rk[a], i) * fast_exp2(tot[i] - loc[a][i]);   // K 2^(B_{p+1} - Gamma)
             kte[a][i] = kt[i] * fke[i];                          // K 2^(Gamma_last - Gamma)
           }
           if constexpr (FULL) {
@@ -560,6 +522,8 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         if (lane == 0) B.flag[w] = 1 | (extw ? 2 : 0);
         ones &= ~(1 << bi);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      load_qk(un);
     };
 
     // step i produces chunk i into bufs[i & 1] while the consumers use chunk i-1;
