@@ -257,19 +257,32 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     auto el = [&](const unsigned (&r)[NWR], int i) __attribute__((always_inline)) -> float {
       return (i & 1) ? __uint_as_float(r[i >> 1] & 0xffff0000u) : __uint_as_float(r[i >> 1] << 16);
     };
-    // this lane's slot for token a in a [token][channel] operand tile: row 4tg+a,
-    // 16-byte unit (ch0 / 8) (DK = 128) or 8-byte half of unit ch0 / 8 (DK = 64)
-    int p_sw = TokTile<DK>::swz(4 * tg);
-    auto slot = [&](unsigned short* tile, int a) __attribute__((always_inline)) -> unsigned short* {
-      return tile + TokTile<DK>::off(4 * tg + a, ch0 >> 3, p_sw ^ TokTile<DK>::swz(a), (ch0 >> 2) & 1);
+    // This lane's slots, as byte offsets inside a buffer (lane part XOR a
+    // compile-time part, plus a compile-time row offset, as for the consumers):
+    //  * token a (row 4tg+a) of a [token][channel] operand tile: 16-byte unit
+    //    ch0 / 8 (DK = 128) or the 8-byte half of it (DK = 64);
+    //  * channel ch0 + i (state keys) / column vc0 + c (values) of a
+    //    [channel | column][token] tile, tokens 4tg..4tg+3.
+    constexpr unsigned kQ = offsetof(BufT, q), kK = offsetof(BufT, k), kKT = offsetof(BufT, kt),
+                       kVT = offsetof(BufT, vt);
+    const unsigned lp_tok =
+        TokTile<DK>::kSwz
+            ? (unsigned)(4 * tg * 256 + ((((ch0 >> 3) ^ TokTile<DK>::swz(4 * tg)) & 15) << 4) + ((ch0 >> 2) & 1) * 8)
+            : (unsigned)(4 * tg * TokTile<DK>::kPitch * 2 + ch0 * 2);
+    const unsigned lp_kt = (unsigned)(ch0 * 128 + ((((tg >> 1) ^ tr_swz(ch0)) & 7) << 4) + (tg & 1) * 8);
+    const unsigned lp_vt = (unsigned)(vc0 * 128 + ((((tg >> 1) ^ tr_swz(vc0)) & 7) << 4) + (tg & 1) * 8);
+    char* const lds = reinterpret_cast<char*>(bufs);
+    unsigned b_tok = 0, b_kt = 0, b_vt = 0;   // this chunk's buffer plus the lane parts
+    auto slot = [&](unsigned tile, int a) __attribute__((always_inline)) -> unsigned short* {
+      const unsigned o = TokTile<DK>::kSwz ? (b_tok ^ ((unsigned)tok_swz(a) << 4)) + a * 256
+                                           : b_tok + a * TokTile<DK>::kPitch * 2;
+      return reinterpret_cast<unsigned short*>(lds + o + tile);
     };
-    // [channel][token] slot of channel ch0 + i (kt) / column vc0 + c (vt), tokens 4tg..4tg+3
-    int kt_sw = tr_swz(ch0), vt_sw = tr_swz(vc0);
-    auto kt_slot = [&](unsigned short* tile, int i) __attribute__((always_inline)) -> unsigned short* {
-      return tile + tr_off(ch0 + i, tg >> 1, kt_sw ^ tr_swz(i), tg & 1);
+    auto kt_slot = [&](int i) __attribute__((always_inline)) -> unsigned short* {
+      return reinterpret_cast<unsigned short*>(lds + (b_kt ^ ((unsigned)tr_swz(i) << 4)) + i * 128);
     };
-    auto vt_slot = [&](unsigned short* tile, int c) __attribute__((always_inline)) -> unsigned short* {
-      return tile + tr_off(vc0 + c, tg >> 1, vt_sw ^ tr_swz(c), tg & 1);
+    auto vt_slot = [&](int c) __attribute__((always_inline)) -> unsigned short* {
+      return reinterpret_cast<unsigned short*>(lds + (b_vt ^ ((unsigned)tr_swz(c) << 4)) + c * 128);
     };
 
     // which LDS buffers hold all-ones safe-path factors for this wave's slice
@@ -281,9 +294,13 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     for (int i = 0; i < CPL; ++i) dsum[i] = 0.f;
     // produce chunk uc into B = bufs[bi] and start loading chunk un (a valid chunk index)
     auto produce = [&](BufT& B, int bi, int un) __attribute__((always_inline)) {
-      launder(p_sw);
-      launder(kt_sw);
-      launder(vt_sw);
+      const unsigned bb = (unsigned)(reinterpret_cast<char*>(&B) - lds);
+      b_tok = lp_tok + bb;
+      b_kt = lp_kt + bb + kKT;
+      b_vt = lp_vt + bb + kVT;
+      launder(b_tok);
+      launder(b_kt);
+      launder(b_vt);
       // V as [column][token]: pair tokens (a, a+1) of one column in one word
       {
 #pragma unroll
@@ -292,7 +309,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
           const unsigned sel = (c & 1) ? 0x07060302u : 0x05040100u;
           const unsigned lo = __builtin_amdgcn_perm(rv[1][wi], rv[0][wi], sel);
           const unsigned hi = __builtin_amdgcn_perm(rv[3][wi], rv[2][wi], sel);
-          *reinterpret_cast<uint2*>(vt_slot(B.vt, c)) = uint2{lo, hi};
+          *reinterpret_cast<uint2*>(vt_slot(c)) = uint2{lo, hi};
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -356,8 +373,8 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
 #pragma unroll
           for (int j = 0; j < NWR; ++j) kw[a][j] = pack_bf16x2(ke[2 * j], ke[2 * j + 1]);
           if constexpr (FULL) {
-            lds_store_n<BF16, CPL>(slot(B.q, a), qe);
-            st(slot(B.k, a), kw[a]);
+            lds_store_n<BF16, CPL>(slot(kQ, a), qe);
+            st(slot(kK, a), kw[a]);
           }
         }
         // state keys = the same bf16 values, [channel][token]: channel 2j (2j+1)
@@ -369,7 +386,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
             const unsigned sel = hb ? 0x07060302u : 0x05040100u;
             const unsigned lo = __builtin_amdgcn_perm(kw[1][j], kw[0][j], sel);
             const unsigned hi = __builtin_amdgcn_perm(kw[3][j], kw[2][j], sel);
-            *reinterpret_cast<uint2*>(kt_slot(B.kt, 2 * j + hb)) = uint2{lo, hi};
+            *reinterpret_cast<uint2*>(kt_slot(2 * j + hb)) = uint2{lo, hi};
           }
         }
         if (tg == 15) {   // this lane's last token is the chunk's last row
@@ -512,13 +529,13 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
             kte[a][i] = kt[i] * fke[i];                          // K 2^(Gamma_last - Gamma)
           }
           if constexpr (FULL) {
-            lds_store_n<BF16, CPL>(slot(B.q, a), qh);
-            lds_store_n<BF16, CPL>(slot(B.k, a), kt);
+            lds_store_n<BF16, CPL>(slot(kQ, a), qh);
+            lds_store_n<BF16, CPL>(slot(kK, a), kt);
           }
         }
 #pragma unroll
         for (int i = 0; i < CPL; ++i)
-          store4<BF16>(kt_slot(B.kt, i), kte[0][i], kte[1][i], kte[2][i], kte[3][i]);
+          store4<BF16>(kt_slot(i), kte[0][i], kte[1][i], kte[2][i], kte[3][i]);
         if (lane == 0) B.flag[w] = 1 | (extw ? 2 : 0);
         ones &= ~(1 << bi);
       }
