@@ -230,7 +230,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context leg")
-    ap.add_argument("--only", choices=["fwd", "decode", "copy", "pmc"], default=None,
+    ap.add_argument("--only", choices=["fwd", "decode", "long", "copy", "pmc"], default=None,
                     help="profiling runs: launch only this part (copy = 512 MiB calibration "
                          "copy; pmc = copy, then forward, then decode, a few launches each)")
     args = ap.parse_args()
@@ -259,6 +259,10 @@ def main():
         bench_forward(args, torch, gla, inputs)
         bench_decode(args, torch, gla, inputs)
         log("[bench] pmc launches done")
+        return
+    if args.only == "long":
+        lg = bench_long(args, torch, gla, inputs)
+        log(f"[bench] long context: {lg['split'] * 1e6:.1f} us split, {lg['unsplit'] * 1e6:.1f} us unsplit")
         return
     if args.only == "decode":
         dec = bench_decode(args, torch, gla, inputs)
