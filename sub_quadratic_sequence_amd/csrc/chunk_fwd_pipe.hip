@@ -153,10 +153,40 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
   // ---- work item ------------------------------------------------------------------
   const int nblk = gridDim.x;
   const int bid = blockIdx.x;
-  const int lin = prm.xcd_remap ? (bid & 7) * (nblk >> 3) + (bid >> 3) : bid;
-  const int item = lin / prm.nvt, vt = lin - item * prm.nvt;   // item = (unit, segment)
-  const int unit = item / prm.nseg, seg = item - unit * prm.nseg;
-  const int n = unit / prm.H, h = unit - n * prm.H;
+  int item, vt, n, h, seg;   // item = (unit, segment), unit = (sequence n, head h)
+  if (prm.sort_units) {
+    // Packed sequences of unequal lengths: work items of the longest sequences
+    // are dispatched first (all slices of a unit on one XCD: blocks 8s + x),
+    // so the longest ones do not start last.  Every workgroup ranks the
+    // lengths the same way (ties by index).
+    __shared__ int order[kMaxSortSeqs];
+    if (wave == 0 && lane < prm.nseq) {
+      const int l0 = prm.cu[lane + 1] - prm.cu[lane];
+      int rank = 0;
+      for (int j = 0; j < prm.nseq; ++j) {
+        const int lj = prm.cu[j + 1] - prm.cu[j];
+        rank += (lj > l0) || (lj == l0 && j < lane);
+      }
+      order[rank] = lane;
+    }
+    __syncthreads();
+    const int x = bid & 7, sl = bid >> 3;
+    const int r = x + 8 * (sl / prm.nvt);   // unit rank, longest first
+    vt = sl - (sl / prm.nvt) * prm.nvt;
+    n = order[r / prm.H];
+    h = r - (r / prm.H) * prm.H;
+    seg = 0;
+    item = n * prm.H + h;
+  } else {
+    const int lin = prm.xcd_remap ? (bid & 7) * (nblk >> 3) + (bid >> 3) : bid;
+    item = lin / prm.nvt;
+    vt = lin - item * prm.nvt;
+    const int u0 = item / prm.nseg;
+    seg = item - u0 * prm.nseg;
+    n = u0 / prm.H;
+    h = u0 - n * prm.H;
+  }
+  const int unit = n * prm.H + h;
   long bos, eos, rowbase;
   if (prm.cu) {
     bos = prm.cu[n];

@@ -112,6 +112,8 @@ int check_chunk_args(const char* fn, const void* q, const void* k, const void* v
   prm.seg_len = T;
   prm.seg_state = nullptr;
   prm.seg_decay = nullptr;
+  prm.nseq = nseq;
+  prm.sort_units = (cu_seqlens && dtype == GLA_BF16 && nseq <= gla::kMaxSortSeqs && units % 8 == 0) ? 1 : 0;
   return GLA_OK;
 }
 

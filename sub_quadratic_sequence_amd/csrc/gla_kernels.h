@@ -25,9 +25,15 @@ struct ChunkParams {
   // the last one shorter), and a work item is one (sequence, head, segment, slice).
   int nseg;
   int seg_len;
+  // Packed sequences: their count, and whether work items go longest sequence
+  // first (nseq <= kMaxSortSeqs, nseq * H a multiple of 8, bf16 kernel).
+  int nseq;
+  int sort_units;
   float* seg_state;  // [units][nseg][dk][dv] fp32: a segment's state from zero, then its incoming state
   float* seg_decay;  // [units][nseg][dk] fp32: exp of the segment's summed log-gates
 };
+
+constexpr int kMaxSortSeqs = 64;
 
 // Kernel modes of the pipelined forward.
 constexpr int kFull = 0;       // outputs (and the final state of unsplit sequences)

@@ -200,6 +200,30 @@ def test_fp32_varlen_with_empty_and_short(dev):
     assert torch.equal(sf[1].cpu(), d["s0"][1]) and torch.equal(sf[5].cpu(), d["s0"][5])
 
 
+@pytest.mark.parametrize("H,lengths", [
+    (2, [5, 0, 64, 1, 130, 0, 77, 300]),            # 16 units: longest-first work order
+    (3, [5, 0, 64, 1, 130, 0, 77]),                  # 21 units: natural order
+    (1, [700, 65, 64, 63, 1, 2, 3, 900]),           # 8 units, sorted, ties and tails
+])
+def test_bf16_varlen_with_empty_and_short(dev, H, lengths):
+    """Packed bf16 sequences, some empty or a single token, with an initial
+    state; with a multiple of 8 (sequence, head) units the work items are
+    dispatched longest sequence first."""
+    w = I.ChunkWorkload("bf16_varlen", B=1, H=H, T=0, dk=128, dv=128, dtype="bf16", seed=29,
+                        k_scaled=True)
+    say(f"bf16 varlen H={H} lengths={lengths} with initial state")
+    d = I.chunk_inputs(w, lengths=lengths, s0=True)
+    o, sf = _fwd(dev, d, s0=d["s0"], cu=d["cu_seqlens"])
+    o_ref, s_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], s0=d["s0"],
+                                     cu_seqlens=d["cu_seqlens"])
+    e_o, e_s = unit_err_varlen(o, o_ref, d["cu_seqlens"]), unit_err_fixed(sf, s_ref)
+    print(f"varlen bf16 H={H}: O err {e_o:.3e} S err {e_s:.3e}", flush=True)
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+    for n, ln in enumerate(lengths):
+        if ln == 0:   # an empty sequence passes its initial state through unchanged
+            assert torch.equal(sf[n].cpu(), d["s0"][n])
+
+
 # ------------------------------------------------------------------ bf16 shapes
 BF16_CASES = [
     ("dk64_dv64_T300", 2, 4, 300, 64, 64, "weak"),
