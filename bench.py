@@ -193,6 +193,28 @@ def bench_long(args, torch, gla, inputs):
     return dict(w=w, split=res[True], unsplit=res[False], flops=flops, bytes=nbytes)
 
 
+def bench_varlen(args, torch, gla, inputs):
+    """The packed workload: 16 sequences of 64..4096 tokens (33,280 in all), H16,
+    d_k 128, d_v 256, strong gates (most chunks take the sub-chunk pivots)."""
+    w = inputs.VARLEN_BF16
+    log(f"[bench] packed sequences {w.name}: generating inputs")
+    d = inputs.chunk_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, g = (d[n].to(dev) for n in "qkvg")
+    cu = d["cu_seqlens"].to(dev)
+    T, nseq = d["T"], d["nseq"]
+    o = torch.empty(1, w.H, T, w.dv, dtype=torch.bfloat16, device=dev)
+    sf = torch.empty(nseq, w.H, w.dk, w.dv, dtype=torch.float32, device=dev)
+
+    def step():
+        gla.gla_chunk_fwd(q, k, v, g, cu_seqlens=cu, out=o, final_state=sf)
+
+    _, t = time_launches(step, 20, 3, torch, 0.3)
+    flops, nbytes = fwd_work(1, w.H, T, w.dk, w.dv, 64, 2)
+    nbytes += (nseq - 1) * w.H * w.dk * w.dv * 4   # one final state per sequence
+    return dict(w=w, t=t, flops=flops, bytes=nbytes, tokens=T)
+
+
 def cpu_baseline(fwd, min_seconds=12.0, max_passes=64):
     """The fp64 oracle as it stands, on the host, on the forward workload's own
     inputs: whole sequences (all heads, all tokens) of the batch are run, cycling
@@ -229,7 +251,8 @@ def main():
                          "runs at its working clocks when timing starts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-long", action="store_true", help="skip the long-context leg")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long-context and packed-sequence legs")
     ap.add_argument("--only", choices=["fwd", "decode", "long", "copy", "pmc"], default=None,
                     help="profiling runs: launch only this part (copy = 512 MiB calibration "
                          "copy; pmc = copy, then forward, then decode, a few launches each)")
@@ -333,6 +356,16 @@ def main():
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": lg["bytes"],
                          "note": "three kernels per call: segment state pass, segment scan, forward"},
+        }
+    if not args.no_long:
+        vl = bench_varlen(args, torch, gla, inputs)
+        gbs = vl["bytes"] / vl["t"] / 1e9
+        log(f"[bench] packed sequences: {vl['t'] * 1e6:.1f} us ({gbs:.0f} GB/s)")
+        out["packed_sequences"] = {
+            "workload": vl["w"].name, "us_per_call": vl["t"] * 1e6,
+            "tokens_per_s": vl["tokens"] / vl["t"], "tflop_s": vl["flops"] / vl["t"] / 1e12,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": vl["bytes"]},
         }
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
