@@ -19,6 +19,11 @@ What is computed, and where the pages define it:
   decode step of the FlashLinearAttention page, section "The O(1) Inference
   Memory Revolution").
 
+* ``oracle.backward`` - gradients of the same recurrence with respect to q, k,
+  v, g and the initial state, for given upstream gradients of the outputs and
+  of the final state: PyTorch fp64 autograd of the token loop (module
+  docstring there; pinned in ``tests/test_oracle_backward.py``).
+
 Parity: the C and NumPy evaluations are pinned in ``tests/test_oracle_pins.py``
 against the pages' unrolled dual form (brute force), the alpha = 1 (linear
 attention) and alpha = gamma (RetNet) closed forms, exact rational arithmetic,

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the GLA forward and decode workloads.
+"""Seeded synthetic inputs for the GLA forward, backward and decode workloads.
 
 This module only draws random numbers and casts them; it holds none of the
 method's arithmetic, so both the HIP path's tests and the oracle can consume
@@ -68,7 +68,12 @@ VARLEN_BF16 = ChunkWorkload("gla_fwd_varlen16_h16dk128dv256_strong_bf16", B=1, H
 DECODE_BF16 = DecodeWorkload("gla_decode_n256h16d128_x64", N=256, H=16, dk=128, dv=128,
                              steps=64, seed=5)
 
-WORKLOADS = {w.name: w for w in (TINY_FP32, TRAIN_BF16, LONG_BF16, VARLEN_BF16, DECODE_BF16)}
+# The backward pass on the training shape (same q, k, v, g; upstream gradients
+# from ``upstream_grads``).
+TRAIN_BWD_BF16 = dataclasses.replace(TRAIN_BF16, name="gla_bwd_b8h16t2048d128_bf16")
+
+WORKLOADS = {w.name: w for w in (TINY_FP32, TRAIN_BF16, LONG_BF16, VARLEN_BF16, DECODE_BF16,
+                                 TRAIN_BWD_BF16)}
 
 
 def _gate(z: torch.Tensor, kind: str) -> torch.Tensor:
@@ -141,10 +146,22 @@ def decode_inputs(w: DecodeWorkload, *, N: Optional[int] = None, H: Optional[int
     return dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), g=g.to(dt), s0=s0)
 
 
+def upstream_grads(w: ChunkWorkload, d: dict, *, seed: Optional[int] = None,
+                   final: bool = True):
+    """Draw the upstream gradients of a backward call for the batch ``d`` of
+    ``chunk_inputs``: dO [B,H,T,dv] ~ N(0, 1) in the workload dtype and, when
+    ``final``, dS_T [Nseq,H,dk,dv] ~ 0.1 * N(0, 1) fp32.  A generator of its own
+    (seed + 1000) leaves the forward draws untouched."""
+    gen = torch.Generator().manual_seed((w.seed if seed is None else seed) + 1000)
+    do = torch.randn(d["B"], d["H"], d["T"], w.dv, generator=gen)
+    dsT = torch.randn(d["nseq"], d["H"], w.dk, w.dv, generator=gen) * 0.1 if final else None
+    return dict(do=do.to(w.torch_dtype), dsT=dsT)
+
+
 def expected_varlen_tokens(w: ChunkWorkload) -> float:
     return w.varlen * (w.len_lo + w.len_hi) / 2.0
 
 
 __all__ = ["ChunkWorkload", "DecodeWorkload", "WORKLOADS", "TINY_FP32", "TRAIN_BF16",
-           "LONG_BF16", "VARLEN_BF16", "DECODE_BF16", "chunk_inputs", "decode_inputs",
-           "expected_varlen_tokens"]
+           "LONG_BF16", "VARLEN_BF16", "DECODE_BF16", "TRAIN_BWD_BF16", "chunk_inputs",
+           "decode_inputs", "upstream_grads", "expected_varlen_tokens"]
