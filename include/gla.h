@@ -23,8 +23,8 @@
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent) owned
  *     by the caller; the library keeps no pointer after the call returns and
- *     allocates no device memory.  Only gla_chunk_fwd_ws takes a workspace,
- *     which the caller allocates.
+ *     allocates no device memory.  Only gla_chunk_fwd_ws and gla_chunk_bwd
+ *     take a workspace, which the caller allocates.
  *   - Layouts are row-major, last index fastest, densely packed, and every
  *     tensor pointer must be 16-byte aligned.
  *   - dtype selects the element type of q, k, v, g and o: GLA_BF16 (bfloat16)
@@ -125,6 +125,50 @@ int gla_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* g,
                      const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk,
                      int dv, int chunk_size, int dtype, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * Device workspace, in bytes, that gla_chunk_bwd needs for this shape (the bf16
+ * state entering every 64-token chunk: H x (sequences + tokens/64 + 1) slots of
+ * dk x dv, rounded up to 256).  num_seqs > 0 for packed sequences (then T is
+ * the packed total), 0 otherwise.  Unsupported shapes give 0.
+ */
+size_t gla_chunk_bwd_workspace_size(int num_seqs, int B, int H, int T, int dk, int dv,
+                                    int chunk_size, int dtype);
+
+/*
+ * Chunkwise backward pass: the gradients of
+ *
+ *     L = sum_t <d_o_t, o_t> + <d_final_state, S_T>
+ *
+ * for the forward computed by gla_chunk_fwd on the same arguments, i.e. the
+ * training half that the GLA page's section "I/O-Aware Kernel Design in
+ * FlashLinearAttention" pairs with the chunkwise forward (chunk states are
+ * recomputed here, not kept from the forward call).
+ *
+ *   q, k, g, v       as for gla_chunk_fwd (GLA_BF16 only)
+ *   initial_state    [Nseq, H, dk, dv] fp32 or NULL (zeros), as in the forward
+ *   d_o              [B, H, T, dv] bf16: gradient of the outputs
+ *   d_final_state    [Nseq, H, dk, dv] fp32 or NULL (zeros): gradient of S_T
+ *   d_q, d_k, d_g    [B, H, T, dk] bf16, written (d_g is the gradient of g = log alpha)
+ *   d_v              [B, H, T, dv] bf16, written
+ *   d_initial_state  [Nseq, H, dk, dv] fp32 or NULL (not written): gradient of S_0
+ *   cu_seqlens, num_seqs, B, H, T, chunk_size   as for gla_chunk_fwd
+ *   workspace        device buffer of at least gla_chunk_bwd_workspace_size(...)
+ *                    bytes, 256-byte aligned, owned by the caller; scratch until
+ *                    the call's kernels complete.
+ *
+ * Supported: dtype GLA_BF16, dk and dv in {64, 128}, chunk_size 64; others give
+ * GLA_ERR_UNSUPPORTED.  A missing, small or misaligned workspace gives
+ * GLA_ERR_INVALID_ARG.  Gates must keep every channel's decay over any 16
+ * consecutive tokens of a sequence at or above 2^-240 (so alpha = 0 is not
+ * supported here); a sequence that breaks this gets NaN gradients.
+ */
+int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
+                  const float* initial_state, const void* d_o, const float* d_final_state,
+                  void* d_q, void* d_k, void* d_v, void* d_g, float* d_initial_state,
+                  const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk, int dv,
+                  int chunk_size, int dtype, void* workspace, size_t workspace_bytes,
+                  void* stream);
 
 /*
  * One recurrent decode step for N sequences x H heads, in place on the state.

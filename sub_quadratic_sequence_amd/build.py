@@ -7,7 +7,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgla.so")
-SOURCES = ["gla_api.hip", "chunk_fwd.hip", "chunk_fwd_pipe.hip", "seg_scan.hip", "recurrent_step.hip"]
+SOURCES = ["gla_api.hip", "chunk_fwd.hip", "chunk_fwd_pipe.hip", "seg_scan.hip", "recurrent_step.hip",
+           "chunk_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

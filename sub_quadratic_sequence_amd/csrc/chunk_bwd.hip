@@ -1,0 +1,718 @@
+// Chunkwise GLA backward pass for gfx950 (MI355X), bf16 inputs, fp32 states.
+//
+// The gradients of L = sum_t <dO_t, o_t> + <dS_T, S_T> for the recurrence of
+// the page "Gated Linear Attention (GLA): Mathematical Foundations ...",
+// section "The Gated Recurrent Update" (S_t = diag(alpha_t) S_{t-1} + k_t^T v_t,
+// o_t = q_t S_t), organised as that page's section "I/O-Aware Kernel Design in
+// FlashLinearAttention" describes the backward kernel: chunk states are
+// recomputed in the backward call instead of being kept from the forward.
+//
+// Two kernels per call:
+//  * chunk_states_kernel: one pass over each sequence that writes the state at
+//    the start of every 64-token chunk (bf16, [dk][dv]) into the workspace.
+//    Its key operand k 2^(Gamma_last - Gamma) never exceeds |k|, so it needs
+//    no pivoting and is exact for any gates.
+//  * chunk_bwd_kernel: one workgroup (8 waves) per (sequence, head) walks the
+//    chunks from last to first.  Per chunk, with 16-token sub-chunks s:
+//      - a forward sweep s = 0..3 carries the state H (fp32 MFMA accumulators,
+//        from the stored chunk-start state) and produces dq;
+//      - a reverse sweep s = 3..0 carries the state gradient B (fp32
+//        accumulators, from dS_T at the sequence end) and produces dk, dv, dg.
+//    With Gamma the in-chunk cumulative log2 gate, the pivot b_s (middle of
+//    the sub-chunk's Gamma range) and Delta = Gamma - b_s:
+//      q~ = q 2^Delta, k~ = k 2^-Delta, A = dO V^T, P = q~ k~^T (causal)
+//      dq = 2^Delta (A k~ + dO H^^T),  dk = 2^-Delta (A^T q~ + V B^^T),
+//      dv = P^T dO + k~ B^,
+//    where H^ = 2^(b_s - Gamma_{s-1,last}) H and B^ = 2^(Gamma_{s,last} - b_s) B
+//    are the carried states scaled by factors <= 1, and
+//      H <- 2^(Gamma_{s,last} - b_s) (H^ + k~^T V),
+//      B <- 2^(b_s - Gamma_{s-1,last}) (B^ + q~^T dO).
+//    The gate gradient is the reverse cumulative sum of q*dq - k*dk inside the
+//    chunk, started from sum_n H[c][n] B[c][n] at the chunk's end (the gradient
+//    of a log-gate is the state times its gradient summed over columns), so
+//    rounding does not accumulate along the sequence.
+//  Every factor stays within 2^+-120 as long as no channel decays by more than
+//  2^-240 inside one 16-token sub-chunk; beyond that the sub-chunk's pivot is
+//  set to NaN and the sequence's gradients come out NaN (a loud failure, not a
+//  silent one).
+#include "gla_device.h"
+#include "gla_kernels.h"
+
+namespace gla {
+
+namespace bwd {
+
+constexpr int C = 64;        // chunk
+constexpr int L = 16;        // sub-chunk
+constexpr int NS = C / L;    // sub-chunks per chunk
+constexpr float kRangeLimit = 240.f;
+constexpr int kBufferFlags = 0x00020000;   // gfx9 buffer descriptor word 3: raw 32-bit dwords
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Workgroup barrier ordering LDS only (outstanding global loads stay in flight).
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// MFMA operand fragments.  A 16-deep operand gives lane (m = lane % 16,
+// grp = lane / 16) four contraction indices 4 grp + 0..3 of row (A) or column
+// (B) m; a 32-deep operand gives it 8 grp + 0..7.  Both operands of a product
+// are built with the same index map, so the contraction is exact whatever
+// order the hardware assigns to the slots.
+//  * row fragment: from storage [m][k] (k contiguous), one 8- or 16-byte read;
+//  * transposed fragment: from storage [k][m] (m contiguous) with the gfx950
+//    transposing read: in each 16-lane group, lane i reads 4 consecutive m of
+//    row k0 + 4 grp + i / 4 at m0 + 4 (i % 4) and receives element m0 + i of
+//    rows k0 + 4 grp + 0..3.
+__device__ __forceinline__ s16x4 row16(const unsigned short* base, int pitch, int m0, int k0, int m, int grp) {
+  return *reinterpret_cast<const s16x4*>(base + (m0 + m) * pitch + k0 + 4 * grp);
+}
+__device__ __forceinline__ s16x8 row32(const unsigned short* base, int pitch, int m0, int k0, int m, int grp) {
+  return *reinterpret_cast<const s16x8*>(base + (m0 + m) * pitch + k0 + 8 * grp);
+}
+__device__ __forceinline__ s16x4 tr_read(const unsigned short* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+__device__ __forceinline__ s16x4 tr16(const unsigned short* base, int pitch, int k0, int m0, int m, int grp) {
+  return tr_read(base + (k0 + 4 * grp + (m >> 2)) * pitch + m0 + 4 * (m & 3));
+}
+__device__ __forceinline__ s16x8 tr32(const unsigned short* base, int pitch, int k0, int m0, int m, int grp) {
+  const s16x4 lo = tr_read(base + (k0 + 8 * grp + (m >> 2)) * pitch + m0 + 4 * (m & 3));
+  const s16x4 hi = tr_read(base + (k0 + 8 * grp + 4 + (m >> 2)) * pitch + m0 + 4 * (m & 3));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// 16-deep contraction: the 16x16x32 instruction with the second half of both
+// operands zero (slots 4-7 pair with slots 4-7, so they add exactly 0).  The
+// legacy 16x16x16 bf16 instruction is not used: its results were read back too
+// early by the generated code on gfx950 (wrong values, no fault).
+__device__ __forceinline__ void mma16(f32x4& acc, s16x4 a, s16x4 b) {
+  const s16x4 z = {0, 0, 0, 0};
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, z, 0, 1, 2, 3, 4, 5, 6, 7)),
+      __builtin_bit_cast(bf16x8, __builtin_shufflevector(b, z, 0, 1, 2, 3, 4, 5, 6, 7)), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(f32x4& acc, s16x8 a, s16x8 b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ float lo_bf16(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 4 floats -> 4 bf16 (RNE) stored as 8 bytes
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+  return uint2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const void* base, long first_elem, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(static_cast<const void*>(static_cast<const unsigned short*>(base) + first_elem)),
+      (short)0, bytes, kBufferFlags);
+}
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t rs, unsigned off) {
+  const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+  return uint4{x[0], x[1], x[2], x[3]};
+}
+// per-lane byte offset plus a wave-uniform one (kept in a scalar register)
+__device__ __forceinline__ uint4 ld16s(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned soff) {
+  const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, (int)soff, 0);
+  return uint4{x[0], x[1], x[2], x[3]};
+}
+__device__ __forceinline__ uint2 ld8s(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned soff) {
+  const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)voff, (int)soff, 0);
+  return uint2{x[0], x[1]};
+}
+
+// Hides a value from the optimiser, so that addresses derived from it are formed
+// inside the chunk loop instead of being hoisted into dozens of live registers.
+__device__ __forceinline__ void pipe_launder(unsigned& x) { asm volatile("" : "+v"(x)); }
+
+// DPP shifts toward lower lanes inside a row of 16 (lane m reads m + k; past the
+// row's end reads 0)
+constexpr int kRowShl1 = 0x101, kRowShl2 = 0x102, kRowShl4 = 0x104, kRowShl8 = 0x108;
+
+// Sequence geometry of a unit: its rows in the [.., T, d] tensors, its length,
+// and the first workspace slot of its chunk states.
+struct Seq {
+  long r0;     // first row
+  long len;    // tokens
+  long slot0;  // workspace slot of chunk 0 (per head: n + start / 64)
+};
+__device__ __forceinline__ Seq seq_of(const BwdParams& prm, int n, int h) {
+  Seq s;
+  if (prm.cu) {
+    const long bos = prm.cu[n], eos = prm.cu[n + 1];
+    s.r0 = (long)h * prm.T + bos;
+    s.len = eos - bos;
+    s.slot0 = (long)h * prm.slots + n + bos / C;
+  } else {
+    s.r0 = ((long)n * prm.H + h) * prm.T;
+    s.len = prm.T;
+    s.slot0 = (long)h * prm.slots + n + (long)n * prm.T / C;
+  }
+  return s;
+}
+
+}  // namespace bwd
+
+// ============================================================================
+// Chunk-start states.  One workgroup (4 waves) per (sequence, head, 64-column
+// slice).  Wave w owns state columns [16w, 16w+16) of the slice for all d_k
+// rows as H^T tiles (MFMA accumulators: lane holds 4 columns x 1 channel).
+// ============================================================================
+template <int DK>
+__global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
+  using namespace bwd;
+  constexpr int KP = DK + 8;       // k-bar tile pitch (elements)
+  constexpr int VP = 64 + 8;       // value tile pitch
+  constexpr int NCG = DK / 8;      // 8-channel groups
+  constexpr int NGL = 16 * NCG;    // gating lanes
+  constexpr int CB = DK / 16;      // 16-channel blocks
+  __shared__ __attribute__((aligned(16))) unsigned short kb[C * KP];
+  __shared__ __attribute__((aligned(16))) unsigned short vs[C * VP];
+  __shared__ float dec[DK];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, m = lane & 15, grp = lane >> 4;
+  const int bid = blockIdx.x, nblk = gridDim.x;
+  const int lin = prm.xcd_remap ? (bid & 7) * (nblk >> 3) + (bid >> 3) : bid;
+  const int unit = lin / prm.nvt, vt = lin - unit * prm.nvt;
+  const int n = unit / prm.H, h = unit - n * prm.H;
+  const int DV = prm.DV, vcol0 = vt * 64;
+  const Seq sq = seq_of(prm, n, h);
+  const int nch = (int)((sq.len + C - 1) / C);
+  unsigned short* const hs = prm.hs + sq.slot0 * DK * DV;
+
+  const __amdgpu_buffer_rsrc_t rs_k = seq_rsrc(prm.k, sq.r0 * DK, (int)(sq.len * DK * 2));
+  const __amdgpu_buffer_rsrc_t rs_g = seq_rsrc(prm.g, sq.r0 * DK, (int)(sq.len * DK * 2));
+  const __amdgpu_buffer_rsrc_t rs_v = seq_rsrc(prm.v, sq.r0 * DV, (int)(sq.len * DV * 2));
+
+  // gating lane: tokens 4tg..4tg+3 x channels 8cg..8cg+7
+  const bool gl = tid < NGL;
+  const int tg = m, cg = tid >> 4;
+  const unsigned qk_lane = (unsigned)((4 * tg) * DK + 8 * cg) * 2u;
+  uint4 rk[4], rg[4], rv[2];
+  auto prefetch = [&](int u) __attribute__((always_inline)) {
+    if (gl) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        rk[a] = ld16(rs_k, qk_lane + (unsigned)(u * C + a) * DK * 2u);
+        rg[a] = ld16(rs_g, qk_lane + (unsigned)(u * C + a) * DK * 2u);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int idx = tid + 256 * it, row = idx >> 3, un = idx & 7;
+      rv[it] = ld16(rs_v, (unsigned)((u * C + row) * DV + vcol0 + 8 * un) * 2u);
+    }
+  };
+
+  // state tiles: (nb = wave, cb = i)
+  f32x4 Ht[CB];
+  const int nb = wave;
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    if (prm.s0) {
+      const float4 x = *reinterpret_cast<const float4*>(
+          prm.s0 + ((long)unit * DK + 16 * i + m) * DV + vcol0 + 16 * nb + 4 * grp);
+      Ht[i] = f32x4{x.x, x.y, x.z, x.w};
+    } else {
+      Ht[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  if (nch > 0) prefetch(0);
+
+  for (int u = 0; u < nch; ++u) {
+    if (gl) {
+      float pp[4][8];
+      const unsigned* gw[4] = {&rg[0].x, &rg[1].x, &rg[2].x, &rg[3].x};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const unsigned w = gw[a][i >> 1];
+          const float y = fmaxf(((i & 1) ? hi_bf16(w) : lo_bf16(w)) * kLog2e, -256.f);
+          pp[a][i] = a ? pp[a - 1][i] + y : y;
+        }
+      }
+      float last[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float x = pp[3][i];
+        x += dpp<kRowShr1>(x);
+        x += dpp<kRowShr2>(x);
+        x += dpp<kRowShr4>(x);
+        x += dpp<kRowShr8>(x);
+        const float ex = x - pp[3][i];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) pp[a][i] += ex;   // Gamma of token 4tg + a
+        last[i] = __shfl(x, lane | 15);                // Gamma of the chunk's last row
+      }
+      const unsigned* kw[4] = {&rk[0].x, &rk[1].x, &rk[2].x, &rk[3].x};
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float kbv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const unsigned w = kw[a][i >> 1];
+          kbv[i] = ((i & 1) ? hi_bf16(w) : lo_bf16(w)) * fast_exp2(last[i] - pp[a][i]);
+        }
+        *reinterpret_cast<uint4*>(kb + (4 * tg + a) * KP + 8 * cg) =
+            uint4{pack_bf16x2(kbv[0], kbv[1]), pack_bf16x2(kbv[2], kbv[3]), pack_bf16x2(kbv[4], kbv[5]),
+                  pack_bf16x2(kbv[6], kbv[7])};
+      }
+      if (tg == 15) {
+        *reinterpret_cast<float4*>(dec + 8 * cg) =
+            make_float4(fast_exp2(last[0]), fast_exp2(last[1]), fast_exp2(last[2]), fast_exp2(last[3]));
+        *reinterpret_cast<float4*>(dec + 8 * cg + 4) =
+            make_float4(fast_exp2(last[4]), fast_exp2(last[5]), fast_exp2(last[6]), fast_exp2(last[7]));
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int idx = tid + 256 * it, row = idx >> 3, un = idx & 7;
+      *reinterpret_cast<uint4*>(vs + row * VP + 8 * un) = rv[it];
+    }
+    if (u + 1 < nch) prefetch(u + 1);
+    barrier_lds();
+
+    // H_u (the state entering chunk u) to the workspace, then the update
+    unsigned short* const hu = hs + (long)u * DK * DV;
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      *reinterpret_cast<uint2*>(hu + (16 * i + m) * DV + vcol0 + 16 * nb + 4 * grp) =
+          pack4(Ht[i][0], Ht[i][1], Ht[i][2], Ht[i][3]);
+      const float d = dec[16 * i + m];
+      Ht[i] = Ht[i] * d;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const s16x8 x = tr32(vs, VP, 32 * ks, 16 * nb, m, grp);
+#pragma unroll
+      for (int i = 0; i < CB; ++i) mma32(Ht[i], x, tr32(kb, KP, 32 * ks, 16 * i, m, grp));
+    }
+    barrier_lds();
+  }
+}
+
+// ============================================================================
+// Backward main kernel: one workgroup (8 waves) per (sequence, head).
+//
+// Wave w < DK/16 owns key channels [16w, 16w+16) of both carried states, all
+// d_v columns, as H^T / B^T accumulator tiles: lane (m, grp) of tile nb holds
+// columns 16nb + 4grp + 0..3 of channel 16w + m.  For a 32-column contraction
+// step kk, tiles 2kk and 2kk+1 are then exactly a 16x16x32 operand (slots 0-3
+// <-> columns 32kk + 4grp + r, slots 4-7 <-> 32kk + 16 + 4grp + r), so the
+// inter terms of dq and dk read the state from registers; only dv, which
+// contracts over channels, needs the bf16 state in LDS.  The same wave owns
+// dq, dk and dg of its channels, so the gate-gradient boundary term and the
+// in-chunk reverse sums stay inside the wave.  Wave w < DV/16 computes dv for
+// columns [16w, 16w+16).
+// ============================================================================
+template <int DK, int DV>
+__global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
+  using namespace bwd;
+  constexpr int QP = DK + 8;       // [token][channel] bf16 tile pitch
+  constexpr int VP = DV + 8;       // [token][column] bf16 tile pitch
+  constexpr int SP = DV + 8;       // [channel][column] state tile pitch
+  constexpr int DP = DK + 4;       // [token][channel] fp32 Delta pitch
+  constexpr int CB = DK / 16, NB = DV / 16;
+  constexpr int NCG = DK / 8;
+  constexpr int NGL = 16 * NCG;             // gating lanes (waves 0 .. NGL/64-1)
+  constexpr int NVU = DV / 8;               // 16-byte units per value row
+  constexpr int NCP = C * NVU / 256;        // units per copy lane (waves 4-7)
+  static_assert(NGL <= 256, "shape");
+
+  struct Smem {
+    unsigned short qs[C * QP];     // q~  [token][channel]
+    unsigned short ks[C * QP];     // k~  [token][channel]
+    unsigned short vs[C * VP];     // v   [token][column]
+    unsigned short os[C * VP];     // dO  [token][column]
+    unsigned short ss[DK * SP];    // B^ (bf16) [channel][column]
+    unsigned short as[NS][L * L];  // A = dO V^T of sub-chunk s, [i][j], j <= i
+    unsigned short ps[NS][L * L];  // P = q~ k~^T of sub-chunk s, [i][j], j <= i
+    float dl[C * DP];              // Delta = Gamma - b_s (log2), [token][channel]
+    float fac[2][NS][DK];          // 0: 2^(b_s - Gamma_{s-1,last}), 1: 2^(Gamma_{s,last} - b_s)
+  };
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  char* const lds = reinterpret_cast<char*>(&sm);
+  constexpr unsigned oQ = offsetof(Smem, qs), oK = offsetof(Smem, ks), oV = offsetof(Smem, vs),
+                     oO = offsetof(Smem, os), oS = offsetof(Smem, ss), oA = offsetof(Smem, as),
+                     oP = offsetof(Smem, ps), oD = offsetof(Smem, dl), oF = offsetof(Smem, fac);
+  auto rd8 = [&](unsigned off) __attribute__((always_inline)) {
+    return *reinterpret_cast<const s16x4*>(lds + off);
+  };
+  auto rd16 = [&](unsigned off) __attribute__((always_inline)) {
+    return *reinterpret_cast<const s16x8*>(lds + off);
+  };
+  auto rdt = [&](unsigned off) __attribute__((always_inline)) { return tr_read(reinterpret_cast<const unsigned short*>(lds + off)); };
+  auto cat = [](s16x4 a, s16x4 b) __attribute__((always_inline)) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool sw = wave < CB;   // owns channels c0.. of the states, dq, dk, dg
+  const bool vw = wave < NB;   // computes dv for columns n0..
+  const int c0 = 16 * wave, n0 = 16 * wave;
+  const int unit = blockIdx.x;
+  const int n = unit / prm.H, h = unit - n * prm.H;
+  const Seq sq = seq_of(prm, n, h);
+  const int nch = (int)((sq.len + C - 1) / C);
+  const __amdgpu_buffer_rsrc_t rs_q = seq_rsrc(prm.q, sq.r0 * DK, (int)(sq.len * DK * 2));
+  const __amdgpu_buffer_rsrc_t rs_k = seq_rsrc(prm.k, sq.r0 * DK, (int)(sq.len * DK * 2));
+  const __amdgpu_buffer_rsrc_t rs_g = seq_rsrc(prm.g, sq.r0 * DK, (int)(sq.len * DK * 2));
+  const __amdgpu_buffer_rsrc_t rs_v = seq_rsrc(prm.v, sq.r0 * DV, (int)(sq.len * DV * 2));
+  const __amdgpu_buffer_rsrc_t rs_o = seq_rsrc(prm.dout, sq.r0 * DV, (int)(sq.len * DV * 2));
+  // this unit's chunk-start states (bf16 [chunk][dk][dv])
+  const __amdgpu_buffer_rsrc_t rs_h =
+      seq_rsrc(prm.hs, sq.slot0 * DK * DV, (int)((long)(nch > 0 ? nch : 1) * DK * DV * 2));
+  unsigned short* const dq_out = static_cast<unsigned short*>(prm.dq) + sq.r0 * DK;
+  unsigned short* const dk_out = static_cast<unsigned short*>(prm.dk) + sq.r0 * DK;
+  unsigned short* const dg_out = static_cast<unsigned short*>(prm.dg) + sq.r0 * DK;
+  unsigned short* const dv_out = static_cast<unsigned short*>(prm.dv) + sq.r0 * DV;
+
+  // ---- lane roles for the load phase ------------------------------------------
+  const bool gl = tid < NGL;               // gating lane: tokens 4tg..+3, channels 8cg..+7
+  const int tg = m, cg = tid >> 4;
+  const bool cl = tid >= 256;              // copy lane (values and output gradients)
+  const int cp = tid - 256;
+  const unsigned qk_lane = (unsigned)((4 * tg) * DK + 8 * cg) * 2u;
+  const unsigned h_lane = (unsigned)((c0 + m) * DV + 4 * grp) * 2u;
+
+  // Next chunk's raw inputs.  Gating lanes and copy lanes are disjoint, so they
+  // share one register array: q, k, g rows (gating) or v, dO units (copy).
+  constexpr int NPF = 12 > 2 * NCP ? 12 : 2 * NCP;
+  uint4 pf[NPF];
+  uint2 rh[NB];   // the chunk-start state of this wave's channels
+  auto prefetch = [&](int u) __attribute__((always_inline)) {
+    if (gl) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const unsigned so = (unsigned)(u * C + a) * DK * 2u;
+        pf[a] = ld16s(rs_q, qk_lane, so);
+        pf[4 + a] = ld16s(rs_k, qk_lane, so);
+        pf[8 + a] = ld16s(rs_g, qk_lane, so);
+      }
+    } else if (cl) {
+#pragma unroll
+      for (int it = 0; it < NCP; ++it) {
+        const int idx = cp + 256 * it, row = idx / NVU, un = idx % NVU;
+        const unsigned so = (unsigned)(u * C) * DV * 2u;
+        pf[it] = ld16s(rs_v, (unsigned)(row * DV + 8 * un) * 2u, so);
+        pf[NCP + it] = ld16s(rs_o, (unsigned)(row * DV + 8 * un) * 2u, so);
+      }
+    }
+  };
+  auto prefetch_state = [&](int u) __attribute__((always_inline)) {
+    if (sw) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) rh[b] = ld8s(rs_h, h_lane + 32u * b, (unsigned)u * DK * DV * 2u);
+    }
+  };
+
+  f32x4 Ht[NB], Bt[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    Bt[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (sw && prm.dsT) {
+      const float4 x = *reinterpret_cast<const float4*>(prm.dsT + ((long)unit * DK + c0 + m) * DV + 16 * b + 4 * grp);
+      Bt[b] = f32x4{x.x, x.y, x.z, x.w};
+    }
+  }
+  if (nch > 0) {
+    prefetch(nch - 1);
+    prefetch_state(nch - 1);
+  }
+
+  // bf16 operand of a 32-column step from two state tiles (see the kernel comment)
+  auto state_op = [](const f32x4& a, const f32x4& b) __attribute__((always_inline)) {
+    return __builtin_bit_cast(s16x8, uint4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                           pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])});
+  };
+
+  for (int u = nch - 1; u >= 0; --u) {
+    const long row0 = (long)u * C;   // first token of this chunk (sequence-relative)
+    // Per-lane LDS byte offsets (wave parts included); every access adds a
+    // compile-time constant, which the DS instructions take as an immediate.
+    unsigned r16Q = (m * QP + 4 * grp) * 2, r16V = (m * VP + 4 * grp) * 2;     // 8 B at col 4grp, row m
+    unsigned r32Q = (m * QP + 8 * grp) * 2, r32V = (m * VP + 8 * grp) * 2;     // 16 B at col 8grp, row m
+    unsigned tQ = ((4 * grp + (m >> 2)) * QP + 4 * (m & 3)) * 2;               // transposed, [token][*]
+    unsigned tV = ((4 * grp + (m >> 2)) * VP + 4 * (m & 3)) * 2;
+    unsigned tL = ((4 * grp + (m >> 2)) * L + 4 * (m & 3)) * 2;                // transposed 16x16 tile
+    unsigned r16L = (m * L + 4 * grp) * 2;
+    unsigned tQc = tQ + 2 * c0, tVn = tV + 2 * n0;
+    unsigned tS = ((8 * grp + (m >> 2)) * SP + n0 + 4 * (m & 3)) * 2;          // transposed state rows
+    unsigned wS = ((c0 + m) * SP + 4 * grp) * 2;                               // state tile writes
+    unsigned eD = (m * DP + c0 + 4 * grp) * 4, eQ = (m * QP + c0 + 4 * grp) * 2;
+    unsigned fC = (c0 + m) * 4;
+    pipe_launder(r16Q); pipe_launder(r16V); pipe_launder(r32Q); pipe_launder(r32V);
+    pipe_launder(tQ); pipe_launder(tV); pipe_launder(tL); pipe_launder(r16L);
+    pipe_launder(tQc); pipe_launder(tVn); pipe_launder(tS); pipe_launder(wS);
+    pipe_launder(eD); pipe_launder(eQ); pipe_launder(fC);
+
+    // ======================= load phase =======================
+    if (sw) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        Ht[b] = f32x4{lo_bf16(rh[b].x), hi_bf16(rh[b].x), lo_bf16(rh[b].y), hi_bf16(rh[b].y)};
+    }
+    if (gl) {
+      // log2 cumulative gate over the chunk, per channel
+      float gm[4][8];
+      const unsigned* gw[4] = {&pf[8].x, &pf[9].x, &pf[10].x, &pf[11].x};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const unsigned w = gw[a][i >> 1];
+          const float y = ((i & 1) ? hi_bf16(w) : lo_bf16(w)) * kLog2e;
+          gm[a][i] = a ? gm[a - 1][i] + y : y;
+        }
+        float x = gm[3][i];
+        x += dpp<kRowShr1>(x);
+        x += dpp<kRowShr2>(x);
+        x += dpp<kRowShr4>(x);
+        x += dpp<kRowShr8>(x);
+        const float ex = x - gm[3][i];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) gm[a][i] += ex;
+      }
+      const int s = tg >> 2;   // this lane's sub-chunk
+      const unsigned* qw[4] = {&pf[0].x, &pf[1].x, &pf[2].x, &pf[3].x};
+      const unsigned* kw[4] = {&pf[4].x, &pf[5].x, &pf[6].x, &pf[7].x};
+      float piv[8], f0[8], f1[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float first = quad_bcast_c<0>(gm[0][i]);   // Gamma at the sub-chunk's first row
+        const float last = quad_bcast_c<3>(gm[3][i]);    // ... and at its last row
+        const float prev = dpp<kRowShr4>(last);          // last row of the previous sub-chunk (0 for s = 0)
+        float b = 0.5f * (first + last);
+        if (!(first - last <= kRangeLimit)) b = __int_as_float(0x7fc00000);
+        piv[i] = b;
+        f0[i] = fast_exp2(b - prev);
+        f1[i] = fast_exp2(last - b);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float qv[8], kv[8], dv8[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float d = gm[a][i] - piv[i];
+          dv8[i] = d;
+          const unsigned wq = qw[a][i >> 1], wk = kw[a][i >> 1];
+          qv[i] = ((i & 1) ? hi_bf16(wq) : lo_bf16(wq)) * fast_exp2(d);
+          kv[i] = ((i & 1) ? hi_bf16(wk) : lo_bf16(wk)) * fast_exp2(-d);
+        }
+        const int r = 4 * tg + a;
+        *reinterpret_cast<uint4*>(sm.qs + r * QP + 8 * cg) =
+            uint4{pack_bf16x2(qv[0], qv[1]), pack_bf16x2(qv[2], qv[3]), pack_bf16x2(qv[4], qv[5]),
+                  pack_bf16x2(qv[6], qv[7])};
+        *reinterpret_cast<uint4*>(sm.ks + r * QP + 8 * cg) =
+            uint4{pack_bf16x2(kv[0], kv[1]), pack_bf16x2(kv[2], kv[3]), pack_bf16x2(kv[4], kv[5]),
+                  pack_bf16x2(kv[6], kv[7])};
+        *reinterpret_cast<float4*>(sm.dl + r * DP + 8 * cg) = make_float4(dv8[0], dv8[1], dv8[2], dv8[3]);
+        *reinterpret_cast<float4*>(sm.dl + r * DP + 8 * cg + 4) = make_float4(dv8[4], dv8[5], dv8[6], dv8[7]);
+      }
+      if ((tg & 3) == 0) {
+        *reinterpret_cast<float4*>(&sm.fac[0][s][8 * cg]) = make_float4(f0[0], f0[1], f0[2], f0[3]);
+        *reinterpret_cast<float4*>(&sm.fac[0][s][8 * cg + 4]) = make_float4(f0[4], f0[5], f0[6], f0[7]);
+        *reinterpret_cast<float4*>(&sm.fac[1][s][8 * cg]) = make_float4(f1[0], f1[1], f1[2], f1[3]);
+        *reinterpret_cast<float4*>(&sm.fac[1][s][8 * cg + 4]) = make_float4(f1[4], f1[5], f1[6], f1[7]);
+      }
+    }
+    if (cl) {
+#pragma unroll
+      for (int it = 0; it < NCP; ++it) {
+        const int idx = cp + 256 * it, row = idx / NVU, un = idx % NVU;
+        *reinterpret_cast<uint4*>(sm.vs + row * VP + 8 * un) = pf[it];
+        *reinterpret_cast<uint4*>(sm.os + row * VP + 8 * un) = pf[NCP + it];
+      }
+    }
+    barrier_lds();
+
+    // =============== score blocks of the four sub-chunks ===============
+    {
+      const int s = wave & 3;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (wave < 4) {   // A^T[j][i] = sum_n v_j[n] dO_i[n]
+        const unsigned b = r32V + (unsigned)(16 * s * VP * 2);
+#pragma unroll
+        for (int kk = 0; kk < DV / 32; ++kk) mma32(acc, rd16(oV + b + 64 * kk), rd16(oO + b + 64 * kk));
+      } else {          // P^T[j][i] = sum_c k~_j[c] q~_i[c]
+        const unsigned b = r32Q + (unsigned)(16 * s * QP * 2);
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) mma32(acc, rd16(oK + b + 64 * kk), rd16(oQ + b + 64 * kk));
+      }
+      // lane holds rows j = 4 grp + r at column i = m; keep j <= i, store as [i][j]
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = (4 * grp + r <= m) ? acc[r] : 0.f;
+      *reinterpret_cast<uint2*>(lds + (wave < 4 ? oA : oP) + s * L * L * 2 + r16L) = pack4(x[0], x[1], x[2], x[3]);
+    }
+    barrier_lds();
+
+    // ======================= forward sweep: dq =======================
+    float qd[NS][4];   // q~ * (dq before its 2^Delta factor), for dg
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      // the next chunk's inputs are requested half-way through this one: early
+      // enough to arrive, late enough to keep the first half's registers free
+      if (s == NS / 2 && u > 0) prefetch(u - 1);
+      if (sw) {
+        // H^ = 2^(b_s - Gamma_{s-1,last}) H
+        const float f = *reinterpret_cast<const float*>(lds + oF + s * DK * 4 + fC);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) Ht[b] = Ht[b] * f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < DV / 32; ++kk) {   // H^[c][n] dO[i][n]
+          const unsigned b = oO + r16V + (unsigned)((16 * s * VP + 32 * kk) * 2);
+          mma32(acc, state_op(Ht[2 * kk], Ht[2 * kk + 1]), cat(rd8(b), rd8(b + 32)));
+        }
+        // k~^T[c][j] A[i][j] over j in the sub-chunk
+        const s16x4 kt = rdt(oK + tQc + (unsigned)(16 * s * QP * 2));
+        mma16(acc, kt, rd8(oA + s * L * L * 2 + r16L));
+        // lane: channels c0 + 4 grp + r at token 16 s + m
+        const float4 d = *reinterpret_cast<const float4*>(lds + oD + eD + (unsigned)(16 * s * DP * 4));
+        const uint2 qv = *reinterpret_cast<const uint2*>(lds + oQ + eQ + (unsigned)(16 * s * QP * 2));
+        qd[s][0] = lo_bf16(qv.x) * acc[0];
+        qd[s][1] = hi_bf16(qv.x) * acc[1];
+        qd[s][2] = lo_bf16(qv.y) * acc[2];
+        qd[s][3] = hi_bf16(qv.y) * acc[3];
+        const long t = row0 + 16 * s + m;
+        if (t < sq.len)
+          *reinterpret_cast<uint2*>(dq_out + t * DK + c0 + 4 * grp) =
+              pack4(fast_exp2(d.x) * acc[0], fast_exp2(d.y) * acc[1], fast_exp2(d.z) * acc[2],
+                    fast_exp2(d.w) * acc[3]);
+        // H <- 2^(Gamma_{s,last} - b_s) (H^ + k~^T V) over the sub-chunk's tokens
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          mma16(Ht[b], rdt(oV + tV + (unsigned)((16 * s * VP + 16 * b) * 2)), kt);
+        const float f1 = *reinterpret_cast<const float*>(lds + oF + (NS + s) * DK * 4 + fC);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) Ht[b] = Ht[b] * f1;
+      }
+    }
+
+    // ===== gate gradient at the chunk end: sum_n H[c][n] B[c][n] per channel =====
+    float carry[4] = {0.f, 0.f, 0.f, 0.f};
+    if (sw) {
+      float p = 0.f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        p += Ht[b][0] * Bt[b][0] + Ht[b][1] * Bt[b][1] + Ht[b][2] * Bt[b][2] + Ht[b][3] * Bt[b][3];
+      p += __shfl_xor(p, 16);
+      p += __shfl_xor(p, 32);   // channel c0 + m, in every lane of column m
+#pragma unroll
+      for (int r = 0; r < 4; ++r) carry[r] = __shfl(p, 4 * grp + r);
+    }
+    // H is not needed again in this chunk: its registers take the next chunk's state
+    if (u > 0) prefetch_state(u - 1);
+
+    // ======================= reverse sweep: dk, dv, dg =======================
+#pragma unroll
+    for (int s = NS - 1; s >= 0; --s) {
+      if (sw) {
+        // B^ = 2^(Gamma_{s,last} - b_s) B, and its bf16 copy for dv
+        const float f = *reinterpret_cast<const float*>(lds + oF + (NS + s) * DK * 4 + fC);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          Bt[b] = Bt[b] * f;
+          *reinterpret_cast<uint2*>(lds + oS + wS + 32 * b) = pack4(Bt[b][0], Bt[b][1], Bt[b][2], Bt[b][3]);
+        }
+      }
+      barrier_lds();
+      if (sw) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < DV / 32; ++kk) {   // B^[c][n] v[j][n]
+          const unsigned b = oV + r16V + (unsigned)((16 * s * VP + 32 * kk) * 2);
+          mma32(acc, state_op(Bt[2 * kk], Bt[2 * kk + 1]), cat(rd8(b), rd8(b + 32)));
+        }
+        // q~^T[c][i] A[i][j] over i in the sub-chunk
+        const s16x4 qt = rdt(oQ + tQc + (unsigned)(16 * s * QP * 2));
+        mma16(acc, qt, rdt(oA + s * L * L * 2 + tL));
+        const float4 d = *reinterpret_cast<const float4*>(lds + oD + eD + (unsigned)(16 * s * DP * 4));
+        const uint2 kv = *reinterpret_cast<const uint2*>(lds + oK + eQ + (unsigned)(16 * s * QP * 2));
+        float x[4] = {qd[s][0] - lo_bf16(kv.x) * acc[0], qd[s][1] - hi_bf16(kv.x) * acc[1],
+                      qd[s][2] - lo_bf16(kv.y) * acc[2], qd[s][3] - hi_bf16(kv.y) * acc[3]};
+        // reverse inclusive sum over the 16 tokens of the sub-chunk (lanes m)
+        float dgv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float y = x[r];
+          y += dpp<kRowShl1>(y);
+          y += dpp<kRowShl2>(y);
+          y += dpp<kRowShl4>(y);
+          y += dpp<kRowShl8>(y);
+          dgv[r] = y + carry[r];
+          carry[r] += __shfl(y, lane & 48);
+        }
+        const long t = row0 + 16 * s + m;
+        if (t < sq.len) {
+          *reinterpret_cast<uint2*>(dk_out + t * DK + c0 + 4 * grp) =
+              pack4(fast_exp2(-d.x) * acc[0], fast_exp2(-d.y) * acc[1], fast_exp2(-d.z) * acc[2],
+                    fast_exp2(-d.w) * acc[3]);
+          *reinterpret_cast<uint2*>(dg_out + t * DK + c0 + 4 * grp) = pack4(dgv[0], dgv[1], dgv[2], dgv[3]);
+        }
+        // B <- 2^(b_s - Gamma_{s-1,last}) (B^ + q~^T dO) over the sub-chunk's tokens
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          mma16(Bt[b], rdt(oO + tV + (unsigned)((16 * s * VP + 16 * b) * 2)), qt);
+        const float f0 = *reinterpret_cast<const float*>(lds + oF + s * DK * 4 + fC);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) Bt[b] = Bt[b] * f0;
+      }
+      if (vw) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {   // B^^T[n][c] k~[j][c]
+          const unsigned b = oS + tS + (unsigned)(32 * kk * SP * 2);
+          mma32(acc, cat(rdt(b), rdt(b + 4 * SP * 2)), rd16(oK + r32Q + (unsigned)((16 * s * QP + 32 * kk) * 2)));
+        }
+        // dO^T[n][i] P[i][j] over i in the sub-chunk
+        mma16(acc, rdt(oO + tVn + (unsigned)(16 * s * VP * 2)), rdt(oP + s * L * L * 2 + tL));
+        const long t = row0 + 16 * s + m;
+        if (t < sq.len)
+          *reinterpret_cast<uint2*>(dv_out + t * DV + n0 + 4 * grp) = pack4(acc[0], acc[1], acc[2], acc[3]);
+      }
+      barrier_lds();
+    }
+  }
+
+  if (sw && prm.ds0) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      *reinterpret_cast<float4*>(prm.ds0 + ((long)unit * DK + c0 + m) * DV + 16 * b + 4 * grp) =
+          make_float4(Bt[b][0], Bt[b][1], Bt[b][2], Bt[b][3]);
+  }
+}
+
+int launch_chunk_states(const BwdParams& prm, int dk, int nblocks, hipStream_t stream) {
+  if (dk == 128)
+    hipLaunchKernelGGL((chunk_states_kernel<128>), dim3(nblocks), dim3(256), 0, stream, prm);
+  else if (dk == 64)
+    hipLaunchKernelGGL((chunk_states_kernel<64>), dim3(nblocks), dim3(256), 0, stream, prm);
+  else
+    return -2;
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_chunk_bwd(const BwdParams& prm, int dk, int dv, int units, hipStream_t stream) {
+  if (dk == 128 && dv == 128)
+    hipLaunchKernelGGL((chunk_bwd_kernel<128, 128>), dim3(units), dim3(512), 0, stream, prm);
+  else if (dk == 128 && dv == 64)
+    hipLaunchKernelGGL((chunk_bwd_kernel<128, 64>), dim3(units), dim3(512), 0, stream, prm);
+  else if (dk == 64 && dv == 128)
+    hipLaunchKernelGGL((chunk_bwd_kernel<64, 128>), dim3(units), dim3(512), 0, stream, prm);
+  else if (dk == 64 && dv == 64)
+    hipLaunchKernelGGL((chunk_bwd_kernel<64, 64>), dim3(units), dim3(512), 0, stream, prm);
+  else
+    return -2;
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace gla

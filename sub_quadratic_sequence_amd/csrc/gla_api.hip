@@ -246,6 +246,102 @@ int gla_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* g,
   return launch_status("gla_chunk_fwd_ws", rc, dk, dtype);
 }
 
+size_t gla_chunk_bwd_workspace_size(int num_seqs, int B, int H, int T, int dk, int dv,
+                                    int chunk_size, int dtype) {
+  if (dtype != GLA_BF16 || chunk_size != 64 || B <= 0 || H <= 0 || T < 0) return 0;
+  if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return 0;
+  const long long nseq = num_seqs > 0 ? num_seqs : B;
+  const long long tokens = num_seqs > 0 ? (long long)T : (long long)B * T;
+  const long long slots = nseq + tokens / 64 + 1;
+  return ((size_t)H * slots * dk * dv * 2 + 255) / 256 * 256;
+}
+
+int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
+                  const float* initial_state, const void* d_o, const float* d_final_state,
+                  void* d_q, void* d_k, void* d_v, void* d_g, float* d_initial_state,
+                  const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk, int dv,
+                  int chunk_size, int dtype, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  g_last_error[0] = '\0';
+  const char* fn = "gla_chunk_bwd";
+  if (dtype != GLA_BF16 && dtype != GLA_F32)
+    return fail(GLA_ERR_INVALID_ARG, "%s: dtype %d is not GLA_BF16 or GLA_F32", fn, dtype);
+  if (dtype != GLA_BF16)
+    return fail(GLA_ERR_UNSUPPORTED, "%s: only GLA_BF16 is implemented", fn);
+  if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0)
+    return fail(GLA_ERR_INVALID_ARG, "%s: B=%d H=%d T=%d dk=%d dv=%d must be positive (T >= 0)", fn,
+                B, H, T, dk, dv);
+  if (chunk_size != 64)
+    return fail(GLA_ERR_UNSUPPORTED, "%s: chunk_size %d (only 64 is implemented)", fn, chunk_size);
+  if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+    return fail(GLA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d (each must be 64 or 128)", fn, dk, dv);
+  int nseq = B;
+  if (cu_seqlens) {
+    if (B != 1)
+      return fail(GLA_ERR_INVALID_ARG, "%s: packed sequences (cu_seqlens) need B == 1, got %d", fn, B);
+    if (num_seqs <= 0)
+      return fail(GLA_ERR_INVALID_ARG, "%s: num_seqs=%d must be positive with cu_seqlens", fn, num_seqs);
+    nseq = num_seqs;
+  }
+  if (!fits_i32((long long)B * H * T * dk) || !fits_i32((long long)B * H * T * dv) ||
+      !fits_i32((long long)nseq * H * dk * dv))
+    return fail(GLA_ERR_INVALID_ARG, "%s: tensor sizes exceed int32 indexing", fn);
+  // one sequence's chunk states are addressed with 32-bit byte offsets
+  if (!fits_i32(((long long)T / 64 + 1) * dk * dv * 2))
+    return fail(GLA_ERR_INVALID_ARG, "%s: T=%d is too long for one call's chunk states", fn, T);
+  const bool any_tokens = (long long)B * H * T > 0;
+  if (any_tokens && (!q || !k || !v || !g || !d_o || !d_q || !d_k || !d_v || !d_g))
+    return fail(GLA_ERR_INVALID_ARG, "%s: q, k, v, g, d_o, d_q, d_k, d_v and d_g must be non-null", fn);
+  const void* ptrs[] = {q, k, v, g, d_o, d_q, d_k, d_v, d_g, initial_state, d_final_state,
+                        d_initial_state, cu_seqlens};
+  const char* names[] = {"q", "k", "v", "g", "d_o", "d_q", "d_k", "d_v", "d_g", "initial_state",
+                         "d_final_state", "d_initial_state", "cu_seqlens"};
+  for (int i = 0; i < 13; ++i)
+    if (ptrs[i] && !aligned16(ptrs[i]))
+      return fail(GLA_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, names[i]);
+  if (!any_tokens && !d_initial_state) return GLA_OK;
+  const size_t need = gla_chunk_bwd_workspace_size(cu_seqlens ? num_seqs : 0, B, H, T, dk, dv,
+                                                   chunk_size, dtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(GLA_ERR_INVALID_ARG, "%s: workspace of %zu bytes given, %zu needed", fn,
+                workspace ? workspace_bytes : (size_t)0, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(GLA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+  const long long units = (long long)nseq * H;
+  const int nvt = dv / 64;
+  if (!fits_i32(units * nvt))
+    return fail(GLA_ERR_INVALID_ARG, "%s: %lld work items", fn, units * nvt);
+  const long long tokens = cu_seqlens ? (long long)T : (long long)B * T;
+
+  gla::BwdParams prm;
+  prm.q = q;
+  prm.k = k;
+  prm.v = v;
+  prm.g = g;
+  prm.dout = d_o;
+  prm.s0 = initial_state;
+  prm.dsT = d_final_state;
+  prm.dq = d_q;
+  prm.dk = d_k;
+  prm.dv = d_v;
+  prm.dg = d_g;
+  prm.ds0 = d_initial_state;
+  prm.hs = static_cast<unsigned short*>(workspace);
+  prm.cu = cu_seqlens;
+  prm.H = H;
+  prm.T = T;
+  prm.DV = dv;
+  prm.nvt = nvt;
+  prm.slots = (int)(nseq + tokens / 64 + 1);
+  prm.xcd_remap = ((units * nvt) % 8 == 0) ? 1 : 0;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // 1. the state entering every chunk, 2. the gradients chunk by chunk, last to first
+  int rc = gla::launch_chunk_states(prm, dk, (int)(units * nvt), s);
+  if (rc != 0) return launch_status(fn, rc, dk, dtype);
+  rc = gla::launch_chunk_bwd(prm, dk, dv, (int)units, s);
+  return launch_status(fn, rc, dk, dtype);
+}
+
 int gla_recurrent_step(const void* q, const void* k, const void* v, const void* g, float* state,
                        void* o, int N, int H, int dk, int dv, int dtype, void* stream) {
   g_last_error[0] = '\0';

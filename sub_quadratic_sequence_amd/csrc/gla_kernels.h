@@ -58,12 +58,38 @@ struct StepParams {
   void* o;
 };
 
+// Arguments of the backward kernels (see include/gla.h for meanings).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* dout;      // gradient of the outputs
+  const float* s0;       // initial state, or null (zeros)
+  const float* dsT;      // gradient of the final state, or null (zeros)
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dg;
+  float* ds0;            // gradient of the initial state, or null (not written)
+  unsigned short* hs;    // workspace: bf16 chunk-start states [H][slots][dk][dv]
+  const int* cu;         // packed varlen offsets on the device, or null
+  int H;
+  int T;                 // tokens per sequence (fixed) or total packed tokens
+  int DV;
+  int nvt;               // DV / 64 column slices (state pass work items per unit)
+  int slots;             // chunk-state slots per head: sequences + tokens / 64 + 1
+  int xcd_remap;         // state pass: consecutive work items share an XCD
+};
+
 // Each returns 0 on success, -1 if the launch failed, -2 if no kernel exists
 // for the shape/dtype.
 int launch_chunk_fwd(const ChunkParams& prm, int dk, int dtype, int nblocks, hipStream_t stream);
 int launch_chunk_fwd_pipe(const ChunkParams& prm, int dk, bool state_only, int nblocks,
                           hipStream_t stream);
 int launch_seg_scan(const SegScanParams& prm, int units, hipStream_t stream);
+int launch_chunk_states(const BwdParams& prm, int dk, int nblocks, hipStream_t stream);
+int launch_chunk_bwd(const BwdParams& prm, int dk, int dv, int units, hipStream_t stream);
 int launch_recurrent_step(const StepParams& prm, int units, int dk, int dv, int dtype,
                           hipStream_t stream);
 

@@ -44,6 +44,10 @@ def load_library():
         lib.gla_chunk_fwd_ws.restype = I
         lib.gla_chunk_fwd_ws.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P,
                                          ctypes.c_size_t, P]
+        lib.gla_chunk_bwd_workspace_size.restype = ctypes.c_size_t
+        lib.gla_chunk_bwd_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
+        lib.gla_chunk_bwd.restype = I
+        lib.gla_chunk_bwd.argtypes = [P] * 13 + [I] * 8 + [P, ctypes.c_size_t, P]
         lib.gla_recurrent_step.restype = I
         lib.gla_recurrent_step.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
         lib.gla_status_string.restype = ctypes.c_char_p
@@ -157,6 +161,96 @@ def gla_chunk_fwd(q, k, v, g, initial_state=None, output_final_state=False, cu_s
     if rc != GLA_OK:
         raise GLAError(rc, last_error())
     return out, final_state
+
+
+def bwd_workspace_size(q, v, cu_seqlens=None, chunk_size: int = 64) -> int:
+    """Bytes of workspace ``gla_chunk_bwd`` needs for these inputs (its chunk states)."""
+    B, H, T, dk = q.shape
+    num_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    return int(load_library().gla_chunk_bwd_workspace_size(num_seqs, B, H, T, dk, v.shape[-1],
+                                                           int(chunk_size), _dtype_code(q)))
+
+
+def _aligned_workspace(workspace):
+    """(pointer, bytes) of the 256-byte aligned part of a uint8 GPU tensor."""
+    _check_gpu("workspace", workspace, torch.uint8)
+    base = workspace.data_ptr()
+    off = (-base) % 256
+    return ctypes.c_void_p(base + off), max(0, workspace.numel() - off)
+
+
+def gla_chunk_bwd(q, k, v, g, do, initial_state=None, d_final_state=None, cu_seqlens=None,
+                  chunk_size: int = 64, want_d_initial_state=None, workspace=None):
+    """Chunkwise GLA backward (C entry point ``gla_chunk_bwd``).
+
+    Gradients of sum(o * do) + sum(final_state * d_final_state) for the forward
+    ``gla_chunk_fwd(q, k, v, g, initial_state)``.  q, k, g: [B, H, T, dk]; v, do:
+    [B, H, T, dv], bfloat16; initial_state, d_final_state: [Nseq, H, dk, dv]
+    float32 or None.  Returns ``(dq, dk, dv, dg, d_initial_state)``;
+    ``d_initial_state`` is computed when ``initial_state`` is given (or
+    ``want_d_initial_state``), else None.  The workspace (the chunk states) is a
+    torch allocation unless ``workspace`` (a uint8 GPU tensor) is passed.
+    """
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    _check_gpu("q", q)
+    dt = q.dtype
+    _check_gpu("k", k, dt, q.shape)
+    _check_gpu("g", g, dt, q.shape)
+    _check_gpu("v", v, dt, (B, H, T, dv))
+    _check_gpu("do", do, dt, (B, H, T, dv))
+    nseq, num_seqs = B, 0
+    if cu_seqlens is not None:
+        _check_gpu("cu_seqlens", cu_seqlens, torch.int32)
+        num_seqs = cu_seqlens.numel() - 1
+        nseq = num_seqs
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if t is not None:
+            _check_gpu(name, t, torch.float32, (nseq, H, dk, dv))
+    if want_d_initial_state is None:
+        want_d_initial_state = initial_state is not None
+    dq = torch.empty_like(q)
+    dk_ = torch.empty_like(k)
+    dg = torch.empty_like(g)
+    dv_ = torch.empty_like(v)
+    ds0 = (torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
+           if want_d_initial_state else None)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        if workspace is None:
+            need = bwd_workspace_size(q, v, cu_seqlens, chunk_size)
+            workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = _aligned_workspace(workspace)
+        rc = lib.gla_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(initial_state), _ptr(do),
+                               _ptr(d_final_state), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg),
+                               _ptr(ds0), _ptr(cu_seqlens), num_seqs, B, H, T, dk, dv,
+                               int(chunk_size), _dtype_code(q), ws_ptr, ws_bytes,
+                               ctypes.c_void_p(stream))
+    if rc != GLA_OK:
+        raise GLAError(rc, last_error())
+    return dq, dk_, dv_, dg, ds0
+
+
+class GLAFunction(torch.autograd.Function):
+    """Autograd wrapper: forward ``gla_chunk_fwd``, backward ``gla_chunk_bwd``
+    (bfloat16, d_k and d_v in {64, 128}).  ``apply(q, k, v, g, initial_state,
+    cu_seqlens)`` returns ``(o, final_state)``."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, g, initial_state=None, cu_seqlens=None):
+        o, sf = gla_chunk_fwd(q, k, v, g, initial_state=initial_state, output_final_state=True,
+                              cu_seqlens=cu_seqlens)
+        ctx.save_for_backward(q, k, v, g, initial_state, cu_seqlens)
+        return o, sf
+
+    @staticmethod
+    def backward(ctx, do, dsf):
+        q, k, v, g, s0, cu = ctx.saved_tensors
+        dq, dk, dv, dg, ds0 = gla_chunk_bwd(q, k, v, g, do.contiguous(), initial_state=s0,
+                                            d_final_state=None if dsf is None else dsf.contiguous(),
+                                            cu_seqlens=cu)
+        return dq, dk, dv, dg, ds0, None
 
 
 def gla_recurrent_step(q, k, v, g, state, out=None):

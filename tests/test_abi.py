@@ -31,8 +31,9 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    assert names == ["gla_chunk_fwd", "gla_chunk_fwd_workspace_size", "gla_chunk_fwd_ws",
-                     "gla_last_error", "gla_recurrent_step", "gla_status_string"]
+    assert names == ["gla_chunk_bwd", "gla_chunk_bwd_workspace_size", "gla_chunk_fwd",
+                     "gla_chunk_fwd_workspace_size", "gla_chunk_fwd_ws", "gla_last_error",
+                     "gla_recurrent_step", "gla_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -154,3 +155,52 @@ def test_chunk_fwd_ws_rejects_workspace(lib, ws, nbytes, needle):
                               1, 16, 65536, 128, 128, 64, 0, P(ws) if ws else None, nbytes, None)
     assert rc == 1
     assert needle in gla.last_error()
+
+
+def test_bwd_workspace_size(lib):
+    lib.gla_chunk_bwd_workspace_size.restype = ctypes.c_size_t
+    # training shape: 16 heads x (8 sequences + 16384 / 64 tokens + 1) chunk states of 128 x 128 bf16
+    assert lib.gla_chunk_bwd_workspace_size(0, 8, 16, 2048, 128, 128, 64, 0) == 16 * 265 * 128 * 128 * 2
+    # packed: 16 heads x (16 sequences + 33000 // 64 + 1) states of 128 x 64, rounded up to 256 bytes
+    assert lib.gla_chunk_bwd_workspace_size(16, 1, 16, 33000, 128, 64, 64, 0) == 16 * 532 * 128 * 64 * 2
+    assert lib.gla_chunk_bwd_workspace_size(0, 8, 16, 2048, 128, 128, 64, 1) == 0   # fp32
+    assert lib.gla_chunk_bwd_workspace_size(0, 8, 16, 2048, 128, 256, 64, 0) == 0   # dv 256
+    assert lib.gla_chunk_bwd_workspace_size(0, 8, 16, 2048, 128, 128, 128, 0) == 0  # chunk 128
+
+
+def _bwd(lib, **kw):
+    P = ctypes.c_void_p
+    a = dict(q=P(FAKE), k=P(FAKE), v=P(FAKE), g=P(FAKE), s0=None, do=P(FAKE), dsT=None,
+             dq=P(FAKE), dk_=P(FAKE), dv_=P(FAKE), dg=P(FAKE), ds0=None, cu=None, num_seqs=0,
+             B=2, H=4, T=256, dk=128, dv=128, chunk=64, dtype=0, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.gla_chunk_bwd(a["q"], a["k"], a["v"], a["g"], a["s0"], a["do"], a["dsT"], a["dq"],
+                             a["dk_"], a["dv_"], a["dg"], a["ds0"], a["cu"], a["num_seqs"], a["B"],
+                             a["H"], a["T"], a["dk"], a["dv"], a["chunk"], a["dtype"], a["ws"],
+                             a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=1), 2, "only GLA_BF16"),
+    (dict(dtype=7), 1, "dtype 7"),
+    (dict(dv=256), 2, "dk=128 dv=256"),
+    (dict(dk=96), 2, "dk=96"),
+    (dict(chunk=128), 2, "chunk_size 128"),
+    (dict(do=None), 1, "must be non-null"),
+    (dict(dg=None), 1, "must be non-null"),
+    (dict(cu=ctypes.c_void_p(FAKE), num_seqs=3), 1, "need B == 1"),
+    (dict(dq=ctypes.c_void_p(FAKE + 8)), 1, "d_q is not 16-byte aligned"),
+    (dict(), 1, "workspace of 0 bytes"),
+    (dict(ws=ctypes.c_void_p(FAKE), ws_bytes=4096), 1, "needed"),
+    (dict(ws=ctypes.c_void_p(FAKE + 16), ws_bytes=1 << 30), 1, "256-byte aligned"),
+    (dict(B=1, H=1, T=1 << 23, dk=128, dv=128), 1, "too long"),
+])
+def test_chunk_bwd_rejects(lib, kw, status, needle):
+    from sub_quadratic_sequence_amd import gla
+
+    assert _bwd(lib, **kw) == status
+    assert needle in gla.last_error(), gla.last_error()
+
+
+def test_chunk_bwd_zero_tokens_without_state_gradient_is_a_noop(lib):
+    assert _bwd(lib, T=0) == 0

@@ -1,0 +1,163 @@
+"""GPU parity of the backward pass (``gla_chunk_bwd`` through the C ABI) against
+the fp64 autograd oracle on the same seeded inputs.  Tolerance: per unit,
+max |X_gpu - X_ref| / max |X_ref| <= 2e-2 for every gradient (bf16 path).
+Every test prints the case it is about to run before touching the GPU."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import backward as OB
+from parity import TOL_BF16, to64, unit_err_fixed, unit_err_varlen
+from sub_quadratic_sequence_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sub_quadratic_sequence_amd import gla
+
+    gla.load_library()
+    return torch.device("cuda:0")
+
+
+def say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _case(B, H, T, dk, dv, gate="weak", s0=True, final=True, seed=11, lengths=None, k_scaled=True):
+    w = I.ChunkWorkload("bwd_test", B=B, H=H, T=T, dk=dk, dv=dv, dtype="bf16", seed=seed, gate=gate,
+                        k_scaled=k_scaled, s0=s0)
+    d = I.chunk_inputs(w, lengths=lengths)
+    d.update(I.upstream_grads(w, d, final=final))
+    return d
+
+
+def _gpu_bwd(dev, d):
+    from sub_quadratic_sequence_amd import gla
+
+    to = lambda x: None if x is None else x.to(dev)
+    out = gla.gla_chunk_bwd(*(to(d[n]) for n in ("q", "k", "v", "g", "do")), initial_state=to(d["s0"]),
+                            d_final_state=to(d["dsT"]), cu_seqlens=to(d["cu_seqlens"]))
+    torch.cuda.synchronize()
+    return out
+
+
+def _check(d, got, label, units=None):
+    ref = OB.backward(d["q"], d["k"], d["v"], d["g"], d["do"], d["s0"], d["dsT"],
+                      cu_seqlens=d["cu_seqlens"], units=units)
+    names = ("dq", "dk", "dv", "dg")
+    errs = {}
+    for name, x, r in zip(names, got[:4], ref[:4]):
+        x64 = to64(x)
+        assert np.all(np.isfinite(x64)), name
+        if units is not None:
+            errs[name] = max(_unit_err_one(x64, to64(r), n, h, d) for n, h in units)
+        elif d["cu_seqlens"] is not None:
+            errs[name] = unit_err_varlen(x64, r, d["cu_seqlens"])
+        else:
+            errs[name] = unit_err_fixed(x64, r)
+    if d["s0"] is not None:
+        x64, r64 = to64(got[4]), to64(ref[4])
+        if units is not None:
+            errs["ds0"] = max(float(np.abs(x64[n, h] - r64[n, h]).max() / np.abs(r64[n, h]).max())
+                              for n, h in units)
+        else:
+            errs["ds0"] = unit_err_fixed(x64, r64)
+    print(label + ": " + "  ".join(f"{k} {v:.3e}" for k, v in errs.items()) + f"  (tol {TOL_BF16})",
+          flush=True)
+    for k, v in errs.items():
+        assert v <= TOL_BF16, (k, v)
+
+
+def _unit_err_one(x, r, n, h, d):
+    if d["cu_seqlens"] is None:
+        a, b = x[n, h], r[n, h]
+    else:
+        cu = [int(c) for c in d["cu_seqlens"]]
+        a, b = x[0, h, cu[n]:cu[n + 1]], r[0, h, cu[n]:cu[n + 1]]
+    return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-300))
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv,gate", [
+    (1, 2, 100, 64, 64, "weak"),       # two chunks, ragged tail
+    (2, 2, 300, 128, 128, "weak"),     # several chunks, ragged tail
+    (1, 2, 256, 128, 128, "strong"),   # strong gates: every sub-chunk uses its own pivot range
+    (1, 2, 130, 128, 64, "weak"),
+    (1, 2, 130, 64, 128, "strong"),
+    (1, 1, 1, 128, 128, "weak"),       # one token
+    (1, 2, 128, 64, 64, "zero"),       # alpha = 1
+])
+def test_bwd_matches_oracle(dev, B, H, T, dk, dv, gate):
+    say(f"gla_chunk_bwd B={B} H={H} T={T} dk={dk} dv={dv} gate={gate} s0 dsT")
+    d = _case(B, H, T, dk, dv, gate=gate)
+    _check(d, _gpu_bwd(dev, d), f"bwd B{B} H{H} T{T} dk{dk} dv{dv} {gate}")
+
+
+def test_bwd_without_initial_or_final_state(dev):
+    say("gla_chunk_bwd B=2 H=2 T=200 d128 no s0, no dsT")
+    d = _case(2, 2, 200, 128, 128, s0=False, final=False)
+    got = _gpu_bwd(dev, d)
+    assert got[4] is None
+    _check(d, got, "bwd no states")
+
+
+@pytest.mark.parametrize("gate", ["weak", "strong"])
+def test_bwd_varlen_with_empty_and_short(dev, gate):
+    lengths = [1, 0, 65, 200, 17, 64]
+    say(f"gla_chunk_bwd varlen lengths={lengths} H=2 d128 gate={gate}")
+    d = _case(1, 2, 0, 128, 128, gate=gate, lengths=lengths)
+    got = _gpu_bwd(dev, d)
+    _check(d, got, f"bwd varlen {gate}")
+    # the empty sequence passes its state through: dS0 = dS_T
+    assert torch.equal(got[4][1].cpu(), d["dsT"][1])
+
+
+def test_bwd_training_shape_sampled_units(dev):
+    w = I.TRAIN_BWD_BF16
+    say(f"{w.name}: gla_chunk_bwd at full size, oracle on sampled units")
+    d = I.chunk_inputs(w)
+    d.update(I.upstream_grads(w, d, final=True))
+    got = _gpu_bwd(dev, d)
+    units = [(0, 0), (3, 7), (7, 15)]
+    _check(d, got, w.name, units=units)
+    for x in got[:4]:
+        assert torch.isfinite(x).all()
+
+
+def test_bwd_deterministic(dev):
+    say("gla_chunk_bwd twice on B=2 H=4 T=500 d128: bitwise equal")
+    d = _case(2, 4, 500, 128, 128, gate="strong")
+    a = _gpu_bwd(dev, d)
+    b = _gpu_bwd(dev, d)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_bwd_alpha_zero_gives_nan_only_in_that_sequence(dev):
+    say("gla_chunk_bwd with one alpha = 0 gate in sequence 1: NaN there, sequence 0 exact")
+    d = _case(2, 1, 150, 64, 64)
+    d["g"][1, 0, 70, 5] = float("-inf")
+    got = _gpu_bwd(dev, d)
+    assert not torch.isfinite(got[0][1]).all() or not torch.isfinite(got[1][1]).all()
+    d0 = {k: (v[:1] if isinstance(v, torch.Tensor) and k != "cu_seqlens" else v) for k, v in d.items()}
+    _check(d0, tuple(x[:1] for x in got), "bwd sequence 0 next to an alpha = 0 sequence")
+
+
+def test_autograd_function_matches_entry_point(dev):
+    from sub_quadratic_sequence_amd import gla
+
+    say("GLAFunction forward + backward vs gla_chunk_bwd, B=1 H=2 T=190 d128")
+    d = _case(1, 2, 190, 128, 128)
+    leaves = [d[n].to(dev).requires_grad_(True) for n in ("q", "k", "v", "g")]
+    s0 = d["s0"].to(dev).requires_grad_(True)
+    o, sf = gla.GLAFunction.apply(*leaves, s0, None)
+    torch.autograd.backward([o, sf], [d["do"].to(dev), d["dsT"].to(dev)])
+    torch.cuda.synchronize()
+    ref = _gpu_bwd(dev, d)
+    for leaf, r in zip(leaves + [s0], ref):
+        assert torch.equal(leaf.grad, r)
