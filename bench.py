@@ -45,6 +45,21 @@ def fwd_work(B, H, T, dk, dv, C, esz):
     return flops, bytes_
 
 
+def bwd_work(B, H, T, dk, dv, L, esz):
+    """FLOPs and bytes of one backward call (gla_chunk_bwd).
+    FLOPs, as the two kernels compute them per token and head (16-token
+    sub-chunks, L = 16): the score blocks dO V^T and q~ k~^T and the three
+    in-sub-chunk products (L (3 dk + 2 dv) multiply-adds), the three inter terms
+    of dq, dk, dv and the two carried-state updates (5 dk dv), and the chunk-state
+    pass (2 dk dv); times 2.  Bytes, the algorithmic minimum: q, k, g, v, dO read
+    once and dq, dk, dg, dv written once (the chunk states the implementation
+    stores and re-reads are not counted; the measured traffic shows them)."""
+    tokens_heads = B * H * T
+    flops = tokens_heads * 2 * (L * (3 * dk + 2 * dv) + 7 * dk * dv)
+    bytes_ = tokens_heads * esz * ((3 * dk + 2 * dv) + (3 * dk + dv))
+    return flops, bytes_
+
+
 def decode_work(N, H, dk, dv, esz):
     """Per decode step: 5 dk dv FLOPs per unit; bytes: the fp32 state read and
     written (8 dk dv) plus q, k, g, v in and o out."""
@@ -215,6 +230,28 @@ def bench_varlen(args, torch, gla, inputs):
     return dict(w=w, t=t, flops=flops, bytes=nbytes, tokens=T)
 
 
+def bench_backward(args, torch, gla, inputs):
+    """The backward pass on the training shape (B8 H16 T2048 d128, no initial
+    state, gradient of the outputs only): one gla_chunk_bwd call = the chunk-state
+    pass plus the backward kernel."""
+    w = inputs.TRAIN_BWD_BF16
+    log(f"[bench] backward {w.name}: generating inputs")
+    d = inputs.chunk_inputs(w)
+    d.update(inputs.upstream_grads(w, d, final=False))
+    dev = torch.device("cuda:0")
+    q, k, v, g, do = (d[n].to(dev) for n in ("q", "k", "v", "g", "do"))
+    outs = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(g))
+    ws = torch.empty(gla.bwd_workspace_size(q, v) + 256, dtype=torch.uint8, device=dev)
+
+    def step():
+        gla.gla_chunk_bwd(q, k, v, g, do, workspace=ws, out=outs)
+
+    steps = max(1, args.steps // 4)
+    wall, gpu = time_launches(step, steps, max(1, args.warmup // 4), torch, args.preroll * 0.5)
+    flops, nbytes = bwd_work(w.B, w.H, w.T, w.dk, w.dv, 16, 2)
+    return dict(w=w, wall=wall, gpu=gpu, flops=flops, bytes=nbytes, tokens=w.B * w.T, steps=steps)
+
+
 def cpu_baseline(fwd, min_seconds=12.0, max_passes=64):
     """The fp64 oracle as it stands, on the host, on the forward workload's own
     inputs: whole sequences (all heads, all tokens) of the batch are run, cycling
@@ -253,7 +290,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the long-context and packed-sequence legs")
-    ap.add_argument("--only", choices=["fwd", "decode", "long", "copy", "pmc"], default=None,
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
+    ap.add_argument("--only", choices=["fwd", "decode", "long", "bwd", "copy", "pmc"], default=None,
                     help="profiling runs: launch only this part (copy = 512 MiB calibration "
                          "copy; pmc = copy, then forward, then decode, a few launches each)")
     args = ap.parse_args()
@@ -286,6 +324,10 @@ def main():
     if args.only == "long":
         lg = bench_long(args, torch, gla, inputs)
         log(f"[bench] long context: {lg['split'] * 1e6:.1f} us split, {lg['unsplit'] * 1e6:.1f} us unsplit")
+        return
+    if args.only == "bwd":
+        bw = bench_backward(args, torch, gla, inputs)
+        log(f"[bench] backward {bw['gpu'] * 1e6:.1f} us/call")
         return
     if args.only == "decode":
         dec = bench_decode(args, torch, gla, inputs)
@@ -366,6 +408,20 @@ def main():
             "tokens_per_s": vl["tokens"] / vl["t"], "tflop_s": vl["flops"] / vl["t"] / 1e12,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": vl["bytes"]},
+        }
+    if not args.no_bwd:
+        bw = bench_backward(args, torch, gla, inputs)
+        gbs = bw["bytes"] / bw["gpu"] / 1e9
+        tf = bw["flops"] / bw["gpu"] / 1e12
+        log(f"[bench] backward: {bw['gpu'] * 1e6:.1f} us/call ({gbs:.0f} GB/s algorithmic, {tf:.1f} TFLOP/s)")
+        out["backward"] = {
+            "workload": bw["w"].name, "us_per_call": bw["gpu"] * 1e6, "steps": bw["steps"],
+            "tokens_per_s": bw["tokens"] / bw["wall"], "tflop_s": tf,
+            "mfma_peak_frac": tf / MFMA_BF16_PEAK_TFLOPS,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": bw["bytes"],
+                         "algorithmic_flops_per_call": bw["flops"],
+                         "note": "two kernels per call: chunk-state pass, backward"},
         }
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")

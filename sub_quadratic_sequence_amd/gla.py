@@ -180,7 +180,7 @@ def _aligned_workspace(workspace):
 
 
 def gla_chunk_bwd(q, k, v, g, do, initial_state=None, d_final_state=None, cu_seqlens=None,
-                  chunk_size: int = 64, want_d_initial_state=None, workspace=None):
+                  chunk_size: int = 64, want_d_initial_state=None, workspace=None, out=None):
     """Chunkwise GLA backward (C entry point ``gla_chunk_bwd``).
 
     Gradients of sum(o * do) + sum(final_state * d_final_state) for the forward
@@ -189,7 +189,8 @@ def gla_chunk_bwd(q, k, v, g, do, initial_state=None, d_final_state=None, cu_seq
     float32 or None.  Returns ``(dq, dk, dv, dg, d_initial_state)``;
     ``d_initial_state`` is computed when ``initial_state`` is given (or
     ``want_d_initial_state``), else None.  The workspace (the chunk states) is a
-    torch allocation unless ``workspace`` (a uint8 GPU tensor) is passed.
+    torch allocation unless ``workspace`` (a uint8 GPU tensor) is passed;
+    ``out`` optionally supplies (dq, dk, dv, dg) to write into.
     """
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -209,10 +210,13 @@ def gla_chunk_bwd(q, k, v, g, do, initial_state=None, d_final_state=None, cu_seq
             _check_gpu(name, t, torch.float32, (nseq, H, dk, dv))
     if want_d_initial_state is None:
         want_d_initial_state = initial_state is not None
-    dq = torch.empty_like(q)
-    dk_ = torch.empty_like(k)
-    dg = torch.empty_like(g)
-    dv_ = torch.empty_like(v)
+    if out is None:
+        dq, dk_, dv_, dg = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                            torch.empty_like(g))
+    else:
+        dq, dk_, dv_, dg = out
+        for name, t, ref in (("dq", dq, q), ("dk", dk_, k), ("dv", dv_, v), ("dg", dg, g)):
+            _check_gpu(name, t, dt, tuple(ref.shape))
     ds0 = (torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
            if want_d_initial_state else None)
     lib = load_library()
