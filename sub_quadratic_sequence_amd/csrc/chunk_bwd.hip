@@ -7,11 +7,16 @@
 // FlashLinearAttention" describes the backward kernel: chunk states are
 // recomputed in the backward call instead of being kept from the forward.
 //
-// Two kernels per call:
-//  * chunk_states_kernel: one pass over each sequence that writes the state at
-//    the start of every 64-token chunk (bf16, [dk][dv]) into the workspace.
-//    Its key operand k 2^(Gamma_last - Gamma) never exceeds |k|, so it needs
-//    no pivoting and is exact for any gates.
+// Kernels of one call:
+//  * chunk_states_kernel<DK, false>: one pass over each sequence that writes the
+//    state at the start of every 64-token chunk (bf16, [dk][dv]) into the
+//    workspace.  Its key operand k 2^(Gamma_last - Gamma) never exceeds |k|, so
+//    it needs no pivoting and is exact for any gates.
+//  * when the sequences are split into segments (few units, long sequences):
+//    chunk_states_kernel<DK, true>, the same pass run backwards over each
+//    segment but one on q 2^Gamma and dO, gives the state gradient a segment
+//    sends to its start from its own outputs (and its total decay); the
+//    reverse segment scan turns those into each segment's incoming gradient.
 //  * chunk_bwd_kernel: one workgroup (8 waves) per (sequence, head) walks the
 //    chunks from last to first.  Per chunk, with 16-token sub-chunks s:
 //      - a forward sweep s = 0..3 carries the state H (fp32 MFMA accumulators,
@@ -159,11 +164,18 @@ __device__ __forceinline__ Seq seq_of(const BwdParams& prm, int n, int h) {
 }  // namespace bwd
 
 // ============================================================================
-// Chunk-start states.  One workgroup (4 waves) per (sequence, head, 64-column
-// slice).  Wave w owns state columns [16w, 16w+16) of the slice for all d_k
-// rows as H^T tiles (MFMA accumulators: lane holds 4 columns x 1 channel).
+// Chunk-start states (REV = false) and segment state gradients (REV = true).
+// One workgroup (4 waves) per (sequence, head, 64-column slice), or per
+// (sequence, head, segment > 0, slice).  Wave w owns state columns
+// [16w, 16w+16) of the slice for all d_k rows as transposed tiles (MFMA
+// accumulators: lane holds 4 columns x 1 channel).
+//  * REV = false, forward over the chunks: store S (bf16), then
+//    S <- diag(2^Gamma_last) S + (k 2^(Gamma_last - Gamma))^T v.
+//  * REV = true, backward over the segment's chunks from B = 0:
+//    B <- diag(2^Gamma_last) B + (q 2^Gamma)^T dO; the result and the
+//    segment's decay exp(sum of its log-gates) go to the split workspace.
 // ============================================================================
-template <int DK>
+template <int DK, bool REV>
 __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
   using namespace bwd;
   constexpr int KP = DK + 8;       // k-bar tile pitch (elements)
@@ -178,16 +190,25 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, m = lane & 15, grp = lane >> 4;
   const int bid = blockIdx.x, nblk = gridDim.x;
   const int lin = prm.xcd_remap ? (bid & 7) * (nblk >> 3) + (bid >> 3) : bid;
-  const int unit = lin / prm.nvt, vt = lin - unit * prm.nvt;
+  const int item = lin / prm.nvt, vt = lin - item * prm.nvt;
+  int unit = item, seg = 0;
+  if constexpr (REV) {   // item = (unit, segment 1 .. nseg-1)
+    unit = item / (prm.nseg - 1);
+    seg = 1 + item - unit * (prm.nseg - 1);
+  }
   const int n = unit / prm.H, h = unit - n * prm.H;
   const int DV = prm.DV, vcol0 = vt * 64;
   const Seq sq = seq_of(prm, n, h);
   const int nch = (int)((sq.len + C - 1) / C);
+  // chunks [u_lo, u_hi) of this work item
+  const int u_lo = REV ? seg * (prm.seg_len / C) : 0;
+  const int u_hi = REV ? min(nch, (seg + 1) * (prm.seg_len / C)) : nch;
   unsigned short* const hs = prm.hs + sq.slot0 * DK * DV;
 
-  const __amdgpu_buffer_rsrc_t rs_k = seq_rsrc(prm.k, sq.r0 * DK, (int)(sq.len * DK * 2));
+  // REV: q and dO stand where k and v are
+  const __amdgpu_buffer_rsrc_t rs_k = seq_rsrc(REV ? prm.q : prm.k, sq.r0 * DK, (int)(sq.len * DK * 2));
   const __amdgpu_buffer_rsrc_t rs_g = seq_rsrc(prm.g, sq.r0 * DK, (int)(sq.len * DK * 2));
-  const __amdgpu_buffer_rsrc_t rs_v = seq_rsrc(prm.v, sq.r0 * DV, (int)(sq.len * DV * 2));
+  const __amdgpu_buffer_rsrc_t rs_v = seq_rsrc(REV ? prm.dout : prm.v, sq.r0 * DV, (int)(sq.len * DV * 2));
 
   // gating lane: tokens 4tg..4tg+3 x channels 8cg..8cg+7
   const bool gl = tid < NGL;
@@ -212,9 +233,10 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
   // state tiles: (nb = wave, cb = i)
   f32x4 Ht[CB];
   const int nb = wave;
+  float dsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // REV: the segment's log2 decay
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
-    if (prm.s0) {
+    if (!REV && prm.s0) {
       const float4 x = *reinterpret_cast<const float4*>(
           prm.s0 + ((long)unit * DK + 16 * i + m) * DV + vcol0 + 16 * nb + 4 * grp);
       Ht[i] = f32x4{x.x, x.y, x.z, x.w};
@@ -222,9 +244,10 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
       Ht[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  if (nch > 0) prefetch(0);
+  if (u_hi > u_lo) prefetch(REV ? u_hi - 1 : u_lo);
 
-  for (int u = 0; u < nch; ++u) {
+  for (int it_u = 0; it_u < u_hi - u_lo; ++it_u) {
+    const int u = REV ? u_hi - 1 - it_u : u_lo + it_u;
     if (gl) {
       float pp[4][8];
       const unsigned* gw[4] = {&rg[0].x, &rg[1].x, &rg[2].x, &rg[3].x};
@@ -250,6 +273,10 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
         for (int a = 0; a < 4; ++a) pp[a][i] += ex;   // Gamma of token 4tg + a
         last[i] = __shfl(x, lane | 15);                // Gamma of the chunk's last row
       }
+      if constexpr (REV) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dsum[i] += last[i];
+      }
       const unsigned* kw[4] = {&rk[0].x, &rk[1].x, &rk[2].x, &rk[3].x};
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
@@ -257,7 +284,7 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const unsigned w = kw[a][i >> 1];
-          kbv[i] = ((i & 1) ? hi_bf16(w) : lo_bf16(w)) * fast_exp2(last[i] - pp[a][i]);
+          kbv[i] = ((i & 1) ? hi_bf16(w) : lo_bf16(w)) * fast_exp2(REV ? pp[a][i] : last[i] - pp[a][i]);
         }
         *reinterpret_cast<uint4*>(kb + (4 * tg + a) * KP + 8 * cg) =
             uint4{pack_bf16x2(kbv[0], kbv[1]), pack_bf16x2(kbv[2], kbv[3]), pack_bf16x2(kbv[4], kbv[5]),
@@ -275,15 +302,16 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
       const int idx = tid + 256 * it, row = idx >> 3, un = idx & 7;
       *reinterpret_cast<uint4*>(vs + row * VP + 8 * un) = rv[it];
     }
-    if (u + 1 < nch) prefetch(u + 1);
+    if (it_u + 1 < u_hi - u_lo) prefetch(REV ? u - 1 : u + 1);
     barrier_lds();
 
     // H_u (the state entering chunk u) to the workspace, then the update
     unsigned short* const hu = hs + (long)u * DK * DV;
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
-      *reinterpret_cast<uint2*>(hu + (16 * i + m) * DV + vcol0 + 16 * nb + 4 * grp) =
-          pack4(Ht[i][0], Ht[i][1], Ht[i][2], Ht[i][3]);
+      if constexpr (!REV)
+        *reinterpret_cast<uint2*>(hu + (16 * i + m) * DV + vcol0 + 16 * nb + 4 * grp) =
+            pack4(Ht[i][0], Ht[i][1], Ht[i][2], Ht[i][3]);
       const float d = dec[16 * i + m];
       Ht[i] = Ht[i] * d;
     }
@@ -294,6 +322,21 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
       for (int i = 0; i < CB; ++i) mma32(Ht[i], x, tr32(kb, KP, 32 * ks, 16 * i, m, grp));
     }
     barrier_lds();
+  }
+  if constexpr (REV) {
+    const long it = (long)unit * prm.nseg + seg;
+    float* const bz = prm.seg_state + it * DK * DV;
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+      *reinterpret_cast<float4*>(bz + (16 * i + m) * DV + vcol0 + 16 * nb + 4 * grp) =
+          make_float4(Ht[i][0], Ht[i][1], Ht[i][2], Ht[i][3]);
+    if (gl && tg == 15 && vt == 0) {
+      float* const dz = prm.seg_decay + it * DK + 8 * cg;
+      *reinterpret_cast<float4*>(dz) =
+          make_float4(fast_exp2(dsum[0]), fast_exp2(dsum[1]), fast_exp2(dsum[2]), fast_exp2(dsum[3]));
+      *reinterpret_cast<float4*>(dz + 4) =
+          make_float4(fast_exp2(dsum[4]), fast_exp2(dsum[5]), fast_exp2(dsum[6]), fast_exp2(dsum[7]));
+    }
   }
 }
 
@@ -357,10 +400,13 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
   const bool sw = wave < CB;   // owns channels c0.. of the states, dq, dk, dg
   const bool vw = wave < NB;   // computes dv for columns n0..
   const int c0 = 16 * wave, n0 = 16 * wave;
-  const int unit = blockIdx.x;
+  const int item = blockIdx.x;                 // (unit, segment)
+  const int unit = item / prm.nseg, seg = item - unit * prm.nseg;
   const int n = unit / prm.H, h = unit - n * prm.H;
   const Seq sq = seq_of(prm, n, h);
   const int nch = (int)((sq.len + C - 1) / C);
+  const int u_lo = seg * (prm.seg_len / C);  // chunks [u_lo, u_hi) of this work item
+  const int u_hi = min(nch, (seg + 1) * (prm.seg_len / C));
   const __amdgpu_buffer_rsrc_t rs_q = seq_rsrc(prm.q, sq.r0 * DK, (int)(sq.len * DK * 2));
   const __amdgpu_buffer_rsrc_t rs_k = seq_rsrc(prm.k, sq.r0 * DK, (int)(sq.len * DK * 2));
   const __amdgpu_buffer_rsrc_t rs_g = seq_rsrc(prm.g, sq.r0 * DK, (int)(sq.len * DK * 2));
@@ -413,18 +459,22 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
     }
   };
 
+  // the state gradient entering this work item from later tokens: dS_T, or the
+  // segment scan's result when the sequence is split
   f32x4 Ht[NB], Bt[NB];
+  const float* const b_in = prm.nseg > 1 ? prm.seg_state + (long)item * DK * DV
+                                         : (prm.dsT ? prm.dsT + (long)unit * DK * DV : nullptr);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     Bt[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (sw && prm.dsT) {
-      const float4 x = *reinterpret_cast<const float4*>(prm.dsT + ((long)unit * DK + c0 + m) * DV + 16 * b + 4 * grp);
+    if (sw && b_in) {
+      const float4 x = *reinterpret_cast<const float4*>(b_in + (c0 + m) * DV + 16 * b + 4 * grp);
       Bt[b] = f32x4{x.x, x.y, x.z, x.w};
     }
   }
-  if (nch > 0) {
-    prefetch(nch - 1);
-    prefetch_state(nch - 1);
+  if (u_hi > u_lo) {
+    prefetch(u_hi - 1);
+    prefetch_state(u_hi - 1);
   }
 
   // bf16 operand of a 32-column step from two state tiles (see the kernel comment)
@@ -433,7 +483,7 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
                                            pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])});
   };
 
-  for (int u = nch - 1; u >= 0; --u) {
+  for (int u = u_hi - 1; u >= u_lo; --u) {
     const long row0 = (long)u * C;   // first token of this chunk (sequence-relative)
     // Per-lane LDS byte offsets (wave parts included); every access adds a
     // compile-time constant, which the DS instructions take as an immediate.
@@ -560,7 +610,7 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
     for (int s = 0; s < NS; ++s) {
       // the next chunk's inputs are requested half-way through this one: early
       // enough to arrive, late enough to keep the first half's registers free
-      if (s == NS / 2 && u > 0) prefetch(u - 1);
+      if (s == NS / 2 && u > u_lo) prefetch(u - 1);
       if (sw) {
         // H^ = 2^(b_s - Gamma_{s-1,last}) H
         const float f = *reinterpret_cast<const float*>(lds + oF + s * DK * 4 + fC);
@@ -610,7 +660,7 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
       for (int r = 0; r < 4; ++r) carry[r] = __shfl(p, 4 * grp + r);
     }
     // H is not needed again in this chunk: its registers take the next chunk's state
-    if (u > 0) prefetch_state(u - 1);
+    if (u > u_lo) prefetch_state(u - 1);
 
     // ======================= reverse sweep: dk, dv, dg =======================
 #pragma unroll
@@ -683,7 +733,7 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
     }
   }
 
-  if (sw && prm.ds0) {
+  if (sw && prm.ds0 && seg == 0) {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
       *reinterpret_cast<float4*>(prm.ds0 + ((long)unit * DK + c0 + m) * DV + 16 * b + 4 * grp) =
@@ -693,23 +743,33 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
 
 int launch_chunk_states(const BwdParams& prm, int dk, int nblocks, hipStream_t stream) {
   if (dk == 128)
-    hipLaunchKernelGGL((chunk_states_kernel<128>), dim3(nblocks), dim3(256), 0, stream, prm);
+    hipLaunchKernelGGL((chunk_states_kernel<128, false>), dim3(nblocks), dim3(256), 0, stream, prm);
   else if (dk == 64)
-    hipLaunchKernelGGL((chunk_states_kernel<64>), dim3(nblocks), dim3(256), 0, stream, prm);
+    hipLaunchKernelGGL((chunk_states_kernel<64, false>), dim3(nblocks), dim3(256), 0, stream, prm);
   else
     return -2;
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_chunk_bwd(const BwdParams& prm, int dk, int dv, int units, hipStream_t stream) {
+int launch_chunk_bstates(const BwdParams& prm, int dk, int nblocks, hipStream_t stream) {
+  if (dk == 128)
+    hipLaunchKernelGGL((chunk_states_kernel<128, true>), dim3(nblocks), dim3(256), 0, stream, prm);
+  else if (dk == 64)
+    hipLaunchKernelGGL((chunk_states_kernel<64, true>), dim3(nblocks), dim3(256), 0, stream, prm);
+  else
+    return -2;
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_chunk_bwd(const BwdParams& prm, int dk, int dv, int nblocks, hipStream_t stream) {
   if (dk == 128 && dv == 128)
-    hipLaunchKernelGGL((chunk_bwd_kernel<128, 128>), dim3(units), dim3(512), 0, stream, prm);
+    hipLaunchKernelGGL((chunk_bwd_kernel<128, 128>), dim3(nblocks), dim3(512), 0, stream, prm);
   else if (dk == 128 && dv == 64)
-    hipLaunchKernelGGL((chunk_bwd_kernel<128, 64>), dim3(units), dim3(512), 0, stream, prm);
+    hipLaunchKernelGGL((chunk_bwd_kernel<128, 64>), dim3(nblocks), dim3(512), 0, stream, prm);
   else if (dk == 64 && dv == 128)
-    hipLaunchKernelGGL((chunk_bwd_kernel<64, 128>), dim3(units), dim3(512), 0, stream, prm);
+    hipLaunchKernelGGL((chunk_bwd_kernel<64, 128>), dim3(nblocks), dim3(512), 0, stream, prm);
   else if (dk == 64 && dv == 64)
-    hipLaunchKernelGGL((chunk_bwd_kernel<64, 64>), dim3(units), dim3(512), 0, stream, prm);
+    hipLaunchKernelGGL((chunk_bwd_kernel<64, 64>), dim3(nblocks), dim3(512), 0, stream, prm);
   else
     return -2;
   return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -239,6 +239,7 @@ int gla_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* g,
   sp.dk = dk;
   sp.dv = dv;
   sp.nseg = nseg;
+  sp.reverse = 0;
   rc = gla::launch_seg_scan(sp, (int)units, s);
   if (rc != 0) return launch_status("gla_chunk_fwd_ws", rc, dk, dtype);
   // 3. the forward pass of every segment from its incoming state
@@ -253,7 +254,10 @@ size_t gla_chunk_bwd_workspace_size(int num_seqs, int B, int H, int T, int dk, i
   const long long nseq = num_seqs > 0 ? num_seqs : B;
   const long long tokens = num_seqs > 0 ? (long long)T : (long long)B * T;
   const long long slots = nseq + tokens / 64 + 1;
-  return ((size_t)H * slots * dk * dv * 2 + 255) / 256 * 256;
+  const size_t states = ((size_t)H * slots * dk * dv * 2 + 255) / 256 * 256;
+  int seg_len = T;
+  const int nseg = split_plan(num_seqs > 0, dtype, nseq * H, T, seg_len);
+  return states + (nseg > 1 ? split_bytes(nseq * H, nseg, dk, dv) : 0);
 }
 
 int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
@@ -334,11 +338,48 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
   prm.nvt = nvt;
   prm.slots = (int)(nseq + tokens / 64 + 1);
   prm.xcd_remap = ((units * nvt) % 8 == 0) ? 1 : 0;
+  // sequence split: as in the forward, fixed-length sequences of too few units
+  // to fill the device are cut into segments of whole chunks
+  int seg_len = T;
+  const int nseg = split_plan(cu_seqlens != nullptr, dtype, units, T, seg_len);
+  prm.nseg = nseg;
+  prm.seg_len = nseg > 1 ? seg_len : (T > 0 ? (T + 63) / 64 * 64 : 64);
+  if (cu_seqlens) prm.seg_len = 1 << 30;   // one segment whatever the packed lengths
+  prm.seg_state = nullptr;
+  prm.seg_decay = nullptr;
+  if (nseg > 1) {
+    char* const sp = static_cast<char*>(workspace) + ((size_t)H * prm.slots * dk * dv * 2 + 255) / 256 * 256;
+    const size_t st_bytes = ((size_t)units * nseg * dk * dv * sizeof(float) + 255) / 256 * 256;
+    prm.seg_state = reinterpret_cast<float*>(sp);
+    prm.seg_decay = reinterpret_cast<float*>(sp + st_bytes);
+  }
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  // 1. the state entering every chunk, 2. the gradients chunk by chunk, last to first
+  // 1. the state entering every chunk
   int rc = gla::launch_chunk_states(prm, dk, (int)(units * nvt), s);
   if (rc != 0) return launch_status(fn, rc, dk, dtype);
-  rc = gla::launch_chunk_bwd(prm, dk, dv, (int)units, s);
+  if (nseg > 1) {
+    // 2. each later segment's own state gradient and decay, 3. every segment's
+    //    incoming state gradient (segments last to first, from d_final_state)
+    const long long nb2 = units * (nseg - 1) * nvt;
+    if (!fits_i32(nb2) || !fits_i32(units * nseg))
+      return fail(GLA_ERR_INVALID_ARG, "%s: %lld work items", fn, nb2);
+    prm.xcd_remap = (nb2 % 8 == 0) ? 1 : 0;
+    rc = gla::launch_chunk_bstates(prm, dk, (int)nb2, s);
+    if (rc != 0) return launch_status(fn, rc, dk, dtype);
+    gla::SegScanParams sp;
+    sp.s0 = d_final_state;
+    sp.sT = nullptr;
+    sp.seg_state = prm.seg_state;
+    sp.seg_decay = prm.seg_decay;
+    sp.dk = dk;
+    sp.dv = dv;
+    sp.nseg = nseg;
+    sp.reverse = 1;
+    rc = gla::launch_seg_scan(sp, (int)units, s);
+    if (rc != 0) return launch_status(fn, rc, dk, dtype);
+  }
+  // 4. the gradients chunk by chunk, last to first, per (unit, segment)
+  rc = gla::launch_chunk_bwd(prm, dk, dv, (int)(units * nseg), s);
   return launch_status(fn, rc, dk, dtype);
 }
 

@@ -46,6 +46,7 @@ struct SegScanParams {
   float* seg_state;  // in: states from zero; out: incoming states
   const float* seg_decay;
   int dk, dv, nseg;
+  int reverse;       // 1: segments from last to first (the state gradient of the backward pass)
 };
 
 // Arguments of the decode step kernel.
@@ -80,6 +81,14 @@ struct BwdParams {
   int nvt;               // DV / 64 column slices (state pass work items per unit)
   int slots;             // chunk-state slots per head: sequences + tokens / 64 + 1
   int xcd_remap;         // state pass: consecutive work items share an XCD
+  // Sequence split (fixed-length inputs; nseg = 1 otherwise): nseg segments of
+  // seg_len tokens (a multiple of 64, the last one shorter).  The backward work
+  // items are (sequence, head, segment); a segment's incoming state gradient
+  // comes from the gradient-state pass and the reverse segment scan.
+  int nseg;
+  int seg_len;
+  float* seg_state;      // [units][nseg][dk][dv] fp32: a segment's state gradient from zero, then its incoming one
+  float* seg_decay;      // [units][nseg][dk] fp32: exp of the segment's summed log-gates
 };
 
 // Each returns 0 on success, -1 if the launch failed, -2 if no kernel exists
@@ -89,7 +98,8 @@ int launch_chunk_fwd_pipe(const ChunkParams& prm, int dk, bool state_only, int n
                           hipStream_t stream);
 int launch_seg_scan(const SegScanParams& prm, int units, hipStream_t stream);
 int launch_chunk_states(const BwdParams& prm, int dk, int nblocks, hipStream_t stream);
-int launch_chunk_bwd(const BwdParams& prm, int dk, int dv, int units, hipStream_t stream);
+int launch_chunk_bstates(const BwdParams& prm, int dk, int nblocks, hipStream_t stream);
+int launch_chunk_bwd(const BwdParams& prm, int dk, int dv, int nblocks, hipStream_t stream);
 int launch_recurrent_step(const StepParams& prm, int units, int dk, int dv, int dtype,
                           hipStream_t stream);
 

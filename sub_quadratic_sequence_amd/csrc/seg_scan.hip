@@ -11,6 +11,12 @@
 // it replaces each S_zero by the segment's incoming state S_start, in place,
 // and writes the state after the last segment as the final state.
 //
+// The backward pass uses the same scan in the other direction: the gradient of
+// the state obeys B_start = diag(a) B_end + B_zero over a segment (B_zero from
+// the segment's own outputs), so with `reverse` the segments are visited from
+// last to first, starting from the gradient of the final state, and each slot
+// receives the gradient entering its segment from the later ones.
+//
 // One thread owns 4 consecutive elements of the d_k x d_v state for every
 // segment of its unit; elements are independent, so 256 threads x (d_k d_v /
 // 1024) workgroups per unit stream the states with 16-byte accesses.
@@ -27,9 +33,14 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(SegScanParams prm) {
   const long dkdv = (long)prm.dk * prm.dv;
   float4 S = prm.s0 ? *reinterpret_cast<const float4*>(prm.s0 + unit * dkdv + e)
                     : make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int sgi = 0; sgi < prm.nseg; ++sgi) {
+  for (int k = 0; k < prm.nseg; ++k) {
+    const int sgi = prm.reverse ? prm.nseg - 1 - k : k;
     const long it = (long)unit * prm.nseg + sgi;
     float4* slot = reinterpret_cast<float4*>(prm.seg_state + it * dkdv + e);
+    if (k == prm.nseg - 1 && !prm.sT) {   // nothing after the last segment is needed
+      *slot = S;
+      break;
+    }
     const float4 z = *slot;
     *slot = S;
     const float a = prm.seg_decay[it * prm.dk + row];

@@ -159,8 +159,14 @@ def test_chunk_fwd_ws_rejects_workspace(lib, ws, nbytes, needle):
 
 def test_bwd_workspace_size(lib):
     lib.gla_chunk_bwd_workspace_size.restype = ctypes.c_size_t
-    # training shape: 16 heads x (8 sequences + 16384 / 64 tokens + 1) chunk states of 128 x 128 bf16
-    assert lib.gla_chunk_bwd_workspace_size(0, 8, 16, 2048, 128, 128, 64, 0) == 16 * 265 * 128 * 128 * 2
+    # training shape: 16 heads x (8 sequences + 16384 / 64 tokens + 1) chunk states of 128 x 128
+    # bf16, plus the sequence split (128 units < 256 compute units: 2 segments per sequence):
+    # fp32 state gradients and decays per (unit, segment)
+    states = 16 * 265 * 128 * 128 * 2
+    split = 128 * 2 * 128 * 128 * 4 + 128 * 2 * 128 * 4
+    assert lib.gla_chunk_bwd_workspace_size(0, 8, 16, 2048, 128, 128, 64, 0) == states + split
+    # enough units to fill the device: no split
+    assert lib.gla_chunk_bwd_workspace_size(0, 16, 16, 2048, 128, 128, 64, 0) == 16 * 529 * 128 * 128 * 2
     # packed: 16 heads x (16 sequences + 33000 // 64 + 1) states of 128 x 64, rounded up to 256 bytes
     assert lib.gla_chunk_bwd_workspace_size(16, 1, 16, 33000, 128, 64, 64, 0) == 16 * 532 * 128 * 64 * 2
     assert lib.gla_chunk_bwd_workspace_size(0, 8, 16, 2048, 128, 128, 64, 1) == 0   # fp32

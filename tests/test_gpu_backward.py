@@ -98,6 +98,24 @@ def test_bwd_matches_oracle(dev, B, H, T, dk, dv, gate):
     _check(d, _gpu_bwd(dev, d), f"bwd B{B} H{H} T{T} dk{dk} dv{dv} {gate}")
 
 
+@pytest.mark.parametrize("B,H,T,dk,dv,gate", [
+    (1, 2, 1000, 128, 128, "weak"),    # 2 segments of 8 chunks, ragged tail
+    (1, 1, 3000, 128, 128, "strong"),  # 5 segments
+    (2, 2, 2050, 64, 64, "weak"),      # 4 segments, the last one a single token
+    (1, 2, 1100, 128, 64, "strong"),
+])
+def test_bwd_sequence_split(dev, B, H, T, dk, dv, gate):
+    from sub_quadratic_sequence_amd import gla
+
+    say(f"gla_chunk_bwd sequence split B={B} H={H} T={T} dk={dk} dv={dv} gate={gate} s0 dsT")
+    d = _case(B, H, T, dk, dv, gate=gate)
+    # the split is in use: its state-gradient workspace is part of the size
+    nch = (T + 63) // 64
+    unsplit = (H * (B + B * T // 64 + 1) * dk * dv * 2 + 255) // 256 * 256
+    assert gla.bwd_workspace_size(d["q"].to(dev), d["v"].to(dev)) > unsplit, nch
+    _check(d, _gpu_bwd(dev, d), f"bwd split B{B} H{H} T{T} dk{dk} dv{dv} {gate}")
+
+
 def test_bwd_without_initial_or_final_state(dev):
     say("gla_chunk_bwd B=2 H=2 T=200 d128 no s0, no dsT")
     d = _case(2, 2, 200, 128, 128, s0=False, final=False)
