@@ -1,4 +1,5 @@
-"""Seeded synthetic inputs for the GLA forward, backward and decode workloads.
+"""Seeded synthetic inputs for the GLA forward, backward and decode workloads,
+and for the Gated DeltaNet (GDN) chunk forward.
 
 This module only draws random numbers and casts them; it holds none of the
 method's arithmetic, so both the HIP path's tests and the oracle can consume
@@ -10,6 +11,10 @@ Gate recipes (g = log alpha, one value per key channel and token):
   * ``weak``   g = logsigmoid(z) / 16            (alpha close to 1)
   * ``strong`` g = logsigmoid(2 z - 1)            (tau = 1; alpha far from 1)
 Edge-case tests may also ask for ``zero`` (g = 0, i.e. alpha = 1).
+
+GDN (``gdn_inputs``): one forget gate g = log alpha and one update gate beta
+per token and head ([B, H, T], fp32); q and k drawn N(0, 1) and scaled to unit
+L2 norm per token before the cast, v ~ N(0, 1), beta = sigmoid(N(0, 1)).
 """
 from __future__ import annotations
 
@@ -72,8 +77,12 @@ DECODE_BF16 = DecodeWorkload("gla_decode_n256h16d128_x64", N=256, H=16, dk=128, 
 # from ``upstream_grads``).
 TRAIN_BWD_BF16 = dataclasses.replace(TRAIN_BF16, name="gla_bwd_b8h16t2048d128_bf16")
 
+# Gated DeltaNet chunk forward at the training shape (per-token scalar gates).
+GDN_TRAIN_BF16 = ChunkWorkload("gdn_fwd_b8h16t2048d128_bf16", B=8, H=16, T=2048, dk=128, dv=128,
+                               dtype="bf16", seed=6)
+
 WORKLOADS = {w.name: w for w in (TINY_FP32, TRAIN_BF16, LONG_BF16, VARLEN_BF16, DECODE_BF16,
-                                 TRAIN_BWD_BF16)}
+                                 TRAIN_BWD_BF16, GDN_TRAIN_BF16)}
 
 
 def _gate(z: torch.Tensor, kind: str) -> torch.Tensor:
@@ -124,6 +133,49 @@ def chunk_inputs(w: ChunkWorkload, *, T: Optional[int] = None, B: Optional[int] 
                 B=B, H=H, T=T, nseq=nseq)
 
 
+def gdn_inputs(w: ChunkWorkload, *, T: Optional[int] = None, B: Optional[int] = None,
+               H: Optional[int] = None, seed: Optional[int] = None,
+               lengths: Optional[list] = None, gate: Optional[str] = None,
+               s0: Optional[bool] = None, dk: Optional[int] = None, dv: Optional[int] = None):
+    """Draw one batch for a GDN forward workload.
+
+    Returns a dict of CPU tensors: q, k [B,H,T,dk] (unit L2 norm per token
+    before the cast) and v [B,H,T,dv] in the workload dtype; g (log of the
+    forget gate) and beta [B,H,T] fp32; ``s0`` [Nseq,H,dk,dv] fp32 or None;
+    ``cu_seqlens`` int32 [Nseq+1] or None (varlen: B == 1, T = packed total).
+    """
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    dk = w.dk if dk is None else dk
+    dv = w.dv if dv is None else dv
+    gate = w.gate if gate is None else gate
+    want_s0 = w.s0 if s0 is None else s0
+    gen = torch.Generator().manual_seed(w.seed if seed is None else seed)
+    cu = None
+    if w.varlen or lengths is not None:
+        if lengths is None:
+            lengths = torch.randint(w.len_lo, w.len_hi + 1, (w.varlen,), generator=gen).tolist()
+        cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+        cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+        B, T, nseq = 1, int(cu[-1]), len(lengths)
+    else:
+        T = w.T if T is None else T
+        nseq = B
+    q = torch.randn(B, H, T, dk, generator=gen)
+    k = torch.randn(B, H, T, dk, generator=gen)
+    v = torch.randn(B, H, T, dv, generator=gen)
+    z = torch.randn(B, H, T, generator=gen)
+    zb = torch.randn(B, H, T, generator=gen)
+    s0_t = torch.randn(nseq, H, dk, dv, generator=gen) * 0.1 if want_s0 else None
+    q = q / q.norm(dim=-1, keepdim=True).clamp_min(1e-6)
+    k = k / k.norm(dim=-1, keepdim=True).clamp_min(1e-6)
+    g = _gate(z, gate)
+    beta = torch.sigmoid(zb)
+    dt = w.torch_dtype
+    return dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), g=g.float(), beta=beta.float(), s0=s0_t,
+                cu_seqlens=cu, B=B, H=H, T=T, nseq=nseq)
+
+
 def decode_inputs(w: DecodeWorkload, *, N: Optional[int] = None, H: Optional[int] = None,
                   steps: Optional[int] = None, seed: Optional[int] = None,
                   dk: Optional[int] = None, dv: Optional[int] = None):
@@ -163,5 +215,6 @@ def expected_varlen_tokens(w: ChunkWorkload) -> float:
 
 
 __all__ = ["ChunkWorkload", "DecodeWorkload", "WORKLOADS", "TINY_FP32", "TRAIN_BF16",
-           "LONG_BF16", "VARLEN_BF16", "DECODE_BF16", "TRAIN_BWD_BF16", "chunk_inputs",
+           "LONG_BF16", "VARLEN_BF16", "DECODE_BF16", "TRAIN_BWD_BF16", "GDN_TRAIN_BF16",
+           "chunk_inputs", "gdn_inputs",
            "decode_inputs", "upstream_grads", "expected_varlen_tokens"]
