@@ -183,6 +183,38 @@ int gla_recurrent_step(const void* q, const void* k, const void* v, const void* 
                        float* state, void* o, int N, int H, int dk, int dv, int dtype,
                        void* stream);
 
+/*
+ * Chunkwise Gated DeltaNet forward (page "Qwen Team Releases FlashQLA for
+ * High-Performance Linear Attention": the GDN update with a forget gate alpha
+ * and an update gate beta per token, the transition I - beta k k^T, and its
+ * chunkwise WY form).  For every unit (sequence, head) and token t in order:
+ *
+ *     S_t = alpha_t (I - beta_t k_t^T k_t) S_{t-1} + beta_t k_t^T v_t,
+ *     o_t = q_t S_t,            alpha_t = exp(g_t),
+ *
+ * S a dk x dv fp32 matrix, k_t a row vector.  The keys are meant to have unit
+ * L2 norm (not checked); beta in [0, 1], g <= 0 (not checked; g = -inf is
+ * allowed and acts as alpha = 0).
+ *
+ *   q, k          [B, H, T, dk]  bf16        v, o  [B, H, T, dv]  bf16
+ *   g, beta       [B, H, T]      fp32 (one value per token and head)
+ *   initial_state [Nseq, H, dk, dv] fp32 or NULL (zeros)
+ *   final_state   [Nseq, H, dk, dv] fp32 or NULL (not written); may alias
+ *                 initial_state
+ *   cu_seqlens    packed sequences exactly as for gla_chunk_fwd (B == 1,
+ *                 device int32 [num_seqs + 1]); NULL for fixed length
+ *
+ * q, k, v, o, the states and cu_seqlens must be 16-byte aligned, g and beta
+ * 4-byte aligned, all contiguous device memory owned by the caller.  The call
+ * only enqueues work on `stream` (a hipStream_t; NULL is the null stream), keeps
+ * no pointer and allocates nothing.  Supported: dtype GLA_BF16, dk in {64, 128},
+ * dv a multiple of 64 up to 512, chunk_size 64; others give GLA_ERR_UNSUPPORTED.
+ */
+int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                  const float* initial_state, void* o, float* final_state,
+                  const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk, int dv,
+                  int chunk_size, int dtype, void* stream);
+
 /* Static, human-readable name of a gla_status value. */
 const char* gla_status_string(int status);
 

@@ -8,7 +8,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgla.so")
 SOURCES = ["gla_api.hip", "chunk_fwd.hip", "chunk_fwd_pipe.hip", "seg_scan.hip", "recurrent_step.hip",
-           "chunk_bwd.hip"]
+           "chunk_bwd.hip", "gdn_fwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -383,6 +383,72 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
   return launch_status(fn, rc, dk, dtype);
 }
 
+int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                  const float* initial_state, void* o, float* final_state, const int32_t* cu_seqlens,
+                  int num_seqs, int B, int H, int T, int dk, int dv, int chunk_size, int dtype,
+                  void* stream) {
+  g_last_error[0] = '\0';
+  const char* fn = "gdn_chunk_fwd";
+  if (dtype != GLA_BF16 && dtype != GLA_F32)
+    return fail(GLA_ERR_INVALID_ARG, "%s: dtype %d is not GLA_BF16 or GLA_F32", fn, dtype);
+  if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0)
+    return fail(GLA_ERR_INVALID_ARG, "%s: B=%d H=%d T=%d dk=%d dv=%d must be positive (T >= 0)", fn,
+                B, H, T, dk, dv);
+  if (dtype != GLA_BF16)
+    return fail(GLA_ERR_UNSUPPORTED, "%s: only GLA_BF16 is implemented", fn);
+  if (chunk_size != 64)
+    return fail(GLA_ERR_UNSUPPORTED, "%s: chunk_size %d (only 64 is implemented)", fn, chunk_size);
+  if (dk != 64 && dk != 128)
+    return fail(GLA_ERR_UNSUPPORTED, "%s: dk=%d (64 or 128)", fn, dk);
+  if (dv % 64 != 0 || dv > 512)
+    return fail(GLA_ERR_UNSUPPORTED, "%s: dv=%d must be a multiple of 64 up to 512", fn, dv);
+  int nseq = B;
+  if (cu_seqlens) {
+    if (B != 1)
+      return fail(GLA_ERR_INVALID_ARG, "%s: packed sequences (cu_seqlens) need B == 1, got %d", fn, B);
+    if (num_seqs <= 0)
+      return fail(GLA_ERR_INVALID_ARG, "%s: num_seqs=%d must be positive with cu_seqlens", fn,
+                  num_seqs);
+    nseq = num_seqs;
+  }
+  if (!fits_i32((long long)B * H * T * dv) || !fits_i32((long long)B * H * T * dk) ||
+      !fits_i32((long long)nseq * H * dk * dv))
+    return fail(GLA_ERR_INVALID_ARG, "%s: tensor sizes exceed int32 indexing", fn);
+  const bool any_tokens = (long long)B * H * T > 0;
+  if (any_tokens && (!q || !k || !v || !g || !beta || !o))
+    return fail(GLA_ERR_INVALID_ARG, "%s: q, k, v, g, beta and o must be non-null", fn);
+  const void* ptrs[] = {q, k, v, o, initial_state, final_state, cu_seqlens};
+  const char* names[] = {"q", "k", "v", "o", "initial_state", "final_state", "cu_seqlens"};
+  for (int i = 0; i < 7; ++i)
+    if (ptrs[i] && !aligned16(ptrs[i]))
+      return fail(GLA_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, names[i]);
+  if ((g && (reinterpret_cast<uintptr_t>(g) & 3u)) || (beta && (reinterpret_cast<uintptr_t>(beta) & 3u)))
+    return fail(GLA_ERR_INVALID_ARG, "%s: g and beta must be 4-byte aligned", fn);
+  const long long units = (long long)nseq * H;
+  const int nvt = dv / 64;
+  const long long nblocks = units * nvt;
+  if (!fits_i32(nblocks))
+    return fail(GLA_ERR_INVALID_ARG, "%s: %lld work items", fn, nblocks);
+  if (!any_tokens && !final_state) return GLA_OK;
+  gla::GdnParams prm;
+  prm.q = q;
+  prm.k = k;
+  prm.v = v;
+  prm.g = g;
+  prm.beta = beta;
+  prm.s0 = initial_state;
+  prm.o = o;
+  prm.sT = final_state;
+  prm.cu = cu_seqlens;
+  prm.H = H;
+  prm.T = T;
+  prm.DV = dv;
+  prm.nvt = nvt;
+  prm.xcd_remap = (nblocks % 8 == 0) ? 1 : 0;
+  const int rc = gla::launch_gdn_chunk_fwd(prm, dk, (int)nblocks, reinterpret_cast<hipStream_t>(stream));
+  return launch_status(fn, rc, dk, dtype);
+}
+
 int gla_recurrent_step(const void* q, const void* k, const void* v, const void* g, float* state,
                        void* o, int N, int H, int dk, int dv, int dtype, void* stream) {
   g_last_error[0] = '\0';

@@ -91,6 +91,24 @@ struct BwdParams {
   float* seg_decay;      // [units][nseg][dk] fp32: exp of the segment's summed log-gates
 };
 
+// Arguments of the Gated DeltaNet chunk forward (see include/gla.h for meanings).
+struct GdnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;      // [B, H, T] log forget gate
+  const float* beta;   // [B, H, T] update gate
+  const float* s0;     // may be null (zeros)
+  void* o;
+  float* sT;           // may be null (not written)
+  const int* cu;       // packed varlen offsets on the device, or null
+  int H;
+  int T;               // tokens per sequence (fixed) or total packed tokens
+  int DV;
+  int nvt;             // DV / 64 column slices
+  int xcd_remap;       // 1: consecutive work items share an XCD (grid size % 8 == 0)
+};
+
 // Each returns 0 on success, -1 if the launch failed, -2 if no kernel exists
 // for the shape/dtype.
 int launch_chunk_fwd(const ChunkParams& prm, int dk, int dtype, int nblocks, hipStream_t stream);
@@ -100,6 +118,7 @@ int launch_seg_scan(const SegScanParams& prm, int units, hipStream_t stream);
 int launch_chunk_states(const BwdParams& prm, int dk, int nblocks, hipStream_t stream);
 int launch_chunk_bstates(const BwdParams& prm, int dk, int nblocks, hipStream_t stream);
 int launch_chunk_bwd(const BwdParams& prm, int dk, int dv, int nblocks, hipStream_t stream);
+int launch_gdn_chunk_fwd(const GdnParams& prm, int dk, int nblocks, hipStream_t stream);
 int launch_recurrent_step(const StepParams& prm, int units, int dk, int dv, int dtype,
                           hipStream_t stream);
 

@@ -48,6 +48,8 @@ def load_library():
         lib.gla_chunk_bwd_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
         lib.gla_chunk_bwd.restype = I
         lib.gla_chunk_bwd.argtypes = [P] * 13 + [I] * 8 + [P, ctypes.c_size_t, P]
+        lib.gdn_chunk_fwd.restype = I
+        lib.gdn_chunk_fwd.argtypes = [P] * 9 + [I] * 8 + [P]
         lib.gla_recurrent_step.restype = I
         lib.gla_recurrent_step.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
         lib.gla_status_string.restype = ctypes.c_char_p
@@ -280,3 +282,49 @@ def gla_recurrent_step(q, k, v, g, state, out=None):
     if rc != GLA_OK:
         raise GLAError(rc, last_error())
     return out
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=False,
+                  cu_seqlens=None, chunk_size: int = 64, out=None, final_state=None):
+    """Chunkwise Gated DeltaNet forward (C entry point ``gdn_chunk_fwd``).
+
+    q, k: [B, H, T, dk] and v: [B, H, T, dv] bfloat16; g (log forget gate) and
+    beta (update gate): [B, H, T] float32; initial_state: [Nseq, H, dk, dv]
+    float32 or None; cu_seqlens: int32 [Nseq+1] on the GPU for packed sequences
+    (B == 1).  Returns ``(o, final_state)``; ``final_state`` is None unless
+    ``output_final_state`` (or ``final_state`` is passed; it may alias
+    ``initial_state``).
+    """
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    _check_gpu("q", q)
+    dt = q.dtype
+    _check_gpu("k", k, dt, q.shape)
+    _check_gpu("v", v, dt, (B, H, T, dv))
+    _check_gpu("g", g, torch.float32, (B, H, T))
+    _check_gpu("beta", beta, torch.float32, (B, H, T))
+    nseq = B
+    num_seqs = 0
+    if cu_seqlens is not None:
+        _check_gpu("cu_seqlens", cu_seqlens, torch.int32)
+        num_seqs = cu_seqlens.numel() - 1
+        nseq = num_seqs
+    if initial_state is not None:
+        _check_gpu("initial_state", initial_state, torch.float32, (nseq, H, dk, dv))
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=dt, device=q.device)
+    else:
+        _check_gpu("out", out, dt, (B, H, T, dv))
+    if final_state is None and output_final_state:
+        final_state = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif final_state is not None:
+        _check_gpu("final_state", final_state, torch.float32, (nseq, H, dk, dv))
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                               _ptr(out), _ptr(final_state), _ptr(cu_seqlens), num_seqs, B, H, T,
+                               dk, dv, int(chunk_size), _dtype_code(q), ctypes.c_void_p(stream))
+    if rc != GLA_OK:
+        raise GLAError(rc, last_error())
+    return out, final_state

@@ -15,7 +15,8 @@ HEADER = os.path.join(ROOT, "include", "gla.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gla_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*((?:gla|gdn)_\w+)\s*\(", text,
+                                 flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -31,7 +32,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    assert names == ["gla_chunk_bwd", "gla_chunk_bwd_workspace_size", "gla_chunk_fwd",
+    assert names == ["gdn_chunk_fwd", "gla_chunk_bwd", "gla_chunk_bwd_workspace_size", "gla_chunk_fwd",
                      "gla_chunk_fwd_workspace_size", "gla_chunk_fwd_ws", "gla_last_error",
                      "gla_recurrent_step", "gla_status_string"]
 
@@ -210,3 +211,38 @@ def test_chunk_bwd_rejects(lib, kw, status, needle):
 
 def test_chunk_bwd_zero_tokens_without_state_gradient_is_a_noop(lib):
     assert _bwd(lib, T=0) == 0
+
+
+def _gdn(lib, **kw):
+    P = ctypes.c_void_p
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None, o=FAKE, sT=None, cu=None,
+             num_seqs=0, B=1, H=2, T=64, dk=128, dv=128, C=64, dtype=0)
+    a.update(kw)
+    return lib.gdn_chunk_fwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]), P(a["s0"]),
+                             P(a["o"]), P(a["sT"]), P(a["cu"]), a["num_seqs"], a["B"], a["H"],
+                             a["T"], a["dk"], a["dv"], a["C"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(beta=None), 1, "non-null"),
+    (dict(g=None), 1, "non-null"),
+    (dict(q=FAKE + 8), 1, "q is not 16-byte aligned"),
+    (dict(g=FAKE + 2), 1, "4-byte aligned"),
+    (dict(B=0), 1, "must be positive"),
+    (dict(dtype=1), 2, "only GLA_BF16"),
+    (dict(dtype=9), 1, "dtype 9"),
+    (dict(C=32), 2, "chunk_size"),
+    (dict(dk=256), 2, "dk=256"),
+    (dict(dv=100), 2, "dv=100"),
+    (dict(cu=FAKE, B=2, num_seqs=2), 1, "B == 1"),
+    (dict(B=4096, H=4096, T=4096), 1, "int32"),
+])
+def test_gdn_chunk_fwd_rejects(lib, kw, status, needle):
+    from sub_quadratic_sequence_amd import gla
+
+    assert _gdn(lib, **kw) == status
+    assert needle in gla.last_error(), gla.last_error()
+
+
+def test_gdn_zero_tokens_without_outputs_is_a_noop(lib):
+    assert _gdn(lib, q=None, k=None, v=None, g=None, beta=None, o=None, T=0) == 0

@@ -1,0 +1,139 @@
+"""GPU parity of the Gated DeltaNet chunk forward (gdn_chunk_fwd through the C
+ABI) against the fp64 GDN oracle on the same seeded inputs, at the bf16
+tolerance (per-unit max error over max |reference|, see parity.py).  Every
+test prints the case it is about to run before touching the GPU."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import gdn as ogdn
+from parity import TOL_BF16, to64, unit_err_fixed, unit_err_varlen
+from sub_quadratic_sequence_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = min(16, os.cpu_count() or 1)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sub_quadratic_sequence_amd import gla
+
+    gla.load_library()
+    return torch.device("cuda:0")
+
+
+def say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _run(dev, d, s0=None, final=True, cu=None):
+    from sub_quadratic_sequence_amd import gla
+
+    o, sf = gla.gdn_chunk_fwd(*(d[n].to(dev) for n in ("q", "k", "v", "g", "beta")),
+                              initial_state=None if s0 is None else s0.to(dev),
+                              output_final_state=final,
+                              cu_seqlens=None if cu is None else cu.to(dev))
+    torch.cuda.synchronize()
+    return o, sf
+
+
+def _check(d, o, sf, s0, label, cu=None):
+    o_ref, s_ref = ogdn.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"], s0=s0,
+                                   cu_seqlens=cu, nthreads=NTHREADS)
+    assert np.all(np.isfinite(to64(o))) and np.all(np.isfinite(to64(sf)))
+    if cu is None:
+        e_o = unit_err_fixed(o, o_ref)
+    else:
+        e_o = unit_err_varlen(o, o_ref, cu)
+    e_s = unit_err_fixed(sf, s_ref)
+    print(f"{label}: O err {e_o:.3e}  S err {e_s:.3e}  (tol {TOL_BF16})", flush=True)
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16, (e_o, e_s)
+
+
+W = I.GDN_TRAIN_BF16
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 130, 300])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 192)])
+def test_shapes(dev, T, dk, dv):
+    say(f"gdn B2 H2 T{T} dk{dk} dv{dv} with S0")
+    d = I.gdn_inputs(W, B=2, H=2, T=T, dk=dk, dv=dv, s0=True, seed=100 + T)
+    o, sf = _run(dev, d, s0=d["s0"])
+    _check(d, o, sf, d["s0"], f"T{T} dk{dk} dv{dv}")
+
+
+@pytest.mark.parametrize("gate", ["weak", "strong", "zero"])
+def test_gates(dev, gate):
+    say(f"gdn B1 H4 T512 d128 gate={gate} no S0")
+    d = I.gdn_inputs(W, B=1, H=4, T=512, gate=gate, seed=7)
+    o, sf = _run(dev, d)
+    _check(d, o, sf, None, f"gate {gate}")
+
+
+def test_beta_zero_and_one(dev):
+    say("gdn beta = 0 (pure decay of S0) and beta = 1")
+    d = I.gdn_inputs(W, B=1, H=2, T=200, s0=True, seed=8)
+    d["beta"] = torch.zeros_like(d["beta"])
+    o, sf = _run(dev, d, s0=d["s0"])
+    _check(d, o, sf, d["s0"], "beta = 0")
+    d["beta"] = torch.ones_like(d["beta"])
+    o, sf = _run(dev, d, s0=d["s0"])
+    _check(d, o, sf, d["s0"], "beta = 1")
+
+
+def test_alpha_zero_tokens(dev):
+    say("gdn with alpha = 0 (g = -inf) at some tokens")
+    d = I.gdn_inputs(W, B=1, H=2, T=256, s0=True, seed=9)
+    d["g"][:, :, 17] = float("-inf")
+    d["g"][:, 1, 100:104] = float("-inf")
+    o, sf = _run(dev, d, s0=d["s0"])
+    _check(d, o, sf, d["s0"], "alpha = 0 tokens")
+
+
+def test_packed_sequences(dev):
+    lens = [5, 0, 700, 1, 64, 333, 128, 2]
+    say(f"gdn packed lengths {lens} H3 d128 with S0")
+    d = I.gdn_inputs(W, H=3, lengths=lens, s0=True, seed=10)
+    o, sf = _run(dev, d, s0=d["s0"], cu=d["cu_seqlens"])
+    _check(d, o, sf, d["s0"], "packed", cu=d["cu_seqlens"])
+
+
+def test_training_shape_sampled_units(dev):
+    say(f"{W.name} seed={W.seed} gdn_chunk_fwd (full size), oracle on sequences 0 and 7")
+    d = I.gdn_inputs(W)
+    o, sf = _run(dev, d)
+    sub = {n: d[n][[0, 7]] for n in ("q", "k", "v", "g", "beta")}
+    _check(sub, o[[0, 7]].cpu(), sf[[0, 7]].cpu(), None, W.name + " (sequences 0, 7)")
+
+
+def test_deterministic_and_in_place_state(dev):
+    from sub_quadratic_sequence_amd import gla
+
+    say("gdn bitwise determinism and final_state aliasing initial_state")
+    d = I.gdn_inputs(W, B=2, H=2, T=300, s0=True, seed=11)
+    args = [d[n].to(dev) for n in ("q", "k", "v", "g", "beta")]
+    s0 = d["s0"].to(dev)
+    o1, s1 = gla.gdn_chunk_fwd(*args, initial_state=s0, output_final_state=True)
+    o2, s2 = gla.gdn_chunk_fwd(*args, initial_state=s0, output_final_state=True)
+    st = s0.clone()
+    o3, s3 = gla.gdn_chunk_fwd(*args, initial_state=st, final_state=st)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert torch.equal(o1, o3) and torch.equal(s1, st)
+
+
+def test_split_call_composition(dev):
+    say("gdn: [0, 192) then [192, 300) from its final state equals one call")
+    d = I.gdn_inputs(W, B=1, H=2, T=300, s0=True, seed=12)
+    o, sf = _run(dev, d, s0=d["s0"])
+    a = {n: d[n][:, :, :192].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    b = {n: d[n][:, :, 192:].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    oa, sa = _run(dev, a, s0=d["s0"])
+    ob, sb = _run(dev, b, s0=sa.cpu())
+    assert unit_err_fixed(torch.cat([oa, ob], 2).float(), o.float()) < 1e-2
+    assert unit_err_fixed(sb, sf) < 1e-2
