@@ -7,7 +7,8 @@ stages run inside that call (gate cumsum, intra-chunk scores, P.V, inter term,
 state carry, varlen/tail handling).  Inputs are synthetic (seeded) and resident
 in HBM before timing starts.  The decode step (256 sequences x 16 heads,
 d=128, 64 consecutive steps) is timed in the same run and reported under
-"decode".  The fp64 CPU oracle is timed on the host on the same inputs.
+"decode"; the long-context, packed-sequence, backward and Gated DeltaNet
+workloads under keys of their own.  The fp64 CPU oracle is timed on the host on the same inputs.
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -57,6 +58,18 @@ def bwd_work(B, H, T, dk, dv, L, esz):
     tokens_heads = B * H * T
     flops = tokens_heads * 2 * (L * (3 * dk + 2 * dv) + 7 * dk * dv)
     bytes_ = tokens_heads * esz * ((3 * dk + 2 * dv) + (3 * dk + dv))
+    return flops, bytes_
+
+
+def gdn_work(B, H, T, dk, dv, C):
+    """Gated DeltaNet forward (bf16 q, k, v, o; fp32 g and beta per token).
+    FLOPs per token and head, as the chunk form computes them (full C x C
+    blocks): Q K^T and K K^T (4 C dk), the triangular solve and P U (2 C dv),
+    K S, Q S and the state update (6 dk dv).  Bytes: q, k, v read once, o
+    written once, g and beta read once, the fp32 final state written once."""
+    tokens_heads = B * H * T
+    flops = tokens_heads * (4 * C * dk + 2 * C * dv + 6 * dk * dv)
+    bytes_ = tokens_heads * (2 * (2 * dk + 2 * dv) + 8) + B * H * dk * dv * 4
     return flops, bytes_
 
 
@@ -252,6 +265,40 @@ def bench_backward(args, torch, gla, inputs):
     return dict(w=w, wall=wall, gpu=gpu, flops=flops, bytes=nbytes, tokens=w.B * w.T, steps=steps)
 
 
+def bench_gdn(args, torch, gla, inputs):
+    """The Gated DeltaNet chunk forward on the training shape (B8 H16 T2048 d128,
+    bf16, fp32 final state): one gdn_chunk_fwd call, one kernel.  The fp64 GDN
+    oracle is timed beside it on one sequence of the same batch (all heads)."""
+    w = inputs.GDN_TRAIN_BF16
+    log(f"[bench] gated deltanet {w.name}: generating inputs")
+    d = inputs.gdn_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, g, beta = (d[n].to(dev) for n in ("q", "k", "v", "g", "beta"))
+    o = torch.empty(w.B, w.H, w.T, w.dv, dtype=torch.bfloat16, device=dev)
+    sf = torch.empty(w.B, w.H, w.dk, w.dv, dtype=torch.float32, device=dev)
+
+    def step():
+        gla.gdn_chunk_fwd(q, k, v, g, beta, out=o, final_state=sf)
+
+    steps = max(1, args.steps // 2)
+    wall, gpu = time_launches(step, steps, max(1, args.warmup // 2), torch, args.preroll * 0.5)
+    flops, nbytes = gdn_work(w.B, w.H, w.T, w.dk, w.dv, 64)
+    res = dict(w=w, wall=wall, gpu=gpu, flops=flops, bytes=nbytes, tokens=w.B * w.T, steps=steps)
+    if not args.no_cpu_baseline:
+        from oracle import gdn as ogdn
+
+        threads = min(16, os.cpu_count() or 1)
+        t0 = time.perf_counter()
+        _, _, used = ogdn.recurrence(d["q"][:1], d["k"][:1], d["v"][:1], d["g"][:1], d["beta"][:1],
+                                     nthreads=threads, return_threads=True)
+        el = time.perf_counter() - t0
+        res["oracle"] = {"value": w.T / el, "unit": "tokens/s", "cores": used, "kind": "oracle",
+                         "sample": f"1 sequence x {w.H} heads x {w.T} tokens of the same batch "
+                                   "(fp64 GDN token recurrence, OpenMP over heads)",
+                         "seconds": round(el, 3)}
+    return res
+
+
 def cpu_baseline(fwd, min_seconds=12.0, max_passes=64):
     """The fp64 oracle as it stands, on the host, on the forward workload's own
     inputs: whole sequences (all heads, all tokens) of the batch are run, cycling
@@ -291,7 +338,9 @@ def main():
     ap.add_argument("--no-long", action="store_true",
                     help="skip the long-context and packed-sequence legs")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
-    ap.add_argument("--only", choices=["fwd", "decode", "long", "bwd", "copy", "pmc"], default=None,
+    ap.add_argument("--no-gdn", action="store_true", help="skip the Gated DeltaNet leg")
+    ap.add_argument("--only", choices=["fwd", "decode", "long", "bwd", "gdn", "copy", "pmc"],
+                    default=None,
                     help="profiling runs: launch only this part (copy = 512 MiB calibration "
                          "copy; pmc = copy, then forward, then decode, a few launches each)")
     args = ap.parse_args()
@@ -328,6 +377,11 @@ def main():
     if args.only == "bwd":
         bw = bench_backward(args, torch, gla, inputs)
         log(f"[bench] backward {bw['gpu'] * 1e6:.1f} us/call")
+        return
+    if args.only == "gdn":
+        args.no_cpu_baseline = True
+        gd = bench_gdn(args, torch, gla, inputs)
+        log(f"[bench] gated deltanet {gd['gpu'] * 1e6:.1f} us/call")
         return
     if args.only == "decode":
         dec = bench_decode(args, torch, gla, inputs)
@@ -423,6 +477,22 @@ def main():
                          "algorithmic_flops_per_call": bw["flops"],
                          "note": "two kernels per call: chunk-state pass, backward"},
         }
+    if not args.no_gdn:
+        gd = bench_gdn(args, torch, gla, inputs)
+        gbs = gd["bytes"] / gd["gpu"] / 1e9
+        tf = gd["flops"] / gd["gpu"] / 1e12
+        log(f"[bench] gated deltanet: {gd['gpu'] * 1e6:.1f} us/call ({gbs:.0f} GB/s, {tf:.1f} TFLOP/s)")
+        out["gated_deltanet"] = {
+            "workload": gd["w"].name, "us_per_call": gd["gpu"] * 1e6, "steps": gd["steps"],
+            "tokens_per_s": gd["tokens"] / gd["wall"], "tflop_s": tf,
+            "mfma_peak_frac": tf / MFMA_BF16_PEAK_TFLOPS,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": gd["bytes"],
+                         "algorithmic_flops_per_call": gd["flops"],
+                         "kernel": "gla::gdn_chunk_fwd_kernel<128>"},
+        }
+        if "oracle" in gd:
+            out["gated_deltanet"]["cpu_baseline"] = gd["oracle"]
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
         out["cpu_baseline"] = cpu_baseline(fwd)
