@@ -16,18 +16,24 @@
 //     S <- gamma_C S + (K * exp(G_C - G))^T U
 // Every exponential is of a non-positive argument, so no factor exceeds 1.
 //
-// Work decomposition: one workgroup of 4 waves per (sequence, head, 64-column
-// slice of d_v).  Wave w owns state columns [16w, 16w+16) of the slice for all
-// d_k rows in MFMA accumulators; it computes its columns of K S, U, O and the
-// state update.  The chunk-wide pieces (score blocks, the inverses of the four
-// 16x16 diagonal blocks of M) are split across the waves through LDS.
-// M^{-1} is never formed whole: each wave solves M U = R by 16-token block
-// forward substitution, U_p = T_pp (R_p - sum_{r<p} M_pr U_r), with T_pp the
-// inverse of diagonal block p.
-//
-// Per chunk: stage the tiles | scores, K S, S^T Q^T, R | diagonal inverses |
-// block solve, outputs, state update - four workgroup barriers.  The next
-// chunk's raw q, k, v, g, beta are loaded into registers one chunk ahead.
+// Work decomposition: one workgroup of 8 waves per (sequence, head, 64-column
+// slice of d_v), one producer and one consumer wave per SIMD, over two LDS
+// buffers.  The state-independent half of a chunk runs one chunk ahead of the
+// state-dependent half:
+//  * producer waves 0-3 stage chunk u+1 (q, k rows; the state keys
+//    (K exp(G_C - G))^T; V^T; the gates), then compute its score blocks
+//    (M below the diagonal blocks, the causal Gamma * Q K^T) and, wave w, the
+//    inverse T_ww of M's 16x16 diagonal block w, in fp32;
+//  * consumer wave 4 + c owns state columns [16c, 16c+16) for all d_k rows in
+//    MFMA accumulators and, for chunk u: K S and O = gamma Q S, R = beta (V -
+//    gamma K S), then the 16-token block forward substitution
+//    U_p = T_pp (R_p - sum_{r<p} M_pr U_r) (M^{-1} is never formed), O += P U,
+//    and the state update.
+// Two workgroup barriers per chunk: after the producers stage chunk u+1 (their
+// score blocks read each other's rows) and at the buffer swap.  The next
+// chunk's raw inputs are loaded into producer registers one chunk ahead.
+#include <type_traits>
+
 #include "gla_device.h"
 #include "gla_kernels.h"
 
@@ -40,21 +46,49 @@ constexpr int DVT = 64;                    // columns per workgroup
 constexpr int kBufferFlags = 0x00020000;   // gfx9 buffer descriptor word 3: raw 32-bit dwords
 constexpr float kGateFloor = -64.f;        // log-gates below this count as this (alpha = 0 included)
 
+// LDS tiles are dense; their 16- or 8-byte units are permuted within a row by
+// XOR with a function of the row, so that the producers' row writes and the
+// MFMA fragment reads of a 16-lane group reach distinct banks.
+//  * [token][channel] rows (q, k): 16-byte unit u of row r at u ^ f(r)
 template <int DK>
-struct alignas(16) Smem {
-  static constexpr int PK = DK + 8;        // [token][channel] pitch (elements)
-  static constexpr int PT = C + 8;         // [channel | column | token][token] pitch
-  unsigned short k[C * PK];                // K rows
-  unsigned short q[C * PK];                // Q rows
-  unsigned short kt[DK * PT];              // (K * exp(G_C - G))^T  [channel][token]
-  unsigned short vt[DVT * PT];             // V^T of the slice      [column][token]
-  unsigned short p[C * PT];                // Gamma * Q K^T, j <= i  [query][key]
-  unsigned short mneg[C * PT];             // -M below the diagonal blocks [row][col]
-  unsigned short tinv[4][16][24];          // inverses of the diagonal blocks, bf16 [row][col]
-  float mdt[4][16][20];                    // strictly-lower diagonal blocks of M, fp32, [col][row]
-  float g2[C];                             // G in log2 units
-  float gam[C];                            // gamma
-  float bet[C];                            // beta
+__device__ __forceinline__ int tok_off(int r, int ch) {
+  const int f = DK == 128 ? (r & 15) : ((r >> 1) & 7);
+  return r * DK + (((ch >> 3) ^ f) << 3) + (ch & 7);
+}
+//  * state keys [channel][token] (128-byte rows, 8-byte units)
+__device__ __forceinline__ int kt_off(int r, int tok) {
+  const int f = ((r >> 3) & 15) ^ (((r >> 1) & 1) << 2);
+  return r * C + (((tok >> 2) ^ f) << 2) + (tok & 3);
+}
+//  * V^T [column][token]
+__device__ __forceinline__ int vt_off(int r, int tok) {
+  const int f = ((r >> 2) & 15) ^ (((r >> 1) & 1) << 3);
+  return r * C + (((tok >> 2) ^ f) << 2) + (tok & 3);
+}
+//  * [token][token] tiles (scores, -M)
+__device__ __forceinline__ int tt_off(int r, int tok) {
+  const int f = (r >> 1) & 7;
+  return r * C + (((tok >> 2) ^ f) << 2) + (tok & 3);
+}
+
+template <int DK>
+struct alignas(16) Buf {
+  unsigned short k[C * DK];        // K rows
+  unsigned short q[C * DK];        // Q rows
+  unsigned short kt[DK * C];       // (K * exp(G_C - G))^T
+  unsigned short vt[DVT * C];      // V^T of the slice
+  unsigned short p[C * C];         // Gamma * Q K^T for j <= i, zero above the diagonal blocks
+  unsigned short mneg[C * C];      // -M below the diagonal blocks
+  unsigned short tinv[4][16][20];  // inverses of the diagonal blocks, bf16 [row][col]
+  float gam[C];                    // gamma
+  float bet[C];                    // beta
+  float g2[C];                     // G in log2 units
+};
+
+template <int DK>
+struct Smem {
+  Buf<DK> b[2];
+  float mdt[4][16][20];            // producer wave w: its diagonal block of M, fp32, [col][row]
 };
 
 // state-row map (as in the GLA consumer): accumulator tile rb, row r -> key
@@ -64,7 +98,10 @@ __device__ __forceinline__ int srow(int rb, int r) {
   return 32 * (rb >> 1) + 8 * (r >> 2) + 4 * (rb & 1) + (r & 3);
 }
 
-__device__ __forceinline__ void barrier() { __syncthreads(); }
+// Workgroup barrier ordering LDS only (outstanding global loads stay in flight).
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // 4 + 4 zero slots: a 16-deep contraction on the 32-deep MFMA
 __device__ __forceinline__ Frag<BF16> half_frag(uint2 lo) {
@@ -93,23 +130,25 @@ __device__ __forceinline__ Frag<BF16> lds_frag8x2(const unsigned short* p0, cons
   f.v = __builtin_bit_cast(bf16x8, uint4{a.x, a.y, b.x, b.y});
   return f;
 }
+__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
 }  // namespace gdn
 
 template <int DK>
-__global__ __launch_bounds__(256, 1) void gdn_chunk_fwd_kernel(GdnParams prm) {
+__global__ __launch_bounds__(512, 1) void gdn_chunk_fwd_kernel(GdnParams prm) {
   using namespace gdn;
-  using SM = Smem<DK>;
-  constexpr int PK = SM::PK, PT = SM::PT;
+  using BufT = Buf<DK>;
   constexpr int KS = DK / 32;    // 32-channel contraction steps
   constexpr int NRB = DK / 16;   // 16-row state tiles
   constexpr int CPT = DK / 16;   // staging: channels per thread (16 threads per token row)
   constexpr int NW = CPT / 2;    // staging: 32-bit words per token row per thread
 
-  __shared__ SM sm;
+  __shared__ Smem<DK> sm;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, m = lane & 15, gq = lane >> 4;
+  const bool producer = wave < 4;
 
   // ---- work item -----------------------------------------------------------------
   const int bid = blockIdx.x;
@@ -130,297 +169,315 @@ __global__ __launch_bounds__(256, 1) void gdn_chunk_fwd_kernel(GdnParams prm) {
   const int DV = prm.DV;
   const int vcol0 = vt * DVT;
   const int nch = (int)((eos - bos + C - 1) / C);
-  const float* s_in = prm.s0 ? prm.s0 + (long)unit * DK * DV : nullptr;
-  float* s_out = prm.sT ? prm.sT + (long)unit * DK * DV : nullptr;
-
-  // ---- raw loads: buffer records end at the sequence's last row, so reads past
-  // it return zeros (q = k = v = 0, g = beta = 0 on the padding of a last chunk)
-  const long r0 = rowbase + bos;
-  const int nrow = (int)(eos - bos);
-  const int qk_rec = (int)(unsigned)((eos - bos) * DK * 2);   // < 2^32 (host-checked sizes)
-  const int v_rec = (int)(unsigned)((eos - bos) * DV * 2);
-  const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(static_cast<const void*>(static_cast<const unsigned short*>(prm.q) + r0 * DK)),
-      (short)0, qk_rec, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(static_cast<const void*>(static_cast<const unsigned short*>(prm.k) + r0 * DK)),
-      (short)0, qk_rec, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(static_cast<const void*>(static_cast<const unsigned short*>(prm.v) + r0 * DV)),
-      (short)0, v_rec, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rs_g = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(static_cast<const void*>(prm.g + r0)), (short)0, nrow * 4, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(static_cast<const void*>(prm.beta + r0)), (short)0, nrow * 4, kBufferFlags);
-
-  // staging roles: thread tid holds tokens 4tg..4tg+3 x channels CPT*cg.. (q, k)
-  // and tokens 4tg..4tg+3 x columns 4cg..4cg+3 (v)
-  const int tg = tid >> 4, cg = tid & 15;
-  const unsigned qk_off = (unsigned)((4 * tg) * DK + cg * CPT) * 2u;
-  const unsigned v_off = (unsigned)((4 * tg) * DV + vcol0 + 4 * cg) * 2u;
-  unsigned rq[4][NW], rk[4][NW], rv[4][2];
-  float rg, rb;
-  auto load = [&](int u) __attribute__((always_inline)) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const unsigned o = qk_off + (unsigned)(u * C + a) * DK * 2u;
-      if constexpr (NW == 4) {
-        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs_q, (int)o, 0, 0);
-        const auto y = __builtin_amdgcn_raw_buffer_load_b128(rs_k, (int)o, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { rq[a][j] = x[j]; rk[a][j] = y[j]; }
-      } else {
-        const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs_q, (int)o, 0, 0);
-        const auto y = __builtin_amdgcn_raw_buffer_load_b64(rs_k, (int)o, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) { rq[a][j] = x[j]; rk[a][j] = y[j]; }
-      }
-      const auto z = __builtin_amdgcn_raw_buffer_load_b64(rs_v, (int)(v_off + (unsigned)(u * C + a) * DV * 2u), 0, 0);
-      rv[a][0] = z[0];
-      rv[a][1] = z[1];
-    }
-    rg = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_g, (int)((u * C + lane) * 4), 0, 0));
-    rb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_b, (int)((u * C + lane) * 4), 0, 0));
-  };
-
-  // ---- state: wave w owns columns [16w, 16w+16) of the slice, all DK rows
-  f32x4 sacc[NRB];
-#pragma unroll
-  for (int t = 0; t < NRB; ++t)
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      sacc[t][s] = s_in ? s_in[(long)srow(t, gq * 4 + s) * DV + vcol0 + wave * 16 + m] : 0.f;
 
   // score blocks above the diagonal blocks are read as zeros by the output product
-  for (int i = tid; i < C * PT; i += 256) sm.p[i] = 0;
+  for (int i = tid; i < C * C; i += 512) {
+    sm.b[0].p[i] = 0;
+    sm.b[1].p[i] = 0;
+  }
 
-  unsigned short* og = reinterpret_cast<unsigned short*>(prm.o) + rowbase * DV + vcol0 + wave * 16;
-  if (nch > 0) load(0);
+  if (producer) {
+    // =========================== producer waves ===========================
+    // raw loads: buffer records end at the sequence's last row, so reads past it
+    // return zeros (q = k = v = 0, g = beta = 0 on the padding of a last chunk)
+    const long r0 = rowbase + bos;
+    const int nrow = (int)(eos - bos);
+    const int qk_rec = (int)(unsigned)((eos - bos) * DK * 2);   // < 2^32 (host-checked sizes)
+    const int v_rec = (int)(unsigned)((eos - bos) * DV * 2);
+    const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(static_cast<const void*>(static_cast<const unsigned short*>(prm.q) + r0 * DK)),
+        (short)0, qk_rec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(static_cast<const void*>(static_cast<const unsigned short*>(prm.k) + r0 * DK)),
+        (short)0, qk_rec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(static_cast<const void*>(static_cast<const unsigned short*>(prm.v) + r0 * DV)),
+        (short)0, v_rec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rs_g = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(static_cast<const void*>(prm.g + r0)), (short)0, nrow * 4, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(static_cast<const void*>(prm.beta + r0)), (short)0, nrow * 4, kBufferFlags);
 
-  for (int u = 0; u < nch; ++u) {
-    // ============ 1. stage the chunk ============
-    {
-      // gates: lane = token; every wave scans the chunk (no cross-wave step needed)
-      const float b_t = rb;
-      float x = fmaxf(rg, kGateFloor) * kLog2e;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const float y = __shfl_up(x, d);
-        x += lane >= d ? y : 0.f;
-      }
-      const float G = x;                       // inclusive, log2 units
-      const float Glast = __shfl(G, 63);
-      const float e = fast_exp2(Glast - G);    // key factor of the state update
-      if (wave == 0) {
-        sm.g2[lane] = G;
-        sm.gam[lane] = fast_exp2(G);
-        sm.bet[lane] = b_t;
-      }
-      // q, k rows as they are; k scaled by exp(G_C - G_t) transposed into kt
+    // staging roles: thread tid holds tokens 4tg..4tg+3 x channels CPT*cg.. (q, k)
+    // and tokens 4tg..4tg+3 x columns 4cg..4cg+3 (v); lane = token for the gates
+    const int tg = tid >> 4, cg = tid & 15;
+    const unsigned qk_off = (unsigned)((4 * tg) * DK + cg * CPT) * 2u;
+    const unsigned v_off = (unsigned)((4 * tg) * DV + vcol0 + 4 * cg) * 2u;
+    unsigned rq[4][NW], rk[4][NW], rv[4][2];
+    float rg, rb;
+    auto load = [&](int u) __attribute__((always_inline)) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        unsigned short* pq = &sm.q[(4 * tg + a) * PK + cg * CPT];
-        unsigned short* pk = &sm.k[(4 * tg + a) * PK + cg * CPT];
+        const unsigned o = qk_off + (unsigned)(u * C + a) * DK * 2u;
         if constexpr (NW == 4) {
-          *reinterpret_cast<uint4*>(pq) = uint4{rq[a][0], rq[a][1], rq[a][2], rq[a][3]};
-          *reinterpret_cast<uint4*>(pk) = uint4{rk[a][0], rk[a][1], rk[a][2], rk[a][3]};
+          const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs_q, (int)o, 0, 0);
+          const auto y = __builtin_amdgcn_raw_buffer_load_b128(rs_k, (int)o, 0, 0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) { rq[a][j] = x[j]; rk[a][j] = y[j]; }
         } else {
-          *reinterpret_cast<uint2*>(pq) = uint2{rq[a][0], rq[a][1]};
-          *reinterpret_cast<uint2*>(pk) = uint2{rk[a][0], rk[a][1]};
+          const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs_q, (int)o, 0, 0);
+          const auto y = __builtin_amdgcn_raw_buffer_load_b64(rs_k, (int)o, 0, 0);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) { rq[a][j] = x[j]; rk[a][j] = y[j]; }
         }
+        const auto z = __builtin_amdgcn_raw_buffer_load_b64(rs_v, (int)(v_off + (unsigned)(u * C + a) * DV * 2u), 0, 0);
+        rv[a][0] = z[0];
+        rv[a][1] = z[1];
       }
-      float ef[4];
+      rg = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_g, (int)((u * C + lane) * 4), 0, 0));
+      rb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_b, (int)((u * C + lane) * 4), 0, 0));
+    };
+
+    // score block D = K_r X_p^T: lane (gq, m) holds k_j . x_t, j = 16r + 4gq + s, t = 16p + m
+    auto score = [&](const BufT& B, const unsigned short* xs, int p, int r) __attribute__((always_inline)) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int a = 0; a < 4; ++a) ef[a] = __shfl(e, (4 * tg + a) & 63);
+      for (int ks = 0; ks < KS; ++ks) {
+        const int ch = 32 * ks + 8 * gq;
+        mma(acc, lds_frag16(&B.k[tok_off<DK>(16 * r + m, ch)]), lds_frag16(&xs[tok_off<DK>(16 * p + m, ch)]));
+      }
+      return acc;
+    };
+
+    auto produce = [&](BufT& B, int un) __attribute__((always_inline)) {
+      // ---- stage the chunk held in registers ----
+      {
+        // gates: lane = token; each producer wave scans the chunk for itself
+        const float b_t = rb;
+        float x = fmaxf(rg, kGateFloor) * kLog2e;
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        float kv[4];
+        for (int d = 1; d < 64; d <<= 1) {
+          const float y = __shfl_up(x, d);
+          x += lane >= d ? y : 0.f;
+        }
+        const float G = x;                       // inclusive, log2 units
+        const float Glast = __shfl(G, 63);
+        const float e = fast_exp2(Glast - G);    // key factor of the state update
+        if (wave == 0) {
+          B.g2[lane] = G;
+          B.gam[lane] = fast_exp2(G);
+          B.bet[lane] = b_t;
+        }
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const unsigned w = rk[a][i >> 1];
-          kv[a] = ((i & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16)) * ef[a];
-        }
-        store4<BF16>(&sm.kt[(cg * CPT + i) * PT + 4 * tg], kv[0], kv[1], kv[2], kv[3]);
-      }
-      // V^T: column 4cg + c, tokens 4tg..4tg+3
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int wi = c >> 1;
-        const unsigned sel = (c & 1) ? 0x07060302u : 0x05040100u;
-        const unsigned lo = __builtin_amdgcn_perm(rv[1][wi], rv[0][wi], sel);
-        const unsigned hi = __builtin_amdgcn_perm(rv[3][wi], rv[2][wi], sel);
-        *reinterpret_cast<uint2*>(&sm.vt[(4 * cg + c) * PT + 4 * tg]) = uint2{lo, hi};
-      }
-    }
-    if (u + 1 < nch) load(u + 1);
-    barrier();
-
-    // ============ 2. scores, K S, S^T Q^T, R ============
-    // wave w: the M^T blocks (r, p = w), r <= w, and the P^T blocks (r, p = 3 - w),
-    // r <= 3 - w: five blocks per wave
-    {
-      auto score_block = [&](bool is_m, int p, int r) __attribute__((always_inline)) {
-        // D = K_r X_p^T: lane (gq, m) holds k_j . x_t, j = 16r + 4gq + s, t = 16p + m
-        const unsigned short* xs = is_m ? sm.k : sm.q;
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const Frag<BF16> a = lds_frag16(&sm.k[(16 * r + m) * PK + 32 * ks + 8 * gq]);
-          const Frag<BF16> b = lds_frag16(&xs[(16 * p + m) * PK + 32 * ks + 8 * gq]);
-          mma(acc, a, b);
-        }
-        const int t = 16 * p + m;
-        const int j0 = 16 * r + 4 * gq;
-        const float gt = sm.g2[t];
-        const float4 gj = *reinterpret_cast<const float4*>(&sm.g2[j0]);
-        const float gjs[4] = {gj.x, gj.y, gj.z, gj.w};
-        if (is_m) {
-          const float bt = sm.bet[t];
-          float mv[4];
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            mv[s] = (j0 + s < t) ? bt * fast_exp2(gt - gjs[s]) * acc[s] : 0.f;
-          if (r == p) {
-            // diagonal block, fp32, stored [col][row]: mdt[p][t % 16][j % 16]
-            // (the raw block is symmetric: read it as rows j, column t)
-            float mt[4];
-            const int jr = 4 * gq;          // this lane's rows 16p + 4gq + s of M, column m
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const int row = jr + s;
-              const float gr = sm.g2[16 * p + row];
-              mt[s] = (m < row) ? sm.bet[16 * p + row] * fast_exp2(gr - sm.g2[16 * p + m]) * acc[s] : 0.f;
-            }
-            *reinterpret_cast<float4*>(&sm.mdt[p][m][jr]) = make_float4(mt[0], mt[1], mt[2], mt[3]);
+          const int row = 4 * tg + a;
+          unsigned short* pq = &B.q[tok_off<DK>(row, cg * CPT)];
+          unsigned short* pk = &B.k[tok_off<DK>(row, cg * CPT)];
+          if constexpr (NW == 4) {
+            *reinterpret_cast<uint4*>(pq) = uint4{rq[a][0], rq[a][1], rq[a][2], rq[a][3]};
+            *reinterpret_cast<uint4*>(pk) = uint4{rk[a][0], rk[a][1], rk[a][2], rk[a][3]};
           } else {
-            store4<BF16>(&sm.mneg[t * PT + j0], -mv[0], -mv[1], -mv[2], -mv[3]);
+            *reinterpret_cast<uint2*>(pq) = uint2{rq[a][0], rq[a][1]};
+            *reinterpret_cast<uint2*>(pk) = uint2{rk[a][0], rk[a][1]};
           }
-        } else {
-          float pv[4];
-#pragma unroll
-          for (int s = 0; s < 4; ++s) pv[s] = (j0 + s <= t) ? fast_exp2(gt - gjs[s]) * acc[s] : 0.f;
-          store4<BF16>(&sm.p[t * PT + j0], pv[0], pv[1], pv[2], pv[3]);
         }
-      };
-      for (int r = 0; r <= wave; ++r) score_block(true, wave, r);
-      for (int r = 0; r <= 3 - wave; ++r) score_block(false, 3 - wave, r);
-    }
-    // K S (tokens x this wave's columns) and O^T = S^T Q^T, from the state entering the chunk
-    f32x4 ks_acc[4], o_acc[4];
-    {
-      Frag<BF16> sf[KS];
+        float ef[4];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sf[ks] = pair_frag(sacc[2 * ks], sacc[2 * ks + 1]);
+        for (int a = 0; a < 4; ++a) ef[a] = __shfl(e, (4 * tg + a) & 63);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        ks_acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-        o_acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < CPT; ++i) {
+          float kv[4];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          mma(ks_acc[p], lds_frag16(&sm.k[(16 * p + m) * PK + 32 * ks + 8 * gq]), sf[ks]);
-          mma(o_acc[p], sf[ks], lds_frag16(&sm.q[(16 * p + m) * PK + 32 * ks + 8 * gq]));
+          for (int a = 0; a < 4; ++a) {
+            const unsigned w = rk[a][i >> 1];
+            kv[a] = ((i & 1) ? bf_hi(w) : bf_lo(w)) * ef[a];
+          }
+          store4<BF16>(&B.kt[kt_off(cg * CPT + i, 4 * tg)], kv[0], kv[1], kv[2], kv[3]);
         }
-        // O^T(column 4gq + s, token 16p + m) *= gamma_t
-        const float gt = sm.gam[16 * p + m];
+        // V^T: column 4cg + c, tokens 4tg..4tg+3
 #pragma unroll
-        for (int s = 0; s < 4; ++s) o_acc[p][s] *= gt;
-        // R = beta (V - gamma K S): rows t = 16p + 4gq + s, column 16w + m
-        const float4 bt = *reinterpret_cast<const float4*>(&sm.bet[16 * p + 4 * gq]);
-        const float4 gm = *reinterpret_cast<const float4*>(&sm.gam[16 * p + 4 * gq]);
-        const uint2 vw = *reinterpret_cast<const uint2*>(&sm.vt[(16 * wave + m) * PT + 16 * p + 4 * gq]);
-        const float vv[4] = {__uint_as_float(vw.x << 16), __uint_as_float(vw.x & 0xffff0000u),
-                             __uint_as_float(vw.y << 16), __uint_as_float(vw.y & 0xffff0000u)};
-        const float bs[4] = {bt.x, bt.y, bt.z, bt.w}, gs[4] = {gm.x, gm.y, gm.z, gm.w};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) ks_acc[p][s] = bs[s] * (vv[s] - gs[s] * ks_acc[p][s]);
+        for (int c = 0; c < 4; ++c) {
+          const int wi = c >> 1;
+          const unsigned sel = (c & 1) ? 0x07060302u : 0x05040100u;
+          const unsigned lo = __builtin_amdgcn_perm(rv[1][wi], rv[0][wi], sel);
+          const unsigned hi = __builtin_amdgcn_perm(rv[3][wi], rv[2][wi], sel);
+          *reinterpret_cast<uint2*>(&B.vt[vt_off(4 * cg + c, 4 * tg)]) = uint2{lo, hi};
+        }
       }
-    }
-    barrier();
+      load(un);
+      barrier_lds();   // (A) every producer's rows are in place
 
-    // ============ 3. inverse of diagonal block p = w (fp32, row per lane) ============
-    {
-      // T (I + L) = I: row i of T from its last column to its first,
-      // T[i][c] = [c == i] - sum_{j > c} T[i][j] L[j][c]; L[j][c] = mdt[w][c][j]
-      const int i = m;
-      float t[16];
+      // ---- scores: wave w takes the M^T blocks (r, p = w), r <= w, and the
+      // P^T blocks (r, p = 3 - w), r <= 3 - w: five blocks per wave ----
+      const int w = wave;
+      {
+        // diagonal block w of M, fp32 [col][row]; the raw block is symmetric, so
+        // lane (gq, m) reads it as rows 16w + 4gq + s, column 16w + m
+        const f32x4 acc = score(B, B.k, w, w);
+        float mt[4];
 #pragma unroll
-      for (int c = 15; c >= 0; --c) {
-        float acc = (c == i) ? 1.f : 0.f;
+        for (int s = 0; s < 4; ++s) {
+          const int row = 4 * gq + s;
+          mt[s] = (m < row) ? B.bet[16 * w + row] * fast_exp2(B.g2[16 * w + row] - B.g2[16 * w + m]) * acc[s] : 0.f;
+        }
+        *reinterpret_cast<float4*>(&sm.mdt[w][m][4 * gq]) = make_float4(mt[0], mt[1], mt[2], mt[3]);
+      }
+      for (int r = 0; r < w; ++r) {
+        // -M below the diagonal blocks: row t = 16w + m, columns j = 16r + 4gq + s
+        const f32x4 acc = score(B, B.k, w, r);
+        const int t = 16 * w + m, j0 = 16 * r + 4 * gq;
+        const float gt = B.g2[t], bt = B.bet[t];
+        const float4 gj = *reinterpret_cast<const float4*>(&B.g2[j0]);
+        store4<BF16>(&B.mneg[tt_off(t, j0)], -bt * fast_exp2(gt - gj.x) * acc[0],
+                     -bt * fast_exp2(gt - gj.y) * acc[1], -bt * fast_exp2(gt - gj.z) * acc[2],
+                     -bt * fast_exp2(gt - gj.w) * acc[3]);
+      }
+      for (int r = 0; r <= 3 - w; ++r) {
+        // P = Gamma * Q K^T, j <= t: row t = 16p + m, columns j = 16r + 4gq + s
+        const int p = 3 - w;
+        const f32x4 acc = score(B, B.q, p, r);
+        const int t = 16 * p + m, j0 = 16 * r + 4 * gq;
+        const float gt = B.g2[t];
+        const float4 gj = *reinterpret_cast<const float4*>(&B.g2[j0]);
+        const float gjs[4] = {gj.x, gj.y, gj.z, gj.w};
+        float pv[4];
 #pragma unroll
-        for (int j = c + 1; j < 16; ++j) acc -= t[j] * sm.mdt[wave][c][j];
-        t[c] = acc;
+        for (int s = 0; s < 4; ++s) pv[s] = (j0 + s <= t) ? fast_exp2(gt - gjs[s]) * acc[s] : 0.f;
+        store4<BF16>(&B.p[tt_off(t, j0)], pv[0], pv[1], pv[2], pv[3]);
       }
-      if (gq == 0) {
-        uint4 lo = {pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3]), pack_bf16x2(t[4], t[5]),
-                    pack_bf16x2(t[6], t[7])};
-        uint4 hi = {pack_bf16x2(t[8], t[9]), pack_bf16x2(t[10], t[11]), pack_bf16x2(t[12], t[13]),
-                    pack_bf16x2(t[14], t[15])};
-        *reinterpret_cast<uint4*>(&sm.tinv[wave][i][0]) = lo;
-        *reinterpret_cast<uint4*>(&sm.tinv[wave][i][8]) = hi;
+      // ---- inverse of diagonal block w, one row per lane (its own mdt block:
+      // a wave-local wait orders the writes above before the reads) ----
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      {
+        // T (I + L) = I: row i of T from its last column to its first,
+        // T[i][c] = [c == i] - sum_{j > c} T[i][j] L[j][c]; L[j][c] = mdt[w][c][j]
+        const int i = m;
+        float t[16];
+#pragma unroll
+        for (int c = 15; c >= 0; --c) {
+          float acc = (c == i) ? 1.f : 0.f;
+#pragma unroll
+          for (int j = 15; j > c; --j) acc -= t[j] * sm.mdt[w][c][j];
+          t[c] = acc;
+        }
+        if (gq == 0) {
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4)
+            *reinterpret_cast<uint2*>(&B.tinv[w][i][4 * c4]) =
+                uint2{pack_bf16x2(t[4 * c4], t[4 * c4 + 1]), pack_bf16x2(t[4 * c4 + 2], t[4 * c4 + 3])};
+        }
       }
-    }
-    barrier();
+    };
 
-    // ============ 4. block solve, outputs, state ============
-    {
-      // U_p = T_pp (R_p - sum_{r<p} M_pr U_r), 16-deep products (4 real slots per lane)
+    if (nch > 0) load(0);
+    for (int i = 0; i <= nch; ++i) {
+      if (i < nch) {
+        produce(sm.b[i & 1], i + 1 < nch ? i + 1 : i);   // clamped look-ahead: no load behind a branch
+      } else {
+        barrier_lds();   // (A)
+      }
+      barrier_lds();     // (B) buffer swap
+    }
+  } else {
+    // =========================== consumer waves ===========================
+    const int cw = wave - 4;   // state / output columns [16cw, 16cw+16) of the slice
+    const float* s_in = prm.s0 ? prm.s0 + (long)unit * DK * DV : nullptr;
+    float* s_out = prm.sT ? prm.sT + (long)unit * DK * DV : nullptr;
+    f32x4 sacc[NRB];
+#pragma unroll
+    for (int t = 0; t < NRB; ++t)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        sacc[t][s] = s_in ? s_in[(long)srow(t, gq * 4 + s) * DV + vcol0 + cw * 16 + m] : 0.f;
+    unsigned short* og = reinterpret_cast<unsigned short*>(prm.o) + rowbase * DV + vcol0 + cw * 16;
+
+    auto consume = [&](const BufT& B, int u) __attribute__((always_inline)) {
+      // ---- K S (tokens x columns) and O^T = gamma S^T Q^T, then R ----
+      f32x4 r_acc[4], o_acc[4];
+      {
+        Frag<BF16> sf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sf[ks] = pair_frag(sacc[2 * ks], sacc[2 * ks + 1]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          r_acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+          o_acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const int ch = 32 * ks + 8 * gq;
+            mma(r_acc[p], lds_frag16(&B.k[tok_off<DK>(16 * p + m, ch)]), sf[ks]);
+            mma(o_acc[p], sf[ks], lds_frag16(&B.q[tok_off<DK>(16 * p + m, ch)]));
+          }
+          // O^T(column 4gq + s, token 16p + m) *= gamma_t
+          const float gt = B.gam[16 * p + m];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) o_acc[p][s] *= gt;
+          // R = beta (V - gamma K S): rows t = 16p + 4gq + s, column 16cw + m
+          const float4 bt = *reinterpret_cast<const float4*>(&B.bet[16 * p + 4 * gq]);
+          const float4 gm = *reinterpret_cast<const float4*>(&B.gam[16 * p + 4 * gq]);
+          const uint2 vw = *reinterpret_cast<const uint2*>(&B.vt[vt_off(16 * cw + m, 16 * p + 4 * gq)]);
+          r_acc[p][0] = bt.x * (bf_lo(vw.x) - gm.x * r_acc[p][0]);
+          r_acc[p][1] = bt.y * (bf_hi(vw.x) - gm.y * r_acc[p][1]);
+          r_acc[p][2] = bt.z * (bf_lo(vw.y) - gm.z * r_acc[p][2]);
+          r_acc[p][3] = bt.w * (bf_hi(vw.y) - gm.w * r_acc[p][3]);
+        }
+      }
+      barrier_lds();   // (A)
+      // ---- U_p = T_pp (R_p - sum_{r<p} M_pr U_r): 16-deep products ----
       f32x4 uacc[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        f32x4 x = ks_acc[p];
+        f32x4 x = r_acc[p];
 #pragma unroll
-        for (int r = 0; r < p; ++r) {
-          const Frag<BF16> a = half_frag(*reinterpret_cast<const uint2*>(&sm.mneg[(16 * p + m) * PT + 16 * r + 4 * gq]));
-          mma(x, a, half_frag(uacc[r]));
-        }
+        for (int r = 0; r < p; ++r)
+          mma(x, half_frag(*reinterpret_cast<const uint2*>(&B.mneg[tt_off(16 * p + m, 16 * r + 4 * gq)])),
+              half_frag(uacc[r]));
         uacc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-        mma(uacc[p], half_frag(*reinterpret_cast<const uint2*>(&sm.tinv[p][m][4 * gq])), half_frag(x));
+        mma(uacc[p], half_frag(*reinterpret_cast<const uint2*>(&B.tinv[p][m][4 * gq])), half_frag(x));
       }
       // U as an operand: slots = tokens 32j + 4gq + s and 32j + 16 + 4gq + s
       Frag<BF16> uf[2];
       uf[0] = pair_frag(uacc[0], uacc[1]);
       uf[1] = pair_frag(uacc[2], uacc[3]);
-      // O^T += U^T P^T (queries 16p + m)
+      // ---- O^T += U^T P^T (queries 16p + m), store ----
+      const long t0 = bos + (long)u * C;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
 #pragma unroll
         for (int j = 0; 2 * j <= p; ++j) {
-          const unsigned short* pr = &sm.p[(16 * p + m) * PT + 32 * j + 4 * gq];
-          mma(o_acc[p], uf[j], lds_frag8x2(pr, pr + 16));
+          const int row = 16 * p + m;
+          mma(o_acc[p], uf[j], lds_frag8x2(&B.p[tt_off(row, 32 * j + 4 * gq)], &B.p[tt_off(row, 32 * j + 16 + 4 * gq)]));
         }
-        const long t = bos + (long)u * C + 16 * p + m;
+        const long t = t0 + 16 * p + m;
         if (t < eos) store4<BF16>(og + t * DV + 4 * gq, o_acc[p][0], o_acc[p][1], o_acc[p][2], o_acc[p][3]);
       }
-      // S <- gamma_C S + Khat^T U
-      const float gC = sm.gam[C - 1];
+      // ---- S <- gamma_C S + Khat^T U ----
+      const float gC = B.gam[C - 1];
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) sacc[rb][s] *= gC;
+        const int row = srow(rb, m);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const unsigned short* kr = &sm.kt[srow(rb, m) * PT + 32 * j + 4 * gq];
-          mma(sacc[rb], lds_frag8x2(kr, kr + 16), uf[j]);
-        }
+        for (int j = 0; j < 2; ++j)
+          mma(sacc[rb], lds_frag8x2(&B.kt[kt_off(row, 32 * j + 4 * gq)], &B.kt[kt_off(row, 32 * j + 16 + 4 * gq)]),
+              uf[j]);
       }
-    }
-    barrier();
-  }
+    };
 
-  if (s_out) {
+    for (int i = 0; i <= nch; ++i) {
+      if (i > 0) {
+        consume(sm.b[(i - 1) & 1], i - 1);
+      } else {
+        barrier_lds();   // (A)
+      }
+      barrier_lds();     // (B) buffer swap
+    }
+    if (s_out) {
 #pragma unroll
-    for (int t = 0; t < NRB; ++t)
+      for (int t = 0; t < NRB; ++t)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        s_out[(long)srow(t, gq * 4 + s) * DV + vcol0 + wave * 16 + m] = sacc[t][s];
+        for (int s = 0; s < 4; ++s)
+          s_out[(long)srow(t, gq * 4 + s) * DV + vcol0 + cw * 16 + m] = sacc[t][s];
+    }
   }
 }
 
 int launch_gdn_chunk_fwd(const GdnParams& prm, int dk, int nblocks, hipStream_t stream) {
   if (dk == 128) {
-    hipLaunchKernelGGL((gdn_chunk_fwd_kernel<128>), dim3(nblocks), dim3(256), 0, stream, prm);
+    hipLaunchKernelGGL((gdn_chunk_fwd_kernel<128>), dim3(nblocks), dim3(512), 0, stream, prm);
   } else if (dk == 64) {
-    hipLaunchKernelGGL((gdn_chunk_fwd_kernel<64>), dim3(nblocks), dim3(256), 0, stream, prm);
+    hipLaunchKernelGGL((gdn_chunk_fwd_kernel<64>), dim3(nblocks), dim3(512), 0, stream, prm);
   } else {
     return -2;
   }
