@@ -21,17 +21,19 @@
 // buffers.  The state-independent half of a chunk runs one chunk ahead of the
 // state-dependent half:
 //  * producer waves 0-3 stage chunk u+1 (q, k rows; the state keys
-//    (K exp(G_C - G))^T; V^T; the gates), then compute its score blocks
-//    (M below the diagonal blocks, the causal Gamma * Q K^T) and, wave w, the
-//    inverse T_ww of M's 16x16 diagonal block w, in fp32;
+//    (K exp(G_C - G))^T; V^T; the gates), then compute its score blocks: M
+//    (its four 16x16 diagonal blocks in fp32, the rest in bf16) and the causal
+//    Gamma * Q K^T;
 //  * consumer wave 4 + c owns state columns [16c, 16c+16) for all d_k rows in
-//    MFMA accumulators and, for chunk u: K S and O = gamma Q S, R = beta (V -
-//    gamma K S), then the 16-token block forward substitution
-//    U_p = T_pp (R_p - sum_{r<p} M_pr U_r) (M^{-1} is never formed), O += P U,
-//    and the state update.
-// Two workgroup barriers per chunk: after the producers stage chunk u+1 (their
-// score blocks read each other's rows) and at the buffer swap.  The next
-// chunk's raw inputs are loaded into producer registers one chunk ahead.
+//    MFMA accumulators and, for chunk u: the inverse T_cc of M's diagonal block
+//    c (fp32, shared with the other consumers through LDS), K S and
+//    O = gamma Q S, R = beta (V - gamma K S), then the 16-token block forward
+//    substitution U_p = T_pp (R_p - sum_{r<p} M_pr U_r) (M^{-1} is never
+//    formed), O += P U, and the state update.
+// Two workgroup barriers per chunk: the middle one orders the producers'
+// staged rows before their score blocks (which read each other's rows) and the
+// consumers' inverses before their block solves; the other swaps the buffers.
+// The next chunk's raw inputs are loaded into producer registers one chunk ahead.
 #include <type_traits>
 
 #include "gla_device.h"
@@ -80,6 +82,7 @@ struct alignas(16) Buf {
   unsigned short p[C * C];         // Gamma * Q K^T for j <= i, zero above the diagonal blocks
   unsigned short mneg[C * C];      // -M below the diagonal blocks
   unsigned short tinv[4][16][20];  // inverses of the diagonal blocks, bf16 [row][col]
+  float mdt[4][16][16];            // M's diagonal blocks, strictly lower, fp32, [col][row]
   float gam[C];                    // gamma
   float bet[C];                    // beta
   float g2[C];                     // G in log2 units
@@ -88,7 +91,6 @@ struct alignas(16) Buf {
 template <int DK>
 struct Smem {
   Buf<DK> b[2];
-  float mdt[4][16][20];            // producer wave w: its diagonal block of M, fp32, [col][row]
 };
 
 // state-row map (as in the GLA consumer): accumulator tile rb, row r -> key
@@ -298,63 +300,48 @@ __global__ __launch_bounds__(512, 1) void gdn_chunk_fwd_kernel(GdnParams prm) {
       barrier_lds();   // (A) every producer's rows are in place
 
       // ---- scores: wave w takes the M^T blocks (r, p = w), r <= w, and the
-      // P^T blocks (r, p = 3 - w), r <= 3 - w: five blocks per wave ----
+      // P^T blocks (r, p = 3 - w), r <= 3 - w: five blocks per wave, block b
+      // being M(w, b) for b <= w (b = w: the diagonal block) and P(3 - w, b - w - 1)
+      // after; all five products are issued before any is scaled ----
       const int w = wave;
-      {
-        // diagonal block w of M, fp32 [col][row]; the raw block is symmetric, so
-        // lane (gq, m) reads it as rows 16w + 4gq + s, column 16w + m
-        const f32x4 acc = score(B, B.k, w, w);
-        float mt[4];
+      f32x4 acc[5];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int row = 4 * gq + s;
-          mt[s] = (m < row) ? B.bet[16 * w + row] * fast_exp2(B.g2[16 * w + row] - B.g2[16 * w + m]) * acc[s] : 0.f;
-        }
-        *reinterpret_cast<float4*>(&sm.mdt[w][m][4 * gq]) = make_float4(mt[0], mt[1], mt[2], mt[3]);
+      for (int b = 0; b < 5; ++b) {
+        const bool is_m = b <= w;
+        acc[b] = score(B, is_m ? B.k : B.q, is_m ? w : 3 - w, is_m ? b : b - w - 1);
       }
-      for (int r = 0; r < w; ++r) {
-        // -M below the diagonal blocks: row t = 16w + m, columns j = 16r + 4gq + s
-        const f32x4 acc = score(B, B.k, w, r);
-        const int t = 16 * w + m, j0 = 16 * r + 4 * gq;
-        const float gt = B.g2[t], bt = B.bet[t];
-        const float4 gj = *reinterpret_cast<const float4*>(&B.g2[j0]);
-        store4<BF16>(&B.mneg[tt_off(t, j0)], -bt * fast_exp2(gt - gj.x) * acc[0],
-                     -bt * fast_exp2(gt - gj.y) * acc[1], -bt * fast_exp2(gt - gj.z) * acc[2],
-                     -bt * fast_exp2(gt - gj.w) * acc[3]);
-      }
-      for (int r = 0; r <= 3 - w; ++r) {
-        // P = Gamma * Q K^T, j <= t: row t = 16p + m, columns j = 16r + 4gq + s
-        const int p = 3 - w;
-        const f32x4 acc = score(B, B.q, p, r);
-        const int t = 16 * p + m, j0 = 16 * r + 4 * gq;
-        const float gt = B.g2[t];
-        const float4 gj = *reinterpret_cast<const float4*>(&B.g2[j0]);
-        const float gjs[4] = {gj.x, gj.y, gj.z, gj.w};
-        float pv[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) pv[s] = (j0 + s <= t) ? fast_exp2(gt - gjs[s]) * acc[s] : 0.f;
-        store4<BF16>(&B.p[tt_off(t, j0)], pv[0], pv[1], pv[2], pv[3]);
-      }
-      // ---- inverse of diagonal block w, one row per lane (its own mdt block:
-      // a wave-local wait orders the writes above before the reads) ----
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      {
-        // T (I + L) = I: row i of T from its last column to its first,
-        // T[i][c] = [c == i] - sum_{j > c} T[i][j] L[j][c]; L[j][c] = mdt[w][c][j]
-        const int i = m;
-        float t[16];
+      for (int b = 0; b < 5; ++b) {
+        if (b == w) {
+          // diagonal block w of M, fp32 [col][row]; the raw block is symmetric, so
+          // lane (gq, m) reads it as rows 16w + 4gq + s, column 16w + m
+          float mt[4];
 #pragma unroll
-        for (int c = 15; c >= 0; --c) {
-          float acc = (c == i) ? 1.f : 0.f;
+          for (int s = 0; s < 4; ++s) {
+            const int row = 4 * gq + s;
+            mt[s] = (m < row) ? B.bet[16 * w + row] * fast_exp2(B.g2[16 * w + row] - B.g2[16 * w + m]) * acc[b][s]
+                              : 0.f;
+          }
+          *reinterpret_cast<float4*>(&B.mdt[w][m][4 * gq]) = make_float4(mt[0], mt[1], mt[2], mt[3]);
+        } else if (b < w) {
+          // -M below the diagonal blocks: row t = 16w + m, columns j = 16b + 4gq + s
+          const int t = 16 * w + m, j0 = 16 * b + 4 * gq;
+          const float gt = B.g2[t], bt = B.bet[t];
+          const float4 gj = *reinterpret_cast<const float4*>(&B.g2[j0]);
+          store4<BF16>(&B.mneg[tt_off(t, j0)], -bt * fast_exp2(gt - gj.x) * acc[b][0],
+                       -bt * fast_exp2(gt - gj.y) * acc[b][1], -bt * fast_exp2(gt - gj.z) * acc[b][2],
+                       -bt * fast_exp2(gt - gj.w) * acc[b][3]);
+        } else {
+          // P = Gamma * Q K^T, j <= t: row t = 16p + m, columns j = 16r + 4gq + s
+          const int p = 3 - w, r = b - w - 1;
+          const int t = 16 * p + m, j0 = 16 * r + 4 * gq;
+          const float gt = B.g2[t];
+          const float4 gj = *reinterpret_cast<const float4*>(&B.g2[j0]);
+          const float gjs[4] = {gj.x, gj.y, gj.z, gj.w};
+          float pv[4];
 #pragma unroll
-          for (int j = 15; j > c; --j) acc -= t[j] * sm.mdt[w][c][j];
-          t[c] = acc;
-        }
-        if (gq == 0) {
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4)
-            *reinterpret_cast<uint2*>(&B.tinv[w][i][4 * c4]) =
-                uint2{pack_bf16x2(t[4 * c4], t[4 * c4 + 1]), pack_bf16x2(t[4 * c4 + 2], t[4 * c4 + 3])};
+          for (int s = 0; s < 4; ++s) pv[s] = (j0 + s <= t) ? fast_exp2(gt - gjs[s]) * acc[b][s] : 0.f;
+          store4<BF16>(&B.p[tt_off(t, j0)], pv[0], pv[1], pv[2], pv[3]);
         }
       }
     };
@@ -381,7 +368,27 @@ __global__ __launch_bounds__(512, 1) void gdn_chunk_fwd_kernel(GdnParams prm) {
         sacc[t][s] = s_in ? s_in[(long)srow(t, gq * 4 + s) * DV + vcol0 + cw * 16 + m] : 0.f;
     unsigned short* og = reinterpret_cast<unsigned short*>(prm.o) + rowbase * DV + vcol0 + cw * 16;
 
-    auto consume = [&](const BufT& B, int u) __attribute__((always_inline)) {
+    auto consume = [&](BufT& B, int u) __attribute__((always_inline)) {
+      // ---- inverse of diagonal block cw of M, one row per lane, fp32:
+      // T (I + L) = I, so row i of T from its last column to its first is
+      // T[i][c] = [c == i] - sum_{j > c} T[i][j] L[j][c], L[j][c] = mdt[cw][c][j] ----
+      {
+        const int i = m;
+        float t[16];
+#pragma unroll
+        for (int c = 15; c >= 0; --c) {
+          float acc = (c == i) ? 1.f : 0.f;
+#pragma unroll
+          for (int j = 15; j > c; --j) acc -= t[j] * B.mdt[cw][c][j];
+          t[c] = acc;
+        }
+        if (gq == 0) {
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4)
+            *reinterpret_cast<uint2*>(&B.tinv[cw][i][4 * c4]) =
+                uint2{pack_bf16x2(t[4 * c4], t[4 * c4 + 1]), pack_bf16x2(t[4 * c4 + 2], t[4 * c4 + 3])};
+        }
+      }
       // ---- K S (tokens x columns) and O^T = gamma S^T Q^T, then R ----
       f32x4 r_acc[4], o_acc[4];
       {
@@ -412,7 +419,7 @@ __global__ __launch_bounds__(512, 1) void gdn_chunk_fwd_kernel(GdnParams prm) {
           r_acc[p][3] = bt.w * (bf_hi(vw.y) - gm.w * r_acc[p][3]);
         }
       }
-      barrier_lds();   // (A)
+      barrier_lds();   // (A) every consumer's inverse is in place
       // ---- U_p = T_pp (R_p - sum_{r<p} M_pr U_r): 16-deep products ----
       f32x4 uacc[4];
 #pragma unroll
