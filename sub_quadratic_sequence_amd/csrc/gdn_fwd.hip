@@ -245,15 +245,20 @@ __global__ __launch_bounds__(512, 1) void gdn_chunk_fwd_kernel(GdnParams prm) {
       // ---- stage the chunk held in registers ----
       {
         // gates: lane = token; each producer wave scans the chunk for itself
+        // (a 16-lane DPP scan, then the totals of the lower rows of 16 added)
         const float b_t = rb;
         float x = fmaxf(rg, kGateFloor) * kLog2e;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const float y = __shfl_up(x, d);
-          x += lane >= d ? y : 0.f;
-        }
+        x += dpp<kRowShr1>(x);
+        x += dpp<kRowShr2>(x);
+        x += dpp<kRowShr4>(x);
+        x += dpp<kRowShr8>(x);
+        const float r0t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+        const float r1t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+        const float r2t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
+        const int row16 = lane >> 4;
+        x += row16 == 0 ? 0.f : row16 == 1 ? r0t : row16 == 2 ? r0t + r1t : (r0t + r1t) + r2t;
         const float G = x;                       // inclusive, log2 units
-        const float Glast = __shfl(G, 63);
+        const float Glast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), 63));
         const float e = fast_exp2(Glast - G);    // key factor of the state update
         if (wave == 0) {
           B.g2[lane] = G;
