@@ -29,6 +29,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "sub_quadratic_sequence_amd", "csrc", "chunk_fwd_pipe.hip")
 STEP_SRC = os.path.join(ROOT, "sub_quadratic_sequence_amd", "csrc", "recurrent_step.hip")
+GDN_SRC = os.path.join(ROOT, "sub_quadratic_sequence_amd", "csrc", "gdn_fwd.hip")
 
 
 def log(*a):
@@ -339,10 +340,11 @@ def main():
                     help="skip the long-context and packed-sequence legs")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-gdn", action="store_true", help="skip the Gated DeltaNet leg")
-    ap.add_argument("--only", choices=["fwd", "decode", "long", "bwd", "gdn", "copy", "pmc"],
+    ap.add_argument("--only", choices=["fwd", "decode", "long", "bwd", "gdn", "copy", "pmc", "gdnpmc"],
                     default=None,
                     help="profiling runs: launch only this part (copy = 512 MiB calibration "
-                         "copy; pmc = copy, then forward, then decode, a few launches each)")
+                         "copy; pmc = copy, then forward, then decode, a few launches each; "
+                         "gdnpmc = copy, then a few Gated DeltaNet launches)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -355,7 +357,7 @@ def main():
     from sub_quadratic_sequence_amd import gla, inputs
 
     gla.load_library()
-    if args.only in ("copy", "pmc"):
+    if args.only in ("copy", "pmc", "gdnpmc"):
         src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)
         for _ in range(5):
@@ -366,6 +368,12 @@ def main():
         if args.only == "copy":
             return
         args.steps, args.warmup, args.preroll = 5, 1, 0.0
+        if args.only == "gdnpmc":
+            args.no_cpu_baseline = True
+            args.steps = 10
+            bench_gdn(args, torch, gla, inputs)
+            log("[bench] gdn pmc launches done")
+            return
         bench_forward(args, torch, gla, inputs)
         bench_decode(args, torch, gla, inputs)
         log("[bench] pmc launches done")
@@ -489,6 +497,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": gd["bytes"],
                          "algorithmic_flops_per_call": gd["flops"],
+                         "traffic": read_traffic("gdn_fwd_b8h16t2048d128_bf16.txt", GDN_SRC),
                          "kernel": "gla::gdn_chunk_fwd_kernel<128>"},
         }
         if "oracle" in gd:
