@@ -394,26 +394,18 @@ __global__ __launch_bounds__(512, 1) void gdn_chunk_fwd_kernel(GdnParams prm) {
                 uint2{pack_bf16x2(t[4 * c4], t[4 * c4 + 1]), pack_bf16x2(t[4 * c4 + 2], t[4 * c4 + 3])};
         }
       }
-      // ---- K S (tokens x columns) and O^T = gamma S^T Q^T, then R ----
+      // ---- K S (tokens x columns), then R ----
       f32x4 r_acc[4], o_acc[4];
-      {
-        Frag<BF16> sf[KS];
+      Frag<BF16> sf[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sf[ks] = pair_frag(sacc[2 * ks], sacc[2 * ks + 1]);
+      for (int ks = 0; ks < KS; ++ks) sf[ks] = pair_frag(sacc[2 * ks], sacc[2 * ks + 1]);
+      {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           r_acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-          o_acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const int ch = 32 * ks + 8 * gq;
-            mma(r_acc[p], lds_frag16(&B.k[tok_off<DK>(16 * p + m, ch)]), sf[ks]);
-            mma(o_acc[p], sf[ks], lds_frag16(&B.q[tok_off<DK>(16 * p + m, ch)]));
-          }
-          // O^T(column 4gq + s, token 16p + m) *= gamma_t
-          const float gt = B.gam[16 * p + m];
-#pragma unroll
-          for (int s = 0; s < 4; ++s) o_acc[p][s] *= gt;
+          for (int ks = 0; ks < KS; ++ks)
+            mma(r_acc[p], lds_frag16(&B.k[tok_off<DK>(16 * p + m, 32 * ks + 8 * gq)]), sf[ks]);
           // R = beta (V - gamma K S): rows t = 16p + 4gq + s, column 16cw + m
           const float4 bt = *reinterpret_cast<const float4*>(&B.bet[16 * p + 4 * gq]);
           const float4 gm = *reinterpret_cast<const float4*>(&B.gam[16 * p + 4 * gq]);
@@ -425,6 +417,14 @@ __global__ __launch_bounds__(512, 1) void gdn_chunk_fwd_kernel(GdnParams prm) {
         }
       }
       barrier_lds();   // (A) every consumer's inverse is in place
+      // ---- O^T = gamma S^T Q^T (issued beside the block solve's dependent chain) ----
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        o_acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          mma(o_acc[p], sf[ks], lds_frag16(&B.q[tok_off<DK>(16 * p + m, 32 * ks + 8 * gq)]));
+      }
       // ---- U_p = T_pp (R_p - sum_{r<p} M_pr U_r): 16-deep products ----
       f32x4 uacc[4];
 #pragma unroll
@@ -441,10 +441,13 @@ __global__ __launch_bounds__(512, 1) void gdn_chunk_fwd_kernel(GdnParams prm) {
       Frag<BF16> uf[2];
       uf[0] = pair_frag(uacc[0], uacc[1]);
       uf[1] = pair_frag(uacc[2], uacc[3]);
-      // ---- O^T += U^T P^T (queries 16p + m), store ----
+      // ---- O^T(column 4gq + s, query 16p + m) = gamma_t S^T Q^T + U^T P^T, store ----
       const long t0 = bos + (long)u * C;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
+        const float gt = B.gam[16 * p + m];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) o_acc[p][s] *= gt;
 #pragma unroll
         for (int j = 0; 2 * j <= p; ++j) {
           const int row = 16 * p + m;
