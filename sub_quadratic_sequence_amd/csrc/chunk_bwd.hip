@@ -183,9 +183,10 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
   constexpr int NCG = DK / 8;      // 8-channel groups
   constexpr int NGL = 16 * NCG;    // gating lanes
   constexpr int CB = DK / 16;      // 16-channel blocks
-  __shared__ __attribute__((aligned(16))) unsigned short kb[C * KP];
-  __shared__ __attribute__((aligned(16))) unsigned short vs[C * VP];
-  __shared__ float dec[DK];
+  // two buffers: the gating of chunk u+1 overlaps the products of chunk u
+  __shared__ __attribute__((aligned(16))) unsigned short kbs[2][C * KP];
+  __shared__ __attribute__((aligned(16))) unsigned short vss[2][C * VP];
+  __shared__ float decs[2][DK];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, m = lane & 15, grp = lane >> 4;
   const int bid = blockIdx.x, nblk = gridDim.x;
@@ -246,8 +247,11 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
   }
   if (u_hi > u_lo) prefetch(REV ? u_hi - 1 : u_lo);
 
-  for (int it_u = 0; it_u < u_hi - u_lo; ++it_u) {
-    const int u = REV ? u_hi - 1 - it_u : u_lo + it_u;
+  // stage chunk u (its raw inputs are in registers) into buffer b
+  auto stage = [&](int b) __attribute__((always_inline)) {
+    unsigned short* const kb = kbs[b];
+    unsigned short* const vs = vss[b];
+    float* const dec = decs[b];
     if (gl) {
       float pp[4][8];
       const unsigned* gw[4] = {&rg[0].x, &rg[1].x, &rg[2].x, &rg[3].x};
@@ -302,10 +306,27 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
       const int idx = tid + 256 * it, row = idx >> 3, un = idx & 7;
       *reinterpret_cast<uint4*>(vs + row * VP + 8 * un) = rv[it];
     }
-    if (it_u + 1 < u_hi - u_lo) prefetch(REV ? u - 1 : u + 1);
-    barrier_lds();
+  };
 
+  const int nit = u_hi - u_lo;
+  if (nit > 0) {
+    stage(0);
+    if (nit > 1) prefetch(REV ? u_hi - 2 : u_lo + 1);
+    barrier_lds();
+  }
+  for (int it_u = 0; it_u < nit; ++it_u) {
+    const int u = REV ? u_hi - 1 - it_u : u_lo + it_u;
+    const int b = it_u & 1;
+    // chunk u+1 (in processing order) is staged into the other buffer while
+    // chunk u's products run
+    if (it_u + 1 < nit) {
+      stage(b ^ 1);
+      if (it_u + 2 < nit) prefetch(REV ? u - 2 : u + 2);
+    }
     // H_u (the state entering chunk u) to the workspace, then the update
+    const unsigned short* const kb = kbs[b];
+    const unsigned short* const vs = vss[b];
+    const float* const dec = decs[b];
     unsigned short* const hu = hs + (long)u * DK * DV;
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
