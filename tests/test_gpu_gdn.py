@@ -137,3 +137,47 @@ def test_split_call_composition(dev):
     ob, sb = _run(dev, b, s0=sa.cpu())
     assert unit_err_fixed(torch.cat([oa, ob], 2).float(), o.float()) < 1e-2
     assert unit_err_fixed(sb, sf) < 1e-2
+
+
+def test_zero_tokens_pass_the_state_through(dev):
+    from sub_quadratic_sequence_amd import gla
+
+    say("gdn T = 0 with an initial state: the final state equals it")
+    s0 = torch.randn(2, 3, 128, 128, generator=torch.Generator().manual_seed(13)) * 0.1
+    z = torch.empty(2, 3, 0, 128, dtype=torch.bfloat16, device=dev)
+    zg = torch.empty(2, 3, 0, dtype=torch.float32, device=dev)
+    o, sf = gla.gdn_chunk_fwd(z, z, z, zg, zg, initial_state=s0.to(dev), output_final_state=True)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 3, 0, 128) and torch.equal(sf.cpu(), s0)
+    o, sf = gla.gdn_chunk_fwd(z, z, z, zg, zg, output_final_state=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(sf) == 0
+
+
+@pytest.mark.parametrize("dv", [256, 512])
+def test_wide_values(dev, dv):
+    say(f"gdn B1 H2 T200 dk128 dv{dv} with S0")
+    d = I.gdn_inputs(W, B=1, H=2, T=200, dv=dv, s0=True, seed=14)
+    o, sf = _run(dev, d, s0=d["s0"])
+    _check(d, o, sf, d["s0"], f"dv {dv}")
+
+
+def test_unit_count_not_a_multiple_of_eight(dev):
+    say("gdn B3 H3 T129 (9 units x 2 slices: no XCD remapping)")
+    d = I.gdn_inputs(W, B=3, H=3, T=129, s0=True, seed=15)
+    o, sf = _run(dev, d, s0=d["s0"])
+    _check(d, o, sf, d["s0"], "B3 H3 T129")
+
+
+def test_nan_stays_in_its_sequence(dev):
+    say("gdn: a NaN in one packed sequence leaves the others finite and correct")
+    lens = [100, 150, 70]
+    d = I.gdn_inputs(W, H=2, lengths=lens, seed=16)
+    d["v"][0, 1, 120] = float("nan")          # sequence 1, head 1
+    o, sf = _run(dev, d, cu=d["cu_seqlens"])
+    o = o.float().cpu()
+    assert torch.isnan(o[0, 1, 120:250]).any()
+    ok = torch.ones(o.shape[2], dtype=torch.bool)
+    ok[100:250] = False
+    assert torch.isfinite(o[0, :, ok]).all() and torch.isfinite(o[0, 0]).all()
+    assert torch.isfinite(sf[[0, 2]]).all() and torch.isfinite(sf[1, 0]).all()
