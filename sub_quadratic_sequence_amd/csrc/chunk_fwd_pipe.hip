@@ -5,17 +5,20 @@
 // Formulation of Chunk Computations"), organised so that the gating work and
 // the matrix-core work of consecutive chunks overlap:
 //
-//  * one workgroup = 8 waves per (sequence, head, 64-column slice of d_v);
-//    waves 0-3 are producers, waves 4-7 consumers, one of each per SIMD.
+//  * one workgroup = 8 waves per (sequence, head, slice of d_v): 64 columns,
+//    or 128 when the batch has enough units to fill the device with those
+//    (NT = 2: the gating of q and k and the score blocks then serve twice the
+//    columns); waves 0-3 are producers, waves 4-7 consumers, one of each per
+//    SIMD.
 //  * producers turn chunk u+1's q, k, g, v into MFMA operand tiles in one LDS
 //    buffer while consumers run chunk u's contractions from the other buffer;
 //    a single workgroup barrier per chunk swaps them.
 //  * producer wave w owns key channels [w DK/4, (w+1) DK/4) of all 64 tokens:
 //    lane (tg, gq) holds tokens 4tg..4tg+3 x DK/16 channels, so the log2-gate
 //    cumulative sum is a serial sum over 4 tokens plus a 16-lane DPP scan.
-//  * consumer wave c owns state columns [16c, 16c+16) (all d_k rows) in MFMA
-//    accumulators and computes the transposed output tile O^T for those
-//    columns and all 64 queries.  The state rows are assigned to accumulator
+//  * consumer wave c owns state columns [16c, 16c+16) of each 64-column half
+//    of the slice (all d_k rows) in MFMA accumulators and computes the
+//    transposed output tile O^T for those columns and all 64 queries.  The state rows are assigned to accumulator
 //    rows so that a lane's accumulator values for a 32-channel step are
 //    exactly the 8 contiguous channels its operand fragments use: the
 //    inter-chunk term takes S straight from the accumulators as an MFMA
@@ -43,7 +46,6 @@ namespace gla {
 namespace pipe {
 
 constexpr int C = 64;
-constexpr int DVT = 64;
 constexpr float kFastLimit = 60.f;
 constexpr float kExtremeLimit = 100.f;
 constexpr int kBufferFlags = 0x00020000;   // gfx9 buffer descriptor word 3: raw 32-bit dwords
@@ -86,9 +88,10 @@ __device__ __forceinline__ int tr_off(int r, int u, int sw, int h = 0) {
   return r * TRP + ((u ^ sw) & 7) * 8 + h * 4;
 }
 
-template <int DK>
+template <int DK, int NT>
 struct alignas(256) Buf {
   static constexpr int PQ = TokTile<DK>::kPitch;
+  static constexpr int DVT = 64 * NT;   // columns of the slice
   unsigned short q[C * PQ];        // query operand  [token][channel]
   unsigned short k[C * PQ];        // key operand    [token][channel]
   unsigned short kt[DK * TRP];     // state keys     [channel][token]
@@ -132,11 +135,12 @@ __device__ __forceinline__ int srow(int rb, int m) {
 // MODE kFull: the forward pass (outputs, and the final state of unsplit sequences).
 // MODE kStateOnly: the state a segment reaches from S = 0 and the segment's total
 // gate decay, for the sequence split (no queries read, no outputs written).
-template <int DK, int MODE>
+template <int DK, int MODE, int NT>
 __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm) {
   using namespace pipe;
   constexpr bool FULL = MODE == kFull;
-  using BufT = Buf<DK>;
+  using BufT = Buf<DK, NT>;
+  constexpr int DVT = BufT::DVT;
   constexpr int PQ = BufT::PQ;
   constexpr int CPL = DK / 16;   // producer: channels per lane
   constexpr int WCH = DK / 4;    // producer: channels per wave
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     const int tg = m;                      // tokens 4tg..4tg+3
     const int ch0 = w * WCH + gq * CPL;    // first channel of this lane
     const int sub = tg >> 2;               // 16-token sub-chunk
-    const int vc0 = w * 16 + gq * 4;       // first of 4 V columns
+    const int vc0 = w * 16 + gq * 4;       // first of 4 V columns (of each 64-column half)
     // Raw buffer loads over the sequence's rows: a read past its last row
     // returns zeros (the buffer's record count ends there), which is exactly
     // the padding of a partial last chunk (q = k = v = 0, log-gate 0).  Offsets
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     const unsigned qk_lane = ((4 * tg) * DK + ch0) * 2u;          // token 4tg, channel ch0
     const unsigned v_lane = ((4 * tg) * DV + vcol0 + vc0) * 2u;   // token 4tg, column vcol0 + vc0
 
-    unsigned rq[4][NWR], rk[4][NWR], rg[4][NWR], rv[4][2];
+    unsigned rq[4][NWR], rk[4][NWR], rg[4][NWR], rv[NT][4][2];
 
     auto ld = [&](unsigned (&r)[NWR], __amdgpu_buffer_rsrc_t rs, unsigned off) __attribute__((always_inline)) {
       if constexpr (NWR == 4) {
@@ -267,10 +271,13 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     };
     auto load_v = [&](int u) __attribute__((always_inline)) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs_v, (int)(v_lane + (unsigned)(u * C + a) * DV * 2u), 0, 0);
-        rv[a][0] = x[0]; rv[a][1] = x[1];
-      }
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const auto x = __builtin_amdgcn_raw_buffer_load_b64(
+              rs_v, (int)(v_lane + 128u * t + (unsigned)(u * C + a) * DV * 2u), 0, 0);
+          rv[t][a][0] = x[0]; rv[t][a][1] = x[1];
+        }
     };
     auto load_g = [&](int u) __attribute__((always_inline)) {
 #pragma unroll
@@ -332,14 +339,15 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       launder(b_kt);
       launder(b_vt);
       // V as [column][token]: pair tokens (a, a+1) of one column in one word
-      {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int wi = c >> 1;
           const unsigned sel = (c & 1) ? 0x07060302u : 0x05040100u;
-          const unsigned lo = __builtin_amdgcn_perm(rv[1][wi], rv[0][wi], sel);
-          const unsigned hi = __builtin_amdgcn_perm(rv[3][wi], rv[2][wi], sel);
-          *reinterpret_cast<uint2*>(vt_slot(c)) = uint2{lo, hi};
+          const unsigned lo = __builtin_amdgcn_perm(rv[t][1][wi], rv[t][0][wi], sel);
+          const unsigned hi = __builtin_amdgcn_perm(rv[t][3][wi], rv[t][2][wi], sel);
+          *reinterpret_cast<uint2*>(vt_slot(64 * t + c)) = uint2{lo, hi};
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -598,8 +606,8 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     }
   } else {
     // =========================== consumer waves ===========================
-    const int cw = wave - 4;               // state / output columns [16cw, 16cw+16)
-    const int vrow = cw * 16 + m;          // this lane's row of the values tile
+    const int cw = wave - 4;               // state / output columns 64t + [16cw, 16cw+16)
+    const int vrow = cw * 16 + m;          // this lane's row of the values tile (t = 0)
     // Per-lane byte offsets of the operand fragments inside a buffer.  With the
     // swizzled layouts a fragment's offset is (lane part) XOR (compile-time part)
     // plus a compile-time row offset: the XOR touches only bits 4-6 (4-7 for the
@@ -615,15 +623,20 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     const unsigned lb_kt = (unsigned)(srow(0, m) * 128 + (((gq ^ tr_swz(srow(0, m))) & 7) << 4));
     const unsigned lb_vb = (unsigned)(vrow * 128 + (((gq ^ tr_swz(vrow)) & 7) << 4));
     const unsigned lb_va = (unsigned)(vrow * 128 + ((((gq >> 1) ^ tr_swz(vrow)) & 7) << 4) + (gq & 1) * 8);
+    // Row 64t + r of a values tile sits at row r's place XOR (tr_swz(64) << 4),
+    // 64 rows (8 KB) further on.
+    constexpr unsigned kHalfX = (unsigned)tr_swz(64) << 4, kHalfOff = 64u * 128u;
     unsigned short* og = reinterpret_cast<unsigned short*>(prm.o) + rowbase * DV + vcol0;
-    f32x4 sacc[NRB];
+    f32x4 sacc[NT][NRB];
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int c = srow(rb, gq * 4 + s);
-        sacc[rb][s] = s_in ? s_in[(long)c * DV + vcol0 + cw * 16 + m] : 0.f;
-      }
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int c = srow(rb, gq * 4 + s);
+          sacc[t][rb][s] = s_in ? s_in[(long)c * DV + vcol0 + 64 * t + cw * 16 + m] : 0.f;
+        }
     // one chunk of contractions; SAFE / EXT are compile-time so the body is branch-free
     auto consume = [&](const BufT& B, int u, auto safe_tag, auto ext_tag) __attribute__((always_inline)) {
       const unsigned bb = (unsigned)(reinterpret_cast<const char*>(&B) - reinterpret_cast<const char*>(bufs));
@@ -659,25 +672,30 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       };
       if constexpr (FULL) {   // outputs of this chunk (the state-only pass has none)
         // S_prev as the inter term's A operand: slots = channels 32ks+8gq..+7 (see srow)
-        Frag<BF16> sa[KS];
+        Frag<BF16> sa[NT][KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const float sv[8] = {sacc[2 * ks][0],     sacc[2 * ks][1],     sacc[2 * ks][2],
-                               sacc[2 * ks][3],     sacc[2 * ks + 1][0], sacc[2 * ks + 1][1],
-                               sacc[2 * ks + 1][2], sacc[2 * ks + 1][3]};
-          frag_from_f32(sa[ks], sv);
-        }
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const float sv[8] = {sacc[t][2 * ks][0],     sacc[t][2 * ks][1],     sacc[t][2 * ks][2],
+                                 sacc[t][2 * ks][3],     sacc[t][2 * ks + 1][0], sacc[t][2 * ks + 1][1],
+                                 sacc[t][2 * ks + 1][2], sacc[t][2 * ks + 1][3]};
+            frag_from_f32(sa[t][ks], sv);
+          }
         // V^T rows of this wave's columns, tokens in the score accumulators' order
-        Frag<BF16> va[2];
+        Frag<BF16> va[NT][2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          // tokens 32ks + 4gq .. +3 and the same 16 tokens later
-          const uint2 lo = *reinterpret_cast<const uint2*>(lds + (b_va ^ ((unsigned)(4 * ks) << 4)));
-          const uint2 hi = *reinterpret_cast<const uint2*>(lds + (b_va ^ ((unsigned)(4 * ks + 2) << 4)));
-          va[ks].v = __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
-        }
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            // tokens 32ks + 4gq .. +3 and the same 16 tokens later
+            const unsigned bt = t ? (b_va ^ kHalfX) + kHalfOff : b_va;
+            const uint2 lo = *reinterpret_cast<const uint2*>(lds + (bt ^ ((unsigned)(4 * ks) << 4)));
+            const uint2 hi = *reinterpret_cast<const uint2*>(lds + (bt ^ ((unsigned)(4 * ks + 2) << 4)));
+            va[t][ks].v = __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
+          }
         Frag<BF16> kf[4][KS];   // key fragments of sub-chunk r, loaded when first needed
-        f32x4 oacc[4];
+        f32x4 oacc[1][4];   // NT == 1: outputs stored after the four sub-chunks
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           Frag<BF16> qf[KS];
@@ -718,7 +736,9 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
           for (int s = 0; s < 4; ++s) pacc[p][s] = (gq * 4 + s > m) ? 0.f : pacc[p][s];  // causal
 
           // O^T(p) = V^T P^T + S_prev^T (Q 2^Gamma)^T
-          f32x4 o1 = f32x4{0.f, 0.f, 0.f, 0.f}, o2 = f32x4{0.f, 0.f, 0.f, 0.f};
+          f32x4 o1[NT], o2[NT];
+#pragma unroll
+          for (int t = 0; t < NT; ++t) o1[t] = o2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; 2 * ks <= p; ++ks) {
             const float pv[8] = {pacc[2 * ks][0],     pacc[2 * ks][1],     pacc[2 * ks][2],
@@ -726,36 +746,57 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
                                  pacc[2 * ks + 1][2], pacc[2 * ks + 1][3]};
             Frag<BF16> pb;
             frag_from_f32(pb, pv);
-            mma(o1, va[ks], pb);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) mma(o1[t], va[t][ks], pb);
           }
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             if constexpr (SAFE) {
               const Frag<BF16> b = scaled(qf[ks], B.bq[p], ks);
-              mma(o2, sa[ks], b);
+#pragma unroll
+              for (int t = 0; t < NT; ++t) mma(o2[t], sa[t][ks], b);
             } else {
-              mma(o2, sa[ks], qf[ks]);
+#pragma unroll
+              for (int t = 0; t < NT; ++t) mma(o2[t], sa[t][ks], qf[ks]);
             }
           }
-          oacc[p] = o1 + o2;
-        }
-        const long t0 = bos + (long)u * C;
+          if constexpr (NT == 1) {
+            oacc[0][p] = o1[0] + o2[0];
+          } else {   // two slices' accumulators do not fit beside the state: store now
+            const long tk = bos + (long)u * C + 16 * p + m;
+            if (tk < eos) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const long t = t0 + 16 * p + m;
-          if (t < eos)
-            store4<BF16>(og + t * DV + cw * 16 + gq * 4, oacc[p][0], oacc[p][1], oacc[p][2], oacc[p][3]);
+              for (int t = 0; t < NT; ++t) {
+                const f32x4 x = o1[t] + o2[t];
+                store4<BF16>(og + tk * DV + 64 * t + cw * 16 + gq * 4, x[0], x[1], x[2], x[3]);
+              }
+            }
+          }
+        }
+        if constexpr (NT == 1) {
+          const long t0 = bos + (long)u * C;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const long tk = t0 + 16 * p + m;
+            if (tk < eos)
+              store4<BF16>(og + tk * DV + cw * 16 + gq * 4, oacc[0][p][0], oacc[0][p][1], oacc[0][p][2],
+                           oacc[0][p][3]);
+          }
         }
       }
 
       // ---- state: S <- post * (pre * S + KT^T V) ----
       // every operand is read first (the output phase's registers are free by now),
       // so the 2 NRB products issue back to back
-      Frag<BF16> vb[2], ka[2][NRB];
+      Frag<BF16> vb[NT][2], ka[2][NRB];
       float4 fpost[NRB];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        vb[ks].v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(lds + (b_vb ^ ((unsigned)(4 * ks) << 4))));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const unsigned bt = t ? (b_vb ^ kHalfX) + kHalfOff : b_vb;
+          vb[t][ks].v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(lds + (bt ^ ((unsigned)(4 * ks) << 4))));
+        }
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
           const unsigned a = (b_kt ^ ((unsigned)(((4 * ks) ^ tr_swz(srow(rb, 0))) & 7) << 4)) + srow(rb, 0) * 128;
@@ -768,17 +809,25 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
           const float4 f = *reinterpret_cast<const float4*>(&B.pre[srow(rb, gq * 4)]);
-          sacc[rb][0] *= f.x; sacc[rb][1] *= f.y; sacc[rb][2] *= f.z; sacc[rb][3] *= f.w;
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            sacc[t][rb][0] *= f.x; sacc[t][rb][1] *= f.y; sacc[t][rb][2] *= f.z; sacc[t][rb][3] *= f.w;
+          }
         }
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) mma(sacc[rb], ka[ks][rb], vb[ks]);
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) mma(sacc[t][rb], ka[ks][rb], vb[t][ks]);
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
         const float4 f = fpost[rb];
-        sacc[rb][0] *= f.x; sacc[rb][1] *= f.y; sacc[rb][2] *= f.z; sacc[rb][3] *= f.w;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          sacc[t][rb][0] *= f.x; sacc[t][rb][1] *= f.y; sacc[t][rb][2] *= f.z; sacc[t][rb][3] *= f.w;
+        }
       }
     };
     using T_ = std::integral_constant<bool, true>;
@@ -799,26 +848,37 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     }
     if (s_out) {
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int c = srow(rb, gq * 4 + s);
-          s_out[(long)c * DV + vcol0 + cw * 16 + m] = sacc[rb][s];
-        }
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const int c = srow(rb, gq * 4 + s);
+            s_out[(long)c * DV + vcol0 + 64 * t + cw * 16 + m] = sacc[t][rb][s];
+          }
     }
   }
 }
 
 int launch_chunk_fwd_pipe(const ChunkParams& prm, int dk, bool state_only, int nblocks,
                           hipStream_t stream) {
-  if (dk == 128 && !state_only) {
-    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<128, kFull>), dim3(nblocks), dim3(512), 0, stream, prm);
+  // the slice width must tile d_v exactly; the 128-column slice exists for the full pass only
+  if (prm.dvt * prm.nvt != prm.DV || (prm.dvt != 64 && prm.dvt != 128) ||
+      (prm.dvt == 128 && state_only))
+    return -2;
+  const bool wide = prm.dvt == 128;
+  if (dk == 128 && !state_only && wide) {
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<128, kFull, 2>), dim3(nblocks), dim3(512), 0, stream, prm);
+  } else if (dk == 128 && !state_only) {
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<128, kFull, 1>), dim3(nblocks), dim3(512), 0, stream, prm);
   } else if (dk == 128) {
-    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<128, kStateOnly>), dim3(nblocks), dim3(512), 0, stream, prm);
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<128, kStateOnly, 1>), dim3(nblocks), dim3(512), 0, stream, prm);
+  } else if (dk == 64 && !state_only && wide) {
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<64, kFull, 2>), dim3(nblocks), dim3(512), 0, stream, prm);
   } else if (dk == 64 && !state_only) {
-    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<64, kFull>), dim3(nblocks), dim3(512), 0, stream, prm);
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<64, kFull, 1>), dim3(nblocks), dim3(512), 0, stream, prm);
   } else if (dk == 64) {
-    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<64, kStateOnly>), dim3(nblocks), dim3(512), 0, stream, prm);
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<64, kStateOnly, 1>), dim3(nblocks), dim3(512), 0, stream, prm);
   } else {
     return -2;
   }

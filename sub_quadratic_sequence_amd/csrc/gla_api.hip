@@ -106,6 +106,7 @@ int check_chunk_args(const char* fn, const void* q, const void* k, const void* v
   prm.H = H;
   prm.T = T;
   prm.DV = dv;
+  prm.dvt = 64;
   prm.nvt = nvt;
   prm.xcd_remap = (nblocks % 8 == 0) ? 1 : 0;
   prm.nseg = 1;
@@ -131,6 +132,18 @@ int device_cus() {
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     return 256;
   return n;
+}
+
+// d_v slice of the bf16 forward: 128 columns when the batch still gives every
+// compute unit at least one work item with them (the gating of q and k and the
+// score blocks then serve twice the columns), else 64.
+void choose_slice(gla::ChunkParams& prm, long long units, int dtype) {
+  if (dtype != GLA_BF16 || prm.DV % 128 != 0) return;
+  const long long items = units * (prm.DV / 128);
+  if (items < device_cus()) return;
+  prm.dvt = 128;
+  prm.nvt = prm.DV / 128;
+  prm.xcd_remap = (items % 8 == 0) ? 1 : 0;
 }
 
 // Sequence split: fixed-length bf16 inputs whose work items do not fill the
@@ -176,6 +189,7 @@ int gla_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                                   cu_seqlens, num_seqs, B, H, T, dk, dv, chunk_size, dtype, prm,
                                   units, nothing);
   if (st != GLA_OK || nothing) return st;
+  choose_slice(prm, units, dtype);
   const int rc = gla::launch_chunk_fwd(prm, dk, dtype, (int)(units * prm.nvt),
                                        reinterpret_cast<hipStream_t>(stream));
   return launch_status("gla_chunk_fwd", rc, dk, dtype);
@@ -208,6 +222,7 @@ int gla_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* g,
   int seg_len = T;
   const int nseg = split_plan(cu_seqlens != nullptr, dtype, units * prm.nvt, T, seg_len);
   if (nseg == 1) {
+    choose_slice(prm, units, dtype);
     const int rc = gla::launch_chunk_fwd(prm, dk, dtype, (int)(units * prm.nvt), s);
     return launch_status("gla_chunk_fwd_ws", rc, dk, dtype);
   }

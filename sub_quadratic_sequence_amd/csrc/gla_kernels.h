@@ -18,7 +18,8 @@ struct ChunkParams {
   int H;
   int T;             // tokens per sequence (fixed) or total packed tokens
   int DV;
-  int nvt;           // DV / 64 column slices
+  int dvt;           // columns per d_v slice: 64, or 128 (bf16 full pass only)
+  int nvt;           // DV / dvt column slices
   int xcd_remap;     // 1: consecutive work items share an XCD (grid size % 8 == 0)
   // Sequence split (fixed-length inputs only; nseg = 1 and seg_len = T otherwise):
   // each sequence is cut into nseg segments of seg_len tokens (a multiple of 64,

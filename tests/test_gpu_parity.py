@@ -242,6 +242,71 @@ def test_bf16_shapes(dev, label, B, H, T, dk, dv, gate):
     _check_fixed(d, o, sf, d["s0"], TOL_BF16, label)
 
 
+# ------------------------------------------------------------------ 128-column d_v slice
+# When (units) x (d_v / 128) reaches the device's compute-unit count, the bf16
+# forward gives each workgroup 128 columns of d_v instead of 64.  H is sized
+# from the CU count so that these cases take that slice on any device.
+def _wide_heads(dev, B, dv):
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    per = B * (dv // 128)
+    return (ncu + per - 1) // per
+
+
+WIDE_CASES = [
+    ("dk128_dv256_weak_T130", 2, 130, 128, 256, "weak"),
+    ("dk128_dv128_strong_T97", 4, 97, 128, 128, "strong"),
+    ("dk64_dv256_weak_T200", 2, 200, 64, 256, "weak"),
+    ("dk64_dv384_strong_T65", 1, 65, 64, 384, "strong"),
+]
+
+
+@pytest.mark.parametrize("label,B,T,dk,dv,gate", WIDE_CASES, ids=[c[0] for c in WIDE_CASES])
+def test_bf16_wide_slice(dev, label, B, T, dk, dv, gate):
+    H = _wide_heads(dev, B, dv)
+    w = I.ChunkWorkload("bf16_wide", B=B, H=H, T=T, dk=dk, dv=dv, dtype="bf16", seed=31)
+    say(f"bf16 128-column slice {label}: B={B} H={H} T={T} dk={dk} dv={dv} gate={gate}, initial state")
+    d = I.chunk_inputs(w, gate=gate, s0=True)
+    o, sf = _fwd(dev, d, s0=d["s0"])
+    _check_fixed(d, o, sf, d["s0"], TOL_BF16, label)
+
+
+def test_bf16_wide_slice_extreme_gates(dev):
+    """The 128-column slice with gates that decay by more than 2^100 inside a
+    sub-chunk (exact diagonal partials) and alpha = 0 tokens."""
+    H = _wide_heads(dev, 2, 128)
+    w = I.ChunkWorkload("bf16_wide_extreme", B=2, H=H, T=80, dk=128, dv=128, dtype="bf16", seed=37,
+                        k_scaled=True)
+    say(f"bf16 128-column slice, extreme gates: B=2 H={H} T=80 dk=128 dv=128")
+    d = I.chunk_inputs(w, s0=True)
+    gen = torch.Generator().manual_seed(6)
+    g = d["g"].float()
+    mask = torch.rand(g.shape, generator=gen) < 0.3
+    g = torch.where(mask, -80.0 * torch.rand(g.shape, generator=gen), g)
+    g[0, 1, 40, 7] = float("-inf")
+    g[1, 3, 10:20, :] = float("-inf")
+    d["g"] = g.to(torch.bfloat16)
+    o, sf = _fwd(dev, d, s0=d["s0"])
+    _check_fixed(d, o, sf, d["s0"], TOL_BF16, "wide extreme")
+
+
+def test_bf16_wide_slice_packed(dev):
+    """Packed sequences (empty, one token, ragged tails) on the 128-column slice,
+    dispatched longest sequence first."""
+    lengths = [300, 5, 0, 129, 1, 64, 200, 77]
+    H = _wide_heads(dev, len(lengths), 256)
+    w = I.ChunkWorkload("bf16_wide_varlen", B=1, H=H, T=0, dk=128, dv=256, dtype="bf16", seed=41,
+                        k_scaled=True)
+    say(f"bf16 128-column slice, packed H={H} lengths={lengths} dv=256, strong gates")
+    d = I.chunk_inputs(w, lengths=lengths, s0=True, gate="strong")
+    o, sf = _fwd(dev, d, s0=d["s0"], cu=d["cu_seqlens"])
+    o_ref, s_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], s0=d["s0"],
+                                     cu_seqlens=d["cu_seqlens"], nthreads=NTHREADS)
+    e_o, e_s = unit_err_varlen(o, o_ref, d["cu_seqlens"]), unit_err_fixed(sf, s_ref)
+    print(f"wide packed: O err {e_o:.3e} S err {e_s:.3e}", flush=True)
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+    assert torch.equal(sf[2].cpu(), d["s0"][2])
+
+
 # ------------------------------------------------------------------ invariants
 def test_decode_fp32_small(dev):
     from sub_quadratic_sequence_amd import gla
