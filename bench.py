@@ -431,7 +431,7 @@ def main():
         "mfma_peak_frac": tflops / MFMA_BF16_PEAK_TFLOPS,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "gla::chunk_fwd_pipe_kernel<128>",
+                     "kernel": "gla::chunk_fwd_pipe_kernel<128, kFull, 1> (64-column d_v slice)",
                      "algorithmic_bytes_per_launch": fwd["bytes"],
                      "algorithmic_flops_per_launch": fwd["flops"],
                      "avg_launch_us": t * 1e6},
@@ -475,7 +475,8 @@ def main():
             "workload": vl["w"].name, "us_per_call": vl["t"] * 1e6,
             "tokens_per_s": vl["tokens"] / vl["t"], "tflop_s": vl["flops"] / vl["t"] / 1e12,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": vl["bytes"]},
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": vl["bytes"],
+                         "kernel": "gla::chunk_fwd_pipe_kernel<128, kFull, 2> (128-column d_v slice)"},
         }
     if not args.no_bwd:
         bw = bench_backward(args, torch, gla, inputs)
