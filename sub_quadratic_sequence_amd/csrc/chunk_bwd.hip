@@ -443,11 +443,16 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
 
   // ---- lane roles for the load phase ------------------------------------------
   const bool gl = tid < NGL;               // gating lane: tokens 4tg..+3, channels 8cg..+7
-  const int tg = m, cg = tid >> 4;
   const bool cl = tid >= 256;              // copy lane (values and output gradients)
-  const int cp = tid - 256;
-  const unsigned qk_lane = (unsigned)((4 * tg) * DK + 8 * cg) * 2u;
-  const unsigned h_lane = (unsigned)((c0 + m) * DV + 4 * grp) * 2u;
+  // Lane-dependent offsets are recomputed where they are used, from an opaque
+  // copy of the lane index: kept live across the chunk loop they would not fit
+  // beside the states, and their spill reloads would wait for every
+  // outstanding global access.
+  auto fresh_tid = [&]() __attribute__((always_inline)) {
+    unsigned t = (unsigned)threadIdx.x;
+    pipe_launder(t);
+    return (int)t;
+  };
 
   // Next chunk's raw inputs.  Gating lanes and copy lanes are disjoint, so they
   // share one register array: q, k, g rows (gating) or v, dO units (copy).
@@ -455,6 +460,9 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
   uint4 pf[NPF];
   uint2 rh[NB];   // the chunk-start state of this wave's channels
   auto prefetch = [&](int u) __attribute__((always_inline)) {
+    const int tl = fresh_tid();
+    const int tg = tl & 15, cg = tl >> 4, cp = tl - 256;
+    const unsigned qk_lane = (unsigned)((4 * tg) * DK + 8 * cg) * 2u;
     if (gl) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
@@ -474,6 +482,8 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
     }
   };
   auto prefetch_state = [&](int u) __attribute__((always_inline)) {
+    const int tl = fresh_tid();
+    const unsigned h_lane = (unsigned)((c0 + (tl & 15)) * DV + 4 * ((tl >> 4) & 3)) * 2u;
     if (sw) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) rh[b] = ld8s(rs_h, h_lane + 32u * b, (unsigned)u * DK * DV * 2u);
@@ -506,31 +516,10 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
 
   for (int u = u_hi - 1; u >= u_lo; --u) {
     const long row0 = (long)u * C;   // first token of this chunk (sequence-relative)
-    // Per-lane LDS byte offsets (wave parts included); every access adds a
-    // compile-time constant, which the DS instructions take as an immediate.
-    unsigned r16Q = (m * QP + 4 * grp) * 2, r16V = (m * VP + 4 * grp) * 2;     // 8 B at col 4grp, row m
-    unsigned r32Q = (m * QP + 8 * grp) * 2, r32V = (m * VP + 8 * grp) * 2;     // 16 B at col 8grp, row m
-    unsigned tQ = ((4 * grp + (m >> 2)) * QP + 4 * (m & 3)) * 2;               // transposed, [token][*]
-    unsigned tV = ((4 * grp + (m >> 2)) * VP + 4 * (m & 3)) * 2;
-    unsigned tL = ((4 * grp + (m >> 2)) * L + 4 * (m & 3)) * 2;                // transposed 16x16 tile
-    unsigned r16L = (m * L + 4 * grp) * 2;
-    unsigned tQc = tQ + 2 * c0, tVn = tV + 2 * n0;
-    unsigned tS = ((8 * grp + (m >> 2)) * SP + n0 + 4 * (m & 3)) * 2;          // transposed state rows
-    unsigned wS = ((c0 + m) * SP + 4 * grp) * 2;                               // state tile writes
-    unsigned eD = (m * DP + c0 + 4 * grp) * 4, eQ = (m * QP + c0 + 4 * grp) * 2;
-    unsigned fC = (c0 + m) * 4;
-    pipe_launder(r16Q); pipe_launder(r16V); pipe_launder(r32Q); pipe_launder(r32V);
-    pipe_launder(tQ); pipe_launder(tV); pipe_launder(tL); pipe_launder(r16L);
-    pipe_launder(tQc); pipe_launder(tVn); pipe_launder(tS); pipe_launder(wS);
-    pipe_launder(eD); pipe_launder(eQ); pipe_launder(fC);
-
     // ======================= load phase =======================
-    if (sw) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-        Ht[b] = f32x4{lo_bf16(rh[b].x), hi_bf16(rh[b].x), lo_bf16(rh[b].y), hi_bf16(rh[b].y)};
-    }
     if (gl) {
+      const int tl = fresh_tid();
+      const int tg = tl & 15, cg = tl >> 4;
       // log2 cumulative gate over the chunk, per channel
       float gm[4][8];
       const unsigned* gw[4] = {&pf[8].x, &pf[9].x, &pf[10].x, &pf[11].x};
@@ -595,6 +584,7 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
       }
     }
     if (cl) {
+      const int cp = fresh_tid() - 256;
 #pragma unroll
       for (int it = 0; it < NCP; ++it) {
         const int idx = cp + 256 * it, row = idx / NVU, un = idx % NVU;
@@ -603,6 +593,28 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
       }
     }
     barrier_lds();
+    // Per-lane LDS byte offsets (wave parts included); every access adds a
+    // compile-time constant, which the DS instructions take as an immediate.
+    // Computed after the load phase, from an opaque lane index, so that they
+    // are neither live during it nor kept across the loop.
+    const int tl = fresh_tid();
+    const int m = tl & 15, grp = (tl >> 4) & 3;
+    unsigned r16Q = (m * QP + 4 * grp) * 2, r16V = (m * VP + 4 * grp) * 2;     // 8 B at col 4grp, row m
+    unsigned r32Q = (m * QP + 8 * grp) * 2, r32V = (m * VP + 8 * grp) * 2;     // 16 B at col 8grp, row m
+    unsigned tQ = ((4 * grp + (m >> 2)) * QP + 4 * (m & 3)) * 2;               // transposed, [token][*]
+    unsigned tV = ((4 * grp + (m >> 2)) * VP + 4 * (m & 3)) * 2;
+    unsigned tL = ((4 * grp + (m >> 2)) * L + 4 * (m & 3)) * 2;                // transposed 16x16 tile
+    unsigned r16L = (m * L + 4 * grp) * 2;
+    unsigned tQc = tQ + 2 * c0, tVn = tV + 2 * n0;
+    unsigned tS = ((8 * grp + (m >> 2)) * SP + n0 + 4 * (m & 3)) * 2;          // transposed state rows
+    unsigned wS = ((c0 + m) * SP + 4 * grp) * 2;                               // state tile writes
+    unsigned eD = (m * DP + c0 + 4 * grp) * 4, eQ = (m * QP + c0 + 4 * grp) * 2;
+    unsigned fC = (c0 + m) * 4;
+    pipe_launder(r16Q); pipe_launder(r16V); pipe_launder(r32Q); pipe_launder(r32V);
+    pipe_launder(tQ); pipe_launder(tV); pipe_launder(tL); pipe_launder(r16L);
+    pipe_launder(tQc); pipe_launder(tVn); pipe_launder(tS); pipe_launder(wS);
+    pipe_launder(eD); pipe_launder(eQ); pipe_launder(fC);
+
 
     // =============== score blocks of the four sub-chunks ===============
     {
@@ -626,6 +638,13 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
     barrier_lds();
 
     // ======================= forward sweep: dq =======================
+    // the chunk-start state, widened only now: during the load phase its bf16
+    // form takes half the registers
+    if (sw) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        Ht[b] = f32x4{lo_bf16(rh[b].x), hi_bf16(rh[b].x), lo_bf16(rh[b].y), hi_bf16(rh[b].y)};
+    }
     float qd[NS][4];   // q~ * (dq before its 2^Delta factor), for dg
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
