@@ -62,6 +62,34 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// LDS tiles.  Rows are 256 bytes (16 units of 16 bytes; a tile of 64 bf16
+// columns uses half of each row, the fp32 Delta tile of 128 channels spans two
+// 256-byte halves), and unit u of row r is stored at unit u ^ swz(r).  gfx950's
+// LDS serves 8-byte and transposing reads 32 consecutive lanes per pass over
+// 64 banks, 16-byte reads in passes that pair lane quads of equal parity of
+// lane bits 2-4, and 8- and 16-byte writes 16 and 8 consecutive lanes per pass
+// over 32 banks (all measured with rocprofv3's SQ_LDS_BANK_CONFLICT).  With
+// this swz every access shape of the kernels below is free of bank conflicts:
+// 8- and 16-byte fragment reads on 16 consecutive rows, transposing reads on
+// 8 rows (4 consecutive rows per 16 lanes, also 8-row strided pairs), the
+// gating writes to rows 4t + a (t = 0..7) and the row-wise copies.  The one
+// exception is the state tile's 8-byte writes, 2-way by their lane shape.
+// swz is linear over the row bits: for row and unit parts with disjoint bits an
+// address is (lane part) ^ cx(compile-time part) + ca(compile-time part).
+__host__ __device__ constexpr unsigned swz(unsigned r) {
+  return ((r & 1) ? 8u : 0u) ^ ((r & 2) ? 4u : 0u) ^ ((r & 4) ? 2u : 0u) ^ ((r & 8) ? 3u : 0u) ^
+         ((r & 16) ? 4u : 0u);
+}
+// byte offset of byte b of unit u in row r of a tile with RB-byte rows
+__host__ __device__ constexpr unsigned toff(unsigned r, unsigned u, unsigned b, unsigned RB = 256) {
+  return r * RB + (((u & 15u) ^ swz(r)) << 4) + ((u & ~15u) << 4) + b;
+}
+// XOR and additive parts of a compile-time row cr and unit cu
+__host__ __device__ constexpr unsigned cx(unsigned cr, unsigned cu) { return ((cu & 15u) ^ swz(cr)) << 4; }
+__host__ __device__ constexpr unsigned ca(unsigned cr, unsigned cu, unsigned RB = 256) {
+  return cr * RB + ((cu & ~15u) << 4);
+}
+
 // MFMA operand fragments.  A 16-deep operand gives lane (m = lane % 16,
 // grp = lane / 16) four contraction indices 4 grp + 0..3 of row (A) or column
 // (B) m; a 32-deep operand gives it 8 grp + 0..7.  Both operands of a product
@@ -93,6 +121,14 @@ __device__ __forceinline__ s16x8 tr32(const unsigned short* base, int pitch, int
 // operands zero (slots 4-7 pair with slots 4-7, so they add exactly 0).  The
 // legacy 16x16x16 bf16 instruction is not used: its results were read back too
 // early by the generated code on gfx950 (wrong values, no fault).
+// The same from a swizzled tile: lane part ln, compile-time row r0 and unit u0;
+// the second half reads 4 rows further on.
+__device__ __forceinline__ s16x4 trs(const char* tile, unsigned ln, unsigned r0, unsigned u0) {
+  return tr_read(reinterpret_cast<const unsigned short*>(tile + ((ln ^ cx(r0, u0)) + ca(r0, u0))));
+}
+__device__ __forceinline__ s16x8 tr32s(const char* tile, unsigned ln, unsigned r0, unsigned u0) {
+  return __builtin_shufflevector(trs(tile, ln, r0, u0), trs(tile, ln, r0 + 4, u0), 0, 1, 2, 3, 4, 5, 6, 7);
+}
 __device__ __forceinline__ void mma16(f32x4& acc, s16x4 a, s16x4 b) {
   const s16x4 z = {0, 0, 0, 0};
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -178,14 +214,13 @@ __device__ __forceinline__ Seq seq_of(const BwdParams& prm, int n, int h) {
 template <int DK, bool REV>
 __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
   using namespace bwd;
-  constexpr int KP = DK + 8;       // k-bar tile pitch (elements)
-  constexpr int VP = 64 + 8;       // value tile pitch
   constexpr int NCG = DK / 8;      // 8-channel groups
   constexpr int NGL = 16 * NCG;    // gating lanes
   constexpr int CB = DK / 16;      // 16-channel blocks
-  // two buffers: the gating of chunk u+1 overlaps the products of chunk u
-  __shared__ __attribute__((aligned(16))) unsigned short kbs[2][C * KP];
-  __shared__ __attribute__((aligned(16))) unsigned short vss[2][C * VP];
+  // two buffers: the gating of chunk u+1 overlaps the products of chunk u;
+  // k-bar [token][channel] and v [token][column] tiles, swizzled 256-byte rows
+  __shared__ __attribute__((aligned(256))) char kbs[2][C * 256];
+  __shared__ __attribute__((aligned(256))) char vss[2][C * 256];
   __shared__ float decs[2][DK];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, m = lane & 15, grp = lane >> 4;
@@ -249,8 +284,8 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
 
   // stage chunk u (its raw inputs are in registers) into buffer b
   auto stage = [&](int b) __attribute__((always_inline)) {
-    unsigned short* const kb = kbs[b];
-    unsigned short* const vs = vss[b];
+    char* const kb = kbs[b];
+    char* const vs = vss[b];
     float* const dec = decs[b];
     if (gl) {
       float pp[4][8];
@@ -290,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
           const unsigned w = kw[a][i >> 1];
           kbv[i] = ((i & 1) ? hi_bf16(w) : lo_bf16(w)) * fast_exp2(REV ? pp[a][i] : last[i] - pp[a][i]);
         }
-        *reinterpret_cast<uint4*>(kb + (4 * tg + a) * KP + 8 * cg) =
+        *reinterpret_cast<uint4*>(kb + ((toff(4 * tg, cg, 0) ^ cx(a, 0)) + ca(a, 0))) =
             uint4{pack_bf16x2(kbv[0], kbv[1]), pack_bf16x2(kbv[2], kbv[3]), pack_bf16x2(kbv[4], kbv[5]),
                   pack_bf16x2(kbv[6], kbv[7])};
       }
@@ -302,10 +337,8 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
       }
     }
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int idx = tid + 256 * it, row = idx >> 3, un = idx & 7;
-      *reinterpret_cast<uint4*>(vs + row * VP + 8 * un) = rv[it];
-    }
+    for (int it = 0; it < 2; ++it)   // row (tid >> 3) + 32 it, unit tid & 7
+      *reinterpret_cast<uint4*>(vs + ((toff(tid >> 3, tid & 7, 0) ^ cx(32 * it, 0)) + ca(32 * it, 0))) = rv[it];
   };
 
   const int nit = u_hi - u_lo;
@@ -324,8 +357,8 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
       if (it_u + 2 < nit) prefetch(REV ? u - 2 : u + 2);
     }
     // H_u (the state entering chunk u) to the workspace, then the update
-    const unsigned short* const kb = kbs[b];
-    const unsigned short* const vs = vss[b];
+    const char* const kb = kbs[b];
+    const char* const vs = vss[b];
     const float* const dec = decs[b];
     unsigned short* const hu = hs + (long)u * DK * DV;
 #pragma unroll
@@ -336,11 +369,14 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
       const float d = dec[16 * i + m];
       Ht[i] = Ht[i] * d;
     }
+    // transposing reads: rows 32 ks + 8 grp + (m >> 2) (+ 4), columns 16 j + 4 (m & 3)
+    const unsigned trl = toff(8 * grp + (m >> 2), (m & 3) >> 1, 8 * (m & 1));
+    const unsigned trv = toff(8 * grp + (m >> 2), 2 * nb + ((m & 3) >> 1), 8 * (m & 1));
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const s16x8 x = tr32(vs, VP, 32 * ks, 16 * nb, m, grp);
+      const s16x8 x = tr32s(vs, trv, 32 * ks, 0);
 #pragma unroll
-      for (int i = 0; i < CB; ++i) mma32(Ht[i], x, tr32(kb, KP, 32 * ks, 16 * i, m, grp));
+      for (int i = 0; i < CB; ++i) mma32(Ht[i], x, tr32s(kb, trl, 32 * ks, 2 * i));
     }
     barrier_lds();
   }
@@ -378,10 +414,8 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
 template <int DK, int DV>
 __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
   using namespace bwd;
-  constexpr int QP = DK + 8;       // [token][channel] bf16 tile pitch
-  constexpr int VP = DV + 8;       // [token][column] bf16 tile pitch
-  constexpr int SP = DV + 8;       // [channel][column] state tile pitch
-  constexpr int DP = DK + 4;       // [token][channel] fp32 Delta pitch
+  constexpr unsigned RD = DK * 4;  // bytes per row of the fp32 Delta tile
+  constexpr int LP = L + 8;        // [i][j] 16x16 score tile pitch (elements)
   constexpr int CB = DK / 16, NB = DV / 16;
   constexpr int NCG = DK / 8;
   constexpr int NGL = 16 * NCG;             // gating lanes (waves 0 .. NGL/64-1)
@@ -389,22 +423,25 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
   constexpr int NCP = C * NVU / 256;        // units per copy lane (waves 4-7)
   static_assert(NGL <= 256, "shape");
 
+  // bf16 tiles with swizzled 256-byte rows (see swz), then the unswizzled rest
   struct Smem {
-    unsigned short qs[C * QP];     // q~  [token][channel]
-    unsigned short ks[C * QP];     // k~  [token][channel]
-    unsigned short vs[C * VP];     // v   [token][column]
-    unsigned short os[C * VP];     // dO  [token][column]
-    unsigned short ss[DK * SP];    // B^ (bf16) [channel][column]
-    unsigned short as[NS][L * L];  // A = dO V^T of sub-chunk s, [i][j], j <= i
-    unsigned short ps[NS][L * L];  // P = q~ k~^T of sub-chunk s, [i][j], j <= i
-    float dl[C * DP];              // Delta = Gamma - b_s (log2), [token][channel]
+    char qs[C * 256];              // q~  [token][channel]
+    char ks[C * 256];              // k~  [token][channel]
+    char vs[C * 256];              // v   [token][column]
+    char os[C * 256];              // dO  [token][column]
+    char ss[DK * 256];             // B^ (bf16) [channel][column]
+    char dl[C * RD];               // Delta = Gamma - b_s (log2), fp32 [token][channel], swizzled units
+    unsigned short as[NS][L * LP]; // A = dO V^T of sub-chunk s, [i][j], j <= i
+    unsigned short ps[NS][L * LP]; // P = q~ k~^T of sub-chunk s, [i][j], j <= i
     float fac[2][NS][DK];          // 0: 2^(b_s - Gamma_{s-1,last}), 1: 2^(Gamma_{s,last} - b_s)
   };
-  __shared__ __attribute__((aligned(16))) Smem sm;
+  __shared__ __attribute__((aligned(256))) Smem sm;
   char* const lds = reinterpret_cast<char*>(&sm);
   constexpr unsigned oQ = offsetof(Smem, qs), oK = offsetof(Smem, ks), oV = offsetof(Smem, vs),
                      oO = offsetof(Smem, os), oS = offsetof(Smem, ss), oA = offsetof(Smem, as),
                      oP = offsetof(Smem, ps), oD = offsetof(Smem, dl), oF = offsetof(Smem, fac);
+  static_assert(oQ % 256 == 0 && oK % 256 == 0 && oV % 256 == 0 && oO % 256 == 0 && oS % 256 == 0 &&
+                oD % 256 == 0, "swizzled tiles start on 256-byte boundaries");
   auto rd8 = [&](unsigned off) __attribute__((always_inline)) {
     return *reinterpret_cast<const s16x4*>(lds + off);
   };
@@ -566,15 +603,19 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
           qv[i] = ((i & 1) ? hi_bf16(wq) : lo_bf16(wq)) * fast_exp2(d);
           kv[i] = ((i & 1) ? hi_bf16(wk) : lo_bf16(wk)) * fast_exp2(-d);
         }
-        const int r = 4 * tg + a;
-        *reinterpret_cast<uint4*>(sm.qs + r * QP + 8 * cg) =
+        // row 4 tg + a: unit cg of the token tiles, units 2 cg and 2 cg + 1 of Delta
+        const unsigned wt = (toff(4 * tg, cg, 0) ^ cx(a, 0)) + ca(a, 0);
+        const unsigned wd = toff(4 * tg, 2 * cg, 0, RD);
+        *reinterpret_cast<uint4*>(lds + oQ + wt) =
             uint4{pack_bf16x2(qv[0], qv[1]), pack_bf16x2(qv[2], qv[3]), pack_bf16x2(qv[4], qv[5]),
                   pack_bf16x2(qv[6], qv[7])};
-        *reinterpret_cast<uint4*>(sm.ks + r * QP + 8 * cg) =
+        *reinterpret_cast<uint4*>(lds + oK + wt) =
             uint4{pack_bf16x2(kv[0], kv[1]), pack_bf16x2(kv[2], kv[3]), pack_bf16x2(kv[4], kv[5]),
                   pack_bf16x2(kv[6], kv[7])};
-        *reinterpret_cast<float4*>(sm.dl + r * DP + 8 * cg) = make_float4(dv8[0], dv8[1], dv8[2], dv8[3]);
-        *reinterpret_cast<float4*>(sm.dl + r * DP + 8 * cg + 4) = make_float4(dv8[4], dv8[5], dv8[6], dv8[7]);
+        *reinterpret_cast<float4*>(lds + oD + ((wd ^ cx(a, 0)) + ca(a, 0, RD))) =
+            make_float4(dv8[0], dv8[1], dv8[2], dv8[3]);
+        *reinterpret_cast<float4*>(lds + oD + ((wd ^ cx(a, 1)) + ca(a, 1, RD))) =
+            make_float4(dv8[4], dv8[5], dv8[6], dv8[7]);
       }
       if ((tg & 3) == 0) {
         *reinterpret_cast<float4*>(&sm.fac[0][s][8 * cg]) = make_float4(f0[0], f0[1], f0[2], f0[3]);
@@ -586,10 +627,11 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
     if (cl) {
       const int cp = fresh_tid() - 256;
 #pragma unroll
-      for (int it = 0; it < NCP; ++it) {
-        const int idx = cp + 256 * it, row = idx / NVU, un = idx % NVU;
-        *reinterpret_cast<uint4*>(sm.vs + row * VP + 8 * un) = pf[it];
-        *reinterpret_cast<uint4*>(sm.os + row * VP + 8 * un) = pf[NCP + it];
+      for (int it = 0; it < NCP; ++it) {   // row cp / NVU + it * 256 / NVU, unit cp % NVU
+        constexpr unsigned RI = 256 / NVU;
+        const unsigned wc = (toff(cp / NVU, cp % NVU, 0) ^ cx(RI * it, 0)) + ca(RI * it, 0);
+        *reinterpret_cast<uint4*>(lds + oV + wc) = pf[it];
+        *reinterpret_cast<uint4*>(lds + oO + wc) = pf[NCP + it];
       }
     }
     barrier_lds();
@@ -599,41 +641,45 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
     // are neither live during it nor kept across the loop.
     const int tl = fresh_tid();
     const int m = tl & 15, grp = (tl >> 4) & 3;
-    unsigned r16Q = (m * QP + 4 * grp) * 2, r16V = (m * VP + 4 * grp) * 2;     // 8 B at col 4grp, row m
-    unsigned r32Q = (m * QP + 8 * grp) * 2, r32V = (m * VP + 8 * grp) * 2;     // 16 B at col 8grp, row m
-    unsigned tQ = ((4 * grp + (m >> 2)) * QP + 4 * (m & 3)) * 2;               // transposed, [token][*]
-    unsigned tV = ((4 * grp + (m >> 2)) * VP + 4 * (m & 3)) * 2;
-    unsigned tL = ((4 * grp + (m >> 2)) * L + 4 * (m & 3)) * 2;                // transposed 16x16 tile
-    unsigned r16L = (m * L + 4 * grp) * 2;
-    unsigned tQc = tQ + 2 * c0, tVn = tV + 2 * n0;
-    unsigned tS = ((8 * grp + (m >> 2)) * SP + n0 + 4 * (m & 3)) * 2;          // transposed state rows
-    unsigned wS = ((c0 + m) * SP + 4 * grp) * 2;                               // state tile writes
-    unsigned eD = (m * DP + c0 + 4 * grp) * 4, eQ = (m * QP + c0 + 4 * grp) * 2;
+    // swizzled tiles (row, unit, byte; see toff):
+    unsigned r16 = toff(m, grp >> 1, 8 * (grp & 1));                 // 8 B at column 4 grp of row m
+    unsigned r32 = toff(m, grp, 0);                                  // 16 B at column 8 grp of row m
+    unsigned tV = toff(4 * grp + (m >> 2), (m & 3) >> 1, 8 * (m & 1));   // transposing: rows 4grp + m/4
+    unsigned tW = toff(4 * grp + (m >> 2), 2 * wave + ((m & 3) >> 1), 8 * (m & 1));   // ... at column 16 wave
+    unsigned tS = toff(8 * grp + (m >> 2), 2 * wave + ((m & 3) >> 1), 8 * (m & 1));   // state rows 8grp + m/4
+    unsigned wS = toff(c0 + m, grp >> 1, 8 * (grp & 1));             // state tile writes, row c0 + m
+    unsigned eQ = toff(m, 2 * wave + (grp >> 1), 8 * (grp & 1));     // channels c0 + 4 grp of row m
+    unsigned eD = toff(m, 4 * wave + grp, 0, RD);                    // the same in the Delta tile
+    // 16x16 score tiles (row pitch LP)
+    unsigned tL = ((4 * grp + (m >> 2)) * LP + 4 * (m & 3)) * 2;     // transposed
+    unsigned r16L = (m * LP + 4 * grp) * 2;
     unsigned fC = (c0 + m) * 4;
-    pipe_launder(r16Q); pipe_launder(r16V); pipe_launder(r32Q); pipe_launder(r32V);
-    pipe_launder(tQ); pipe_launder(tV); pipe_launder(tL); pipe_launder(r16L);
-    pipe_launder(tQc); pipe_launder(tVn); pipe_launder(tS); pipe_launder(wS);
-    pipe_launder(eD); pipe_launder(eQ); pipe_launder(fC);
+    pipe_launder(r16); pipe_launder(r32); pipe_launder(tV); pipe_launder(tW); pipe_launder(tS);
+    pipe_launder(wS); pipe_launder(eQ); pipe_launder(eD); pipe_launder(tL); pipe_launder(r16L);
+    pipe_launder(fC);
+    // address of a swizzled-tile access: lane part ln, compile-time row r and unit u
+    auto at = [](unsigned ln, unsigned r, unsigned u) __attribute__((always_inline)) {
+      return (ln ^ cx(r, u)) + ca(r, u);
+    };
 
 
     // =============== score blocks of the four sub-chunks ===============
     {
       const int s = wave & 3;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const unsigned b = toff(16 * s + m, grp, 0);   // 16 B at column 8 grp of row 16 s + m
       if (wave < 4) {   // A^T[j][i] = sum_n v_j[n] dO_i[n]
-        const unsigned b = r32V + (unsigned)(16 * s * VP * 2);
 #pragma unroll
-        for (int kk = 0; kk < DV / 32; ++kk) mma32(acc, rd16(oV + b + 64 * kk), rd16(oO + b + 64 * kk));
+        for (int kk = 0; kk < DV / 32; ++kk) mma32(acc, rd16(oV + at(b, 0, 4 * kk)), rd16(oO + at(b, 0, 4 * kk)));
       } else {          // P^T[j][i] = sum_c k~_j[c] q~_i[c]
-        const unsigned b = r32Q + (unsigned)(16 * s * QP * 2);
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) mma32(acc, rd16(oK + b + 64 * kk), rd16(oQ + b + 64 * kk));
+        for (int kk = 0; kk < DK / 32; ++kk) mma32(acc, rd16(oK + at(b, 0, 4 * kk)), rd16(oQ + at(b, 0, 4 * kk)));
       }
       // lane holds rows j = 4 grp + r at column i = m; keep j <= i, store as [i][j]
       float x[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[r] = (4 * grp + r <= m) ? acc[r] : 0.f;
-      *reinterpret_cast<uint2*>(lds + (wave < 4 ? oA : oP) + s * L * L * 2 + r16L) = pack4(x[0], x[1], x[2], x[3]);
+      *reinterpret_cast<uint2*>(lds + (wave < 4 ? oA : oP) + s * L * LP * 2 + r16L) = pack4(x[0], x[1], x[2], x[3]);
     }
     barrier_lds();
 
@@ -658,16 +704,15 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
         for (int b = 0; b < NB; ++b) Ht[b] = Ht[b] * f;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < DV / 32; ++kk) {   // H^[c][n] dO[i][n]
-          const unsigned b = oO + r16V + (unsigned)((16 * s * VP + 32 * kk) * 2);
-          mma32(acc, state_op(Ht[2 * kk], Ht[2 * kk + 1]), cat(rd8(b), rd8(b + 32)));
-        }
+        for (int kk = 0; kk < DV / 32; ++kk)   // H^[c][n] dO[i][n]
+          mma32(acc, state_op(Ht[2 * kk], Ht[2 * kk + 1]),
+                cat(rd8(oO + at(r16, 16 * s, 4 * kk)), rd8(oO + at(r16, 16 * s, 4 * kk + 2))));
         // k~^T[c][j] A[i][j] over j in the sub-chunk
-        const s16x4 kt = rdt(oK + tQc + (unsigned)(16 * s * QP * 2));
-        mma16(acc, kt, rd8(oA + s * L * L * 2 + r16L));
+        const s16x4 kt = rdt(oK + at(tW, 16 * s, 0));
+        mma16(acc, kt, rd8(oA + s * L * LP * 2 + r16L));
         // lane: channels c0 + 4 grp + r at token 16 s + m
-        const float4 d = *reinterpret_cast<const float4*>(lds + oD + eD + (unsigned)(16 * s * DP * 4));
-        const uint2 qv = *reinterpret_cast<const uint2*>(lds + oQ + eQ + (unsigned)(16 * s * QP * 2));
+        const float4 d = *reinterpret_cast<const float4*>(lds + oD + ((eD ^ cx(16 * s, 0)) + ca(16 * s, 0, RD)));
+        const uint2 qv = *reinterpret_cast<const uint2*>(lds + oQ + at(eQ, 16 * s, 0));
         qd[s][0] = lo_bf16(qv.x) * acc[0];
         qd[s][1] = hi_bf16(qv.x) * acc[1];
         qd[s][2] = lo_bf16(qv.y) * acc[2];
@@ -680,7 +725,7 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
         // H <- 2^(Gamma_{s,last} - b_s) (H^ + k~^T V) over the sub-chunk's tokens
 #pragma unroll
         for (int b = 0; b < NB; ++b)
-          mma16(Ht[b], rdt(oV + tV + (unsigned)((16 * s * VP + 16 * b) * 2)), kt);
+          mma16(Ht[b], rdt(oV + at(tV, 16 * s, 2 * b)), kt);
         const float f1 = *reinterpret_cast<const float*>(lds + oF + (NS + s) * DK * 4 + fC);
 #pragma unroll
         for (int b = 0; b < NB; ++b) Ht[b] = Ht[b] * f1;
@@ -711,22 +756,21 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           Bt[b] = Bt[b] * f;
-          *reinterpret_cast<uint2*>(lds + oS + wS + 32 * b) = pack4(Bt[b][0], Bt[b][1], Bt[b][2], Bt[b][3]);
+          *reinterpret_cast<uint2*>(lds + oS + at(wS, 0, 2 * b)) = pack4(Bt[b][0], Bt[b][1], Bt[b][2], Bt[b][3]);
         }
       }
       barrier_lds();
       if (sw) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < DV / 32; ++kk) {   // B^[c][n] v[j][n]
-          const unsigned b = oV + r16V + (unsigned)((16 * s * VP + 32 * kk) * 2);
-          mma32(acc, state_op(Bt[2 * kk], Bt[2 * kk + 1]), cat(rd8(b), rd8(b + 32)));
-        }
+        for (int kk = 0; kk < DV / 32; ++kk)   // B^[c][n] v[j][n]
+          mma32(acc, state_op(Bt[2 * kk], Bt[2 * kk + 1]),
+                cat(rd8(oV + at(r16, 16 * s, 4 * kk)), rd8(oV + at(r16, 16 * s, 4 * kk + 2))));
         // q~^T[c][i] A[i][j] over i in the sub-chunk
-        const s16x4 qt = rdt(oQ + tQc + (unsigned)(16 * s * QP * 2));
-        mma16(acc, qt, rdt(oA + s * L * L * 2 + tL));
-        const float4 d = *reinterpret_cast<const float4*>(lds + oD + eD + (unsigned)(16 * s * DP * 4));
-        const uint2 kv = *reinterpret_cast<const uint2*>(lds + oK + eQ + (unsigned)(16 * s * QP * 2));
+        const s16x4 qt = rdt(oQ + at(tW, 16 * s, 0));
+        mma16(acc, qt, rdt(oA + s * L * LP * 2 + tL));
+        const float4 d = *reinterpret_cast<const float4*>(lds + oD + ((eD ^ cx(16 * s, 0)) + ca(16 * s, 0, RD)));
+        const uint2 kv = *reinterpret_cast<const uint2*>(lds + oK + at(eQ, 16 * s, 0));
         float x[4] = {qd[s][0] - lo_bf16(kv.x) * acc[0], qd[s][1] - hi_bf16(kv.x) * acc[1],
                       qd[s][2] - lo_bf16(kv.y) * acc[2], qd[s][3] - hi_bf16(kv.y) * acc[3]};
         // reverse inclusive sum over the 16 tokens of the sub-chunk (lanes m)
@@ -751,7 +795,7 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
         // B <- 2^(b_s - Gamma_{s-1,last}) (B^ + q~^T dO) over the sub-chunk's tokens
 #pragma unroll
         for (int b = 0; b < NB; ++b)
-          mma16(Bt[b], rdt(oO + tV + (unsigned)((16 * s * VP + 16 * b) * 2)), qt);
+          mma16(Bt[b], rdt(oO + at(tV, 16 * s, 2 * b)), qt);
         const float f0 = *reinterpret_cast<const float*>(lds + oF + s * DK * 4 + fC);
 #pragma unroll
         for (int b = 0; b < NB; ++b) Bt[b] = Bt[b] * f0;
@@ -759,12 +803,11 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
       if (vw) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) {   // B^^T[n][c] k~[j][c]
-          const unsigned b = oS + tS + (unsigned)(32 * kk * SP * 2);
-          mma32(acc, cat(rdt(b), rdt(b + 4 * SP * 2)), rd16(oK + r32Q + (unsigned)((16 * s * QP + 32 * kk) * 2)));
-        }
+        for (int kk = 0; kk < DK / 32; ++kk)   // B^^T[n][c] k~[j][c]
+          mma32(acc, cat(rdt(oS + at(tS, 32 * kk, 0)), rdt(oS + at(tS, 32 * kk + 4, 0))),
+                rd16(oK + at(r32, 16 * s, 4 * kk)));
         // dO^T[n][i] P[i][j] over i in the sub-chunk
-        mma16(acc, rdt(oO + tVn + (unsigned)(16 * s * VP * 2)), rdt(oP + s * L * L * 2 + tL));
+        mma16(acc, rdt(oO + at(tW, 16 * s, 0)), rdt(oP + s * L * LP * 2 + tL));
         const long t = row0 + 16 * s + m;
         if (t < sq.len)
           *reinterpret_cast<uint2*>(dv_out + t * DV + n0 + 4 * grp) = pack4(acc[0], acc[1], acc[2], acc[3]);
