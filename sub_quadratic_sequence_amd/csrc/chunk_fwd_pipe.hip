@@ -862,26 +862,27 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
 
 int launch_chunk_fwd_pipe(const ChunkParams& prm, int dk, bool state_only, int nblocks,
                           hipStream_t stream) {
-  // the slice width must tile d_v exactly; the 128-column slice exists for the full pass only
-  if (prm.dvt * prm.nvt != prm.DV || (prm.dvt != 64 && prm.dvt != 128) ||
-      (prm.dvt == 128 && state_only))
-    return -2;
+  // the slice width must tile d_v exactly
+  if (prm.dvt * prm.nvt != prm.DV || (prm.dvt != 64 && prm.dvt != 128)) return -2;
   const bool wide = prm.dvt == 128;
-  if (dk == 128 && !state_only && wide) {
-    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<128, kFull, 2>), dim3(nblocks), dim3(512), 0, stream, prm);
-  } else if (dk == 128 && !state_only) {
-    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<128, kFull, 1>), dim3(nblocks), dim3(512), 0, stream, prm);
-  } else if (dk == 128) {
-    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<128, kStateOnly, 1>), dim3(nblocks), dim3(512), 0, stream, prm);
-  } else if (dk == 64 && !state_only && wide) {
-    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<64, kFull, 2>), dim3(nblocks), dim3(512), 0, stream, prm);
-  } else if (dk == 64 && !state_only) {
-    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<64, kFull, 1>), dim3(nblocks), dim3(512), 0, stream, prm);
+#define GLA_PIPE(D, M, N) \
+  hipLaunchKernelGGL((chunk_fwd_pipe_kernel<D, M, N>), dim3(nblocks), dim3(512), 0, stream, prm)
+  if (dk == 128) {
+    if (state_only) {
+      if (wide) GLA_PIPE(128, kStateOnly, 2); else GLA_PIPE(128, kStateOnly, 1);
+    } else {
+      if (wide) GLA_PIPE(128, kFull, 2); else GLA_PIPE(128, kFull, 1);
+    }
   } else if (dk == 64) {
-    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<64, kStateOnly, 1>), dim3(nblocks), dim3(512), 0, stream, prm);
+    if (state_only) {
+      if (wide) GLA_PIPE(64, kStateOnly, 2); else GLA_PIPE(64, kStateOnly, 1);
+    } else {
+      if (wide) GLA_PIPE(64, kFull, 2); else GLA_PIPE(64, kFull, 1);
+    }
   } else {
     return -2;
   }
+#undef GLA_PIPE
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -146,6 +146,7 @@ void choose_slice(gla::ChunkParams& prm, long long units, int dtype) {
   prm.xcd_remap = (items % 8 == 0) ? 1 : 0;
 }
 
+
 // Sequence split: fixed-length bf16 inputs whose work items do not fill the
 // device are cut into segments of at least kMinSegChunks chunks, about enough to
 // give every compute unit one work item.  Returns the segment count (1 = none)
@@ -165,6 +166,16 @@ int split_plan(bool varlen, int dtype, long long items, int T, int& seg_len) {
   const int seg_chunks = (int)((nch + nseg - 1) / nseg);
   seg_len = seg_chunks * 64;
   return (T + seg_len - 1) / seg_len;
+}
+
+// Segment plan of the forward: split only when the 64-column work items do not
+// fill the device; a split then uses the 128-column slice when d_v allows it
+// (bf16), so the plan cuts each sequence into about twice as many segments.
+int fwd_split_plan(bool varlen, int dtype, long long units, int dv, int T, int& seg_len) {
+  seg_len = T;
+  if (units * (dv / 64) >= device_cus()) return 1;
+  const long long items = units * ((dtype == GLA_BF16 && dv % 128 == 0) ? dv / 128 : dv / 64);
+  return split_plan(varlen, dtype, items, T, seg_len);
 }
 
 size_t split_bytes(long long units, int nseg, int dk, int dv) {
@@ -201,7 +212,7 @@ size_t gla_chunk_fwd_workspace_size(int num_seqs, int B, int H, int T, int dk, i
   if (dv % 64 != 0) return 0;
   const long long units = (long long)B * H;
   int seg_len = 0;
-  const int nseg = split_plan(num_seqs > 0, dtype, units * (dv / 64), T, seg_len);
+  const int nseg = fwd_split_plan(num_seqs > 0, dtype, units, dv, T, seg_len);
   return nseg > 1 ? split_bytes(units, nseg, dk, dv) : 0;
 }
 
@@ -220,11 +231,15 @@ int gla_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* g,
   if (st != GLA_OK || nothing) return st;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int seg_len = T;
-  const int nseg = split_plan(cu_seqlens != nullptr, dtype, units * prm.nvt, T, seg_len);
+  const int nseg = fwd_split_plan(cu_seqlens != nullptr, dtype, units, dv, T, seg_len);
   if (nseg == 1) {
     choose_slice(prm, units, dtype);
     const int rc = gla::launch_chunk_fwd(prm, dk, dtype, (int)(units * prm.nvt), s);
     return launch_status("gla_chunk_fwd_ws", rc, dk, dtype);
+  }
+  if (dtype == GLA_BF16 && dv % 128 == 0) {   // split work items take the 128-column slice
+    prm.dvt = 128;
+    prm.nvt = dv / 128;
   }
   const size_t need = split_bytes(units, nseg, dk, dv);
   if (!workspace || workspace_bytes < need)

@@ -141,6 +141,10 @@ def test_workspace_size_only_for_few_long_fixed_length_sequences(lib):
     assert lib.gla_chunk_fwd_workspace_size(16, 1, 16, 33000, 128, 256, 64, 0) == 0
     assert lib.gla_chunk_fwd_workspace_size(0, 1, 16, 65536, 64, 64, 64, 1) == 0
     assert lib.gla_chunk_fwd_workspace_size(0, 1, 16, 600, 128, 128, 64, 0) == 0   # too short
+    # 16 units of d_v 128 take the 128-column slice when split: 16 segments fill 256 CUs
+    # (the CPU build reads no device and plans for 256), fp32 states plus decays per segment
+    assert lib.gla_chunk_fwd_workspace_size(0, 1, 16, 65536, 128, 128, 64, 0) == \
+        16 * 16 * (128 * 128 + 128) * 4
 
 
 @pytest.mark.parametrize("ws,nbytes,needle", [

@@ -421,6 +421,7 @@ SPLIT_CASES = [
     ("strong_dv256_T3000", 1, 2, 3000, 128, 256, "strong", True),
     ("dk64_T2500", 2, 1, 2500, 64, 64, "weak", True),
     ("ragged_T1025", 1, 1, 1025, 128, 128, "weak", False),
+    ("dk64_dv128_strong_T2100", 1, 2, 2100, 64, 128, "strong", True),
 ]
 
 
