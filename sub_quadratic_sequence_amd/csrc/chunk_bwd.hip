@@ -8,15 +8,15 @@
 // recomputed in the backward call instead of being kept from the forward.
 //
 // Kernels of one call:
-//  * chunk_states_kernel<DK, false>: one pass over each sequence that writes the
-//    state at the start of every 64-token chunk (bf16, [dk][dv]) into the
-//    workspace.  Its key operand k 2^(Gamma_last - Gamma) never exceeds |k|, so
-//    it needs no pivoting and is exact for any gates.
+//  * the forward's pipelined kernel in its chunk-state mode (chunk_fwd_pipe.hip):
+//    one pass over each sequence that writes the state at the start of every
+//    64-token chunk (bf16, one dk x dv slot per chunk, element order
+//    chunk_state_index) into the workspace.
 //  * when the sequences are split into segments (few units, long sequences):
-//    chunk_states_kernel<DK, true>, the same pass run backwards over each
-//    segment but one on q 2^Gamma and dO, gives the state gradient a segment
-//    sends to its start from its own outputs (and its total decay); the
-//    reverse segment scan turns those into each segment's incoming gradient.
+//    seg_bstates_kernel, a pass run backwards over each segment but one on
+//    q 2^Gamma and dO, gives the state gradient a segment sends to its start
+//    from its own outputs (and its total decay); the reverse segment scan turns
+//    those into each segment's incoming gradient.
 //  * chunk_bwd_kernel: one workgroup (8 waves) per (sequence, head) walks the
 //    chunks from last to first.  Per chunk, with 16-token sub-chunks s:
 //      - a forward sweep s = 0..3 carries the state H (fp32 MFMA accumulators,
@@ -200,19 +200,17 @@ __device__ __forceinline__ Seq seq_of(const BwdParams& prm, int n, int h) {
 }  // namespace bwd
 
 // ============================================================================
-// Chunk-start states (REV = false) and segment state gradients (REV = true).
-// One workgroup (4 waves) per (sequence, head, 64-column slice), or per
-// (sequence, head, segment > 0, slice).  Wave w owns state columns
-// [16w, 16w+16) of the slice for all d_k rows as transposed tiles (MFMA
-// accumulators: lane holds 4 columns x 1 channel).
-//  * REV = false, forward over the chunks: store S (bf16), then
-//    S <- diag(2^Gamma_last) S + (k 2^(Gamma_last - Gamma))^T v.
-//  * REV = true, backward over the segment's chunks from B = 0:
-//    B <- diag(2^Gamma_last) B + (q 2^Gamma)^T dO; the result and the
-//    segment's decay exp(sum of its log-gates) go to the split workspace.
+// Segment state gradients of the sequence split.  One workgroup (4 waves) per
+// (sequence, head, segment > 0, 64-column slice) walks the segment's chunks
+// backwards from B = 0: B <- diag(2^Gamma_last) B + (q 2^Gamma)^T dO.  The
+// result and the segment's decay exp(sum of its log-gates) go to the split
+// workspace.  Wave w owns state columns [16w, 16w+16) of the slice for all d_k
+// rows as transposed tiles (MFMA accumulators: lane holds 4 columns x 1 channel).
+// (The chunk-start states come from the forward's pipelined kernel in its
+// chunk-state mode.)
 // ============================================================================
-template <int DK, bool REV>
-__global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
+template <int DK>
+__global__ __launch_bounds__(256, 2) void seg_bstates_kernel(BwdParams prm) {
   using namespace bwd;
   constexpr int NCG = DK / 8;      // 8-channel groups
   constexpr int NGL = 16 * NCG;    // gating lanes
@@ -228,7 +226,7 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
   const int lin = prm.xcd_remap ? (bid & 7) * (nblk >> 3) + (bid >> 3) : bid;
   const int item = lin / prm.nvt, vt = lin - item * prm.nvt;
   int unit = item, seg = 0;
-  if constexpr (REV) {   // item = (unit, segment 1 .. nseg-1)
+  {   // item = (unit, segment 1 .. nseg-1)
     unit = item / (prm.nseg - 1);
     seg = 1 + item - unit * (prm.nseg - 1);
   }
@@ -237,14 +235,13 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
   const Seq sq = seq_of(prm, n, h);
   const int nch = (int)((sq.len + C - 1) / C);
   // chunks [u_lo, u_hi) of this work item
-  const int u_lo = REV ? seg * (prm.seg_len / C) : 0;
-  const int u_hi = REV ? min(nch, (seg + 1) * (prm.seg_len / C)) : nch;
-  unsigned short* const hs = prm.hs + sq.slot0 * DK * DV;
+  const int u_lo = seg * (prm.seg_len / C);
+  const int u_hi = min(nch, (seg + 1) * (prm.seg_len / C));
 
-  // REV: q and dO stand where k and v are
-  const __amdgpu_buffer_rsrc_t rs_k = seq_rsrc(REV ? prm.q : prm.k, sq.r0 * DK, (int)(sq.len * DK * 2));
+  // q and dO take the places of k and v in the state recurrence
+  const __amdgpu_buffer_rsrc_t rs_k = seq_rsrc(prm.q, sq.r0 * DK, (int)(sq.len * DK * 2));
   const __amdgpu_buffer_rsrc_t rs_g = seq_rsrc(prm.g, sq.r0 * DK, (int)(sq.len * DK * 2));
-  const __amdgpu_buffer_rsrc_t rs_v = seq_rsrc(REV ? prm.dout : prm.v, sq.r0 * DV, (int)(sq.len * DV * 2));
+  const __amdgpu_buffer_rsrc_t rs_v = seq_rsrc(prm.dout, sq.r0 * DV, (int)(sq.len * DV * 2));
 
   // gating lane: tokens 4tg..4tg+3 x channels 8cg..8cg+7
   const bool gl = tid < NGL;
@@ -269,18 +266,10 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
   // state tiles: (nb = wave, cb = i)
   f32x4 Ht[CB];
   const int nb = wave;
-  float dsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // REV: the segment's log2 decay
+  float dsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // the segment's log2 decay
 #pragma unroll
-  for (int i = 0; i < CB; ++i) {
-    if (!REV && prm.s0) {
-      const float4 x = *reinterpret_cast<const float4*>(
-          prm.s0 + ((long)unit * DK + 16 * i + m) * DV + vcol0 + 16 * nb + 4 * grp);
-      Ht[i] = f32x4{x.x, x.y, x.z, x.w};
-    } else {
-      Ht[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-  if (u_hi > u_lo) prefetch(REV ? u_hi - 1 : u_lo);
+  for (int i = 0; i < CB; ++i) Ht[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (u_hi > u_lo) prefetch(u_hi - 1);
 
   // stage chunk u (its raw inputs are in registers) into buffer b
   auto stage = [&](int b) __attribute__((always_inline)) {
@@ -312,10 +301,8 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
         for (int a = 0; a < 4; ++a) pp[a][i] += ex;   // Gamma of token 4tg + a
         last[i] = __shfl(x, lane | 15);                // Gamma of the chunk's last row
       }
-      if constexpr (REV) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dsum[i] += last[i];
-      }
+      for (int i = 0; i < 8; ++i) dsum[i] += last[i];
       const unsigned* kw[4] = {&rk[0].x, &rk[1].x, &rk[2].x, &rk[3].x};
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
@@ -323,7 +310,7 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const unsigned w = kw[a][i >> 1];
-          kbv[i] = ((i & 1) ? hi_bf16(w) : lo_bf16(w)) * fast_exp2(REV ? pp[a][i] : last[i] - pp[a][i]);
+          kbv[i] = ((i & 1) ? hi_bf16(w) : lo_bf16(w)) * fast_exp2(pp[a][i]);
         }
         *reinterpret_cast<uint4*>(kb + ((toff(4 * tg, cg, 0) ^ cx(a, 0)) + ca(a, 0))) =
             uint4{pack_bf16x2(kbv[0], kbv[1]), pack_bf16x2(kbv[2], kbv[3]), pack_bf16x2(kbv[4], kbv[5]),
@@ -344,28 +331,24 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
   const int nit = u_hi - u_lo;
   if (nit > 0) {
     stage(0);
-    if (nit > 1) prefetch(REV ? u_hi - 2 : u_lo + 1);
+    if (nit > 1) prefetch(u_hi - 2);
     barrier_lds();
   }
   for (int it_u = 0; it_u < nit; ++it_u) {
-    const int u = REV ? u_hi - 1 - it_u : u_lo + it_u;
+    const int u = u_hi - 1 - it_u;
     const int b = it_u & 1;
     // chunk u+1 (in processing order) is staged into the other buffer while
     // chunk u's products run
     if (it_u + 1 < nit) {
       stage(b ^ 1);
-      if (it_u + 2 < nit) prefetch(REV ? u - 2 : u + 2);
+      if (it_u + 2 < nit) prefetch(u - 2);
     }
-    // H_u (the state entering chunk u) to the workspace, then the update
+    // B <- diag(2^Gamma_last) B + (q 2^Gamma)^T dO
     const char* const kb = kbs[b];
     const char* const vs = vss[b];
     const float* const dec = decs[b];
-    unsigned short* const hu = hs + (long)u * DK * DV;
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
-      if constexpr (!REV)
-        *reinterpret_cast<uint2*>(hu + (16 * i + m) * DV + vcol0 + 16 * nb + 4 * grp) =
-            pack4(Ht[i][0], Ht[i][1], Ht[i][2], Ht[i][3]);
       const float d = dec[16 * i + m];
       Ht[i] = Ht[i] * d;
     }
@@ -380,7 +363,7 @@ __global__ __launch_bounds__(256, 2) void chunk_states_kernel(BwdParams prm) {
     }
     barrier_lds();
   }
-  if constexpr (REV) {
+  {
     const long it = (long)unit * prm.nseg + seg;
     float* const bz = prm.seg_state + it * DK * DV;
 #pragma unroll
@@ -520,10 +503,11 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
   };
   auto prefetch_state = [&](int u) __attribute__((always_inline)) {
     const int tl = fresh_tid();
-    const unsigned h_lane = (unsigned)((c0 + (tl & 15)) * DV + 4 * ((tl >> 4) & 3)) * 2u;
+    // channel c0 + m, columns 16 b + 4 grp .. + 3: 8 contiguous bytes of the slot
+    const unsigned h_lane = 2u * (unsigned)chunk_state_index(c0 + (tl & 15), 4 * ((tl >> 4) & 3), DK);
     if (sw) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) rh[b] = ld8s(rs_h, h_lane + 32u * b, (unsigned)u * DK * DV * 2u);
+      for (int b = 0; b < NB; ++b) rh[b] = ld8s(rs_h, h_lane + 32u * DK * b, (unsigned)u * DK * DV * 2u);
     }
   };
 
@@ -824,21 +808,11 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
   }
 }
 
-int launch_chunk_states(const BwdParams& prm, int dk, int nblocks, hipStream_t stream) {
-  if (dk == 128)
-    hipLaunchKernelGGL((chunk_states_kernel<128, false>), dim3(nblocks), dim3(256), 0, stream, prm);
-  else if (dk == 64)
-    hipLaunchKernelGGL((chunk_states_kernel<64, false>), dim3(nblocks), dim3(256), 0, stream, prm);
-  else
-    return -2;
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
 int launch_chunk_bstates(const BwdParams& prm, int dk, int nblocks, hipStream_t stream) {
   if (dk == 128)
-    hipLaunchKernelGGL((chunk_states_kernel<128, true>), dim3(nblocks), dim3(256), 0, stream, prm);
+    hipLaunchKernelGGL((seg_bstates_kernel<128>), dim3(nblocks), dim3(256), 0, stream, prm);
   else if (dk == 64)
-    hipLaunchKernelGGL((chunk_states_kernel<64, true>), dim3(nblocks), dim3(256), 0, stream, prm);
+    hipLaunchKernelGGL((seg_bstates_kernel<64>), dim3(nblocks), dim3(256), 0, stream, prm);
   else
     return -2;
   return hipGetLastError() == hipSuccess ? 0 : -1;

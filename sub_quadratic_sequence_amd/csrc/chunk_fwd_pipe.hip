@@ -133,12 +133,16 @@ __device__ __forceinline__ int srow(int rb, int m) {
 }  // namespace pipe
 
 // MODE kFull: the forward pass (outputs, and the final state of unsplit sequences).
+// MODE kChunkStates: no outputs; the state entering every chunk, in bf16, to
+// prm.hs (the backward pass's recomputed states).
 // MODE kStateOnly: the state a segment reaches from S = 0 and the segment's total
 // gate decay, for the sequence split (no queries read, no outputs written).
 template <int DK, int MODE, int NT>
 __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm) {
   using namespace pipe;
   constexpr bool FULL = MODE == kFull;
+  constexpr bool STATES = MODE == kChunkStates;
+  static_assert(!STATES || NT == 1, "chunk states come from 64-column slices");
   using BufT = Buf<DK, NT>;
   constexpr int DVT = BufT::DVT;
   constexpr int PQ = BufT::PQ;
@@ -207,7 +211,10 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
   // state in and out of this work item ([DK][DV] fp32, this slice's columns used)
   const float* s_in;
   float* s_out;
-  if constexpr (!FULL) {
+  if constexpr (STATES) {
+    s_in = prm.s0 ? prm.s0 + (long)unit * DK * DV : nullptr;
+    s_out = nullptr;
+  } else if constexpr (!FULL) {
     s_in = nullptr;
     s_out = prm.seg_state + (long)item * DK * DV;
   } else if (prm.nseg > 1) {
@@ -593,7 +600,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       if (i < nch) produce(bufs[i & 1], i & 1, i + 1 < nch ? i + 1 : i);
       barrier_lds();
     }
-    if constexpr (!FULL) {
+    if constexpr (MODE == kStateOnly) {
       // the segment's decay exp(sum of g) per key channel, once per (unit, segment)
       if (vt == 0 && tg == 15) {
         float e[CPL];
@@ -627,6 +634,16 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     // 64 rows (8 KB) further on.
     constexpr unsigned kHalfX = (unsigned)tr_swz(64) << 4, kHalfOff = 64u * 128u;
     unsigned short* og = reinterpret_cast<unsigned short*>(prm.o) + rowbase * DV + vcol0;
+    // chunk-state mode: this unit's first slot, and the lane's element of a slot
+    // for tile 0, slot 0 (chunk_state_index with the tile and slot added per store)
+    unsigned short* hs_unit = nullptr;
+    int hs_lane = 0;
+    if constexpr (STATES) {
+      const long slot0 = prm.cu ? (long)h * prm.slots + n + bos / C
+                                : (long)h * prm.slots + n + (long)n * prm.T / C;
+      hs_unit = prm.hs + slot0 * DK * DV;
+      hs_lane = ((vt * 4 + cw) * NRB * 16 + gq) * 16 + m;
+    }
     f32x4 sacc[NT][NRB];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -785,6 +802,16 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         }
       }
 
+      if constexpr (STATES) {
+        // the state entering chunk u, bf16: for each (tile rb, slot s) the wave's
+        // 64 lanes write 128 contiguous bytes of the slot
+        unsigned short* const hu = hs_unit + (long)u * DK * DV;
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            hu[hs_lane + ((rb * 4 + s) << 6)] = f32_to_bf16_bits(sacc[0][rb][s]);
+      }
       // ---- state: S <- post * (pre * S + KT^T V) ----
       // every operand is read first (the output phase's registers are free by now),
       // so the 2 NRB products issue back to back
@@ -858,6 +885,17 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
           }
     }
   }
+}
+
+int launch_chunk_fwd_states(const ChunkParams& prm, int dk, int nblocks, hipStream_t stream) {
+  if (prm.dvt != 64 || prm.nvt * 64 != prm.DV || prm.nseg != 1 || prm.sort_units) return -2;
+  if (dk == 128)
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<128, kChunkStates, 1>), dim3(nblocks), dim3(512), 0, stream, prm);
+  else if (dk == 64)
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<64, kChunkStates, 1>), dim3(nblocks), dim3(512), 0, stream, prm);
+  else
+    return -2;
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_chunk_fwd_pipe(const ChunkParams& prm, int dk, bool state_only, int nblocks,

@@ -115,6 +115,8 @@ int check_chunk_args(const char* fn, const void* q, const void* k, const void* v
   prm.seg_decay = nullptr;
   prm.nseq = nseq;
   prm.sort_units = (cu_seqlens && dtype == GLA_BF16 && nseq <= gla::kMaxSortSeqs && units % 8 == 0) ? 1 : 0;
+  prm.hs = nullptr;
+  prm.slots = 0;
   return GLA_OK;
 }
 
@@ -384,8 +386,31 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
     prm.seg_decay = reinterpret_cast<float*>(sp + st_bytes);
   }
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  // 1. the state entering every chunk
-  int rc = gla::launch_chunk_states(prm, dk, (int)(units * nvt), s);
+  // 1. the state entering every chunk: the forward's pipelined kernel, states only
+  gla::ChunkParams fp;
+  fp.q = q;
+  fp.k = k;
+  fp.v = v;
+  fp.g = g;
+  fp.s0 = initial_state;
+  fp.o = nullptr;
+  fp.sT = nullptr;
+  fp.cu = cu_seqlens;
+  fp.H = H;
+  fp.T = T;
+  fp.DV = dv;
+  fp.dvt = 64;
+  fp.nvt = nvt;
+  fp.xcd_remap = ((units * nvt) % 8 == 0) ? 1 : 0;
+  fp.nseg = 1;
+  fp.seg_len = T;
+  fp.nseq = nseq;
+  fp.sort_units = 0;
+  fp.seg_state = nullptr;
+  fp.seg_decay = nullptr;
+  fp.hs = prm.hs;
+  fp.slots = prm.slots;
+  int rc = gla::launch_chunk_fwd_states(fp, dk, (int)(units * nvt), s);
   if (rc != 0) return launch_status(fn, rc, dk, dtype);
   if (nseg > 1) {
     // 2. each later segment's own state gradient and decay, 3. every segment's

@@ -37,6 +37,9 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
   bf16x2 r = __builtin_convertvector(v, bf16x2);
   return __builtin_bit_cast(unsigned, r);
 }
+__device__ __forceinline__ unsigned short f32_to_bf16_bits(float x) {
+  return (unsigned short)(pack_bf16x2(x, 0.f) & 0xffffu);
+}
 
 // Load N consecutive elements (N*bytes is 8, 16 or 32) as floats.
 template <typename E, int N>

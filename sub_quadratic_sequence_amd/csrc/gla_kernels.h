@@ -32,6 +32,10 @@ struct ChunkParams {
   int sort_units;
   float* seg_state;  // [units][nseg][dk][dv] fp32: a segment's state from zero, then its incoming state
   float* seg_decay;  // [units][nseg][dk] fp32: exp of the segment's summed log-gates
+  // Chunk-state mode (the backward's recomputation): the state entering every
+  // chunk, bf16, one dk x dv slot per chunk in the order of chunk_state_index.
+  unsigned short* hs;
+  int slots;         // slots per head: sequences + tokens / 64 + 1
 };
 
 constexpr int kMaxSortSeqs = 64;
@@ -39,6 +43,17 @@ constexpr int kMaxSortSeqs = 64;
 // Kernel modes of the pipelined forward.
 constexpr int kFull = 0;       // outputs (and the final state of unsplit sequences)
 constexpr int kStateOnly = 1;  // a segment's state from zero and its total decay
+constexpr int kChunkStates = 2;  // the state entering every chunk, to ChunkParams::hs
+
+// Element (row c, column n) of a chunk-state slot (dk x dv, bf16).  The order
+// follows the forward consumer's accumulators (column slice n / 64, its 16-column
+// tile, the 16-row state tile and accumulator slot of row c, then 16 columns),
+// so the forward stores 128 contiguous bytes per instruction and a backward lane
+// reads 4 consecutive columns of one row as 8 contiguous bytes.
+__host__ __device__ constexpr int chunk_state_index(int c, int n, int dk) {
+  return (((((n >> 4) * (dk / 16) + 2 * (c >> 5) + ((c >> 2) & 1)) * 4 + (c & 3)) * 4 + ((c >> 3) & 3)) << 4) +
+         (n & 15);
+}
 
 // Arguments of the segment scan of the sequence split.
 struct SegScanParams {
@@ -115,8 +130,8 @@ struct GdnParams {
 int launch_chunk_fwd(const ChunkParams& prm, int dk, int dtype, int nblocks, hipStream_t stream);
 int launch_chunk_fwd_pipe(const ChunkParams& prm, int dk, bool state_only, int nblocks,
                           hipStream_t stream);
+int launch_chunk_fwd_states(const ChunkParams& prm, int dk, int nblocks, hipStream_t stream);
 int launch_seg_scan(const SegScanParams& prm, int units, hipStream_t stream);
-int launch_chunk_states(const BwdParams& prm, int dk, int nblocks, hipStream_t stream);
 int launch_chunk_bstates(const BwdParams& prm, int dk, int nblocks, hipStream_t stream);
 int launch_chunk_bwd(const BwdParams& prm, int dk, int dv, int nblocks, hipStream_t stream);
 int launch_gdn_chunk_fwd(const GdnParams& prm, int dk, int nblocks, hipStream_t stream);
