@@ -32,6 +32,8 @@
 //    are the carried states scaled by factors <= 1, and
 //      H <- 2^(Gamma_{s,last} - b_s) (H^ + k~^T V),
 //      B <- 2^(b_s - Gamma_{s-1,last}) (B^ + q~^T dO).
+//    Between two sub-chunks the two factors combine into one, 2^(b_s - b_{s-1}),
+//    so the carried states are scaled once per step.
 //    The gate gradient is the reverse cumulative sum of q*dq - k*dk inside the
 //    chunk, started from sum_n H[c][n] B[c][n] at the chunk's end (the gradient
 //    of a log-gate is the state times its gradient summed over columns), so
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
     char dl[C * RD];               // Delta = Gamma - b_s (log2), fp32 [token][channel], swizzled units
     unsigned short as[NS][L * LP]; // A = dO V^T of sub-chunk s, [i][j], j <= i
     unsigned short ps[NS][L * LP]; // P = q~ k~^T of sub-chunk s, [i][j], j <= i
-    float fac[2][NS][DK];          // 0: 2^(b_s - Gamma_{s-1,last}), 1: 2^(Gamma_{s,last} - b_s)
+    float fac[NS + 1][DK];         // state factors: 2^b_0, 2^(b_s - b_{s-1}) (s = 1..3), 2^(Gamma_last - b_3)
   };
   __shared__ __attribute__((aligned(256))) Smem sm;
   char* const lds = reinterpret_cast<char*>(&sm);
@@ -564,16 +566,17 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
       const int s = tg >> 2;   // this lane's sub-chunk
       const unsigned* qw[4] = {&pf[0].x, &pf[1].x, &pf[2].x, &pf[3].x};
       const unsigned* kw[4] = {&pf[4].x, &pf[5].x, &pf[6].x, &pf[7].x};
+      // The carried states move between sub-chunks by one factor each:
+      // 2^(Gamma_{s-1,last} - b_{s-1}) 2^(b_s - Gamma_{s-1,last}) = 2^(b_s - b_{s-1}).
       float piv[8], f0[8], f1[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float first = quad_bcast_c<0>(gm[0][i]);   // Gamma at the sub-chunk's first row
         const float last = quad_bcast_c<3>(gm[3][i]);    // ... and at its last row
-        const float prev = dpp<kRowShr4>(last);          // last row of the previous sub-chunk (0 for s = 0)
         float b = 0.5f * (first + last);
         if (!(first - last <= kRangeLimit)) b = __int_as_float(0x7fc00000);
         piv[i] = b;
-        f0[i] = fast_exp2(b - prev);
+        f0[i] = fast_exp2(b - dpp<kRowShr4>(b));          // previous sub-chunk's pivot (0 for s = 0)
         f1[i] = fast_exp2(last - b);
       }
 #pragma unroll
@@ -602,10 +605,12 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
             make_float4(dv8[4], dv8[5], dv8[6], dv8[7]);
       }
       if ((tg & 3) == 0) {
-        *reinterpret_cast<float4*>(&sm.fac[0][s][8 * cg]) = make_float4(f0[0], f0[1], f0[2], f0[3]);
-        *reinterpret_cast<float4*>(&sm.fac[0][s][8 * cg + 4]) = make_float4(f0[4], f0[5], f0[6], f0[7]);
-        *reinterpret_cast<float4*>(&sm.fac[1][s][8 * cg]) = make_float4(f1[0], f1[1], f1[2], f1[3]);
-        *reinterpret_cast<float4*>(&sm.fac[1][s][8 * cg + 4]) = make_float4(f1[4], f1[5], f1[6], f1[7]);
+        *reinterpret_cast<float4*>(&sm.fac[s][8 * cg]) = make_float4(f0[0], f0[1], f0[2], f0[3]);
+        *reinterpret_cast<float4*>(&sm.fac[s][8 * cg + 4]) = make_float4(f0[4], f0[5], f0[6], f0[7]);
+        if (s == NS - 1) {
+          *reinterpret_cast<float4*>(&sm.fac[NS][8 * cg]) = make_float4(f1[0], f1[1], f1[2], f1[3]);
+          *reinterpret_cast<float4*>(&sm.fac[NS][8 * cg + 4]) = make_float4(f1[4], f1[5], f1[6], f1[7]);
+        }
       }
     }
     if (cl) {
@@ -668,12 +673,13 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
     barrier_lds();
 
     // ======================= forward sweep: dq =======================
-    // the chunk-start state, widened only now: during the load phase its bf16
-    // form takes half the registers
+    // the chunk-start state, widened only now (during the load phase its bf16
+    // form takes half the registers) and scaled into H^ of sub-chunk 0
     if (sw) {
+      const float f = *reinterpret_cast<const float*>(lds + oF + fC);
 #pragma unroll
       for (int b = 0; b < NB; ++b)
-        Ht[b] = f32x4{lo_bf16(rh[b].x), hi_bf16(rh[b].x), lo_bf16(rh[b].y), hi_bf16(rh[b].y)};
+        Ht[b] = f32x4{lo_bf16(rh[b].x), hi_bf16(rh[b].x), lo_bf16(rh[b].y), hi_bf16(rh[b].y)} * f;
     }
     float qd[NS][4];   // q~ * (dq before its 2^Delta factor), for dg
 #pragma unroll
@@ -681,11 +687,7 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
       // the next chunk's inputs are requested half-way through this one: early
       // enough to arrive, late enough to keep the first half's registers free
       if (s == NS / 2 && u > u_lo) prefetch(u - 1);
-      if (sw) {
-        // H^ = 2^(b_s - Gamma_{s-1,last}) H
-        const float f = *reinterpret_cast<const float*>(lds + oF + s * DK * 4 + fC);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) Ht[b] = Ht[b] * f;
+      if (sw) {   // Ht holds H^ of sub-chunk s
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < DV / 32; ++kk)   // H^[c][n] dO[i][n]
@@ -706,13 +708,14 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
           *reinterpret_cast<uint2*>(dq_out + t * DK + c0 + 4 * grp) =
               pack4(fast_exp2(d.x) * acc[0], fast_exp2(d.y) * acc[1], fast_exp2(d.z) * acc[2],
                     fast_exp2(d.w) * acc[3]);
-        // H <- 2^(Gamma_{s,last} - b_s) (H^ + k~^T V) over the sub-chunk's tokens
+        // H^ + k~^T V over the sub-chunk's tokens, then the factor to H^ of
+        // sub-chunk s + 1 (after the last one: to H at the chunk's end)
 #pragma unroll
         for (int b = 0; b < NB; ++b)
           mma16(Ht[b], rdt(oV + at(tV, 16 * s, 2 * b)), kt);
-        const float f1 = *reinterpret_cast<const float*>(lds + oF + (NS + s) * DK * 4 + fC);
+        const float f = *reinterpret_cast<const float*>(lds + oF + (s + 1) * DK * 4 + fC);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) Ht[b] = Ht[b] * f1;
+        for (int b = 0; b < NB; ++b) Ht[b] = Ht[b] * f;
       }
     }
 
@@ -732,16 +735,17 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
     if (u > u_lo) prefetch_state(u - 1);
 
     // ======================= reverse sweep: dk, dv, dg =======================
+    if (sw) {   // B^ of sub-chunk 3 = 2^(Gamma_last - b_3) B
+      const float f = *reinterpret_cast<const float*>(lds + oF + NS * DK * 4 + fC);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) Bt[b] = Bt[b] * f;
+    }
 #pragma unroll
     for (int s = NS - 1; s >= 0; --s) {
-      if (sw) {
-        // B^ = 2^(Gamma_{s,last} - b_s) B, and its bf16 copy for dv
-        const float f = *reinterpret_cast<const float*>(lds + oF + (NS + s) * DK * 4 + fC);
+      if (sw) {   // Bt holds B^ of sub-chunk s; its bf16 copy for dv
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          Bt[b] = Bt[b] * f;
+        for (int b = 0; b < NB; ++b)
           *reinterpret_cast<uint2*>(lds + oS + at(wS, 0, 2 * b)) = pack4(Bt[b][0], Bt[b][1], Bt[b][2], Bt[b][3]);
-        }
       }
       barrier_lds();
       if (sw) {
@@ -776,13 +780,14 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
                     fast_exp2(-d.w) * acc[3]);
           *reinterpret_cast<uint2*>(dg_out + t * DK + c0 + 4 * grp) = pack4(dgv[0], dgv[1], dgv[2], dgv[3]);
         }
-        // B <- 2^(b_s - Gamma_{s-1,last}) (B^ + q~^T dO) over the sub-chunk's tokens
+        // B^ + q~^T dO over the sub-chunk's tokens, then the factor to B^ of
+        // sub-chunk s - 1 (after the first one: to B at the chunk's start)
 #pragma unroll
         for (int b = 0; b < NB; ++b)
           mma16(Bt[b], rdt(oO + at(tV, 16 * s, 2 * b)), qt);
-        const float f0 = *reinterpret_cast<const float*>(lds + oF + s * DK * 4 + fC);
+        const float f = *reinterpret_cast<const float*>(lds + oF + s * DK * 4 + fC);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) Bt[b] = Bt[b] * f0;
+        for (int b = 0; b < NB; ++b) Bt[b] = Bt[b] * f;
       }
       if (vw) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
