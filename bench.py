@@ -130,6 +130,24 @@ def time_launches(fn, steps, warmup, torch, preroll_s=0.0):
     return (t1 - t0) / steps, ev0.elapsed_time(ev1) / 1e3 / steps
 
 
+def per_launch(fn, n, torch, flush=None):
+    """Per-launch HIP-event times (s) of n calls of fn.  With `flush` (a device
+    buffer larger than the last-level cache), the buffer is overwritten before
+    each call, so every call starts with its inputs evicted from that cache."""
+    evs = []
+    for i in range(n):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) / 1e3 for a, b in evs)
+
+
 def bench_forward(args, torch, gla, inputs):
     w = inputs.TRAIN_BF16
     log(f"[bench] forward {w.name}: generating inputs")
@@ -145,7 +163,16 @@ def bench_forward(args, torch, gla, inputs):
     log(f"[bench] forward: {args.preroll:.1f} s pre-roll, {args.warmup} warmup + {args.steps} timed steps")
     wall, gpu = time_launches(step, args.steps, args.warmup, torch, args.preroll)
     flops, nbytes = fwd_work(w.B, w.H, w.T, w.dk, w.dv, 64, 2)
-    return dict(w=w, d=d, wall=wall, gpu=gpu, flops=flops, bytes=nbytes, tokens=w.B * w.T)
+    # launch-time distribution, warm and with the 256 MB last-level cache evicted
+    # by a 1 GiB fill before each launch (outside the timed steps above)
+    warm = cold = [gpu]
+    if args.only != "pmc":   # counter runs keep to the timed launches
+        warm = per_launch(step, 50, torch)
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cold = per_launch(step, 20, torch, flush)
+        del flush
+    return dict(w=w, d=d, wall=wall, gpu=gpu, flops=flops, bytes=nbytes, tokens=w.B * w.T,
+                warm=warm, cold=cold)
 
 
 def bench_decode(args, torch, gla, inputs):
@@ -407,7 +434,8 @@ def main():
     tflops = fwd["flops"] / t / 1e12
     gbs = fwd["bytes"] / t / 1e9
     log(f"[bench] forward: {t * 1e6:.1f} us/launch (events), {fwd['wall'] * 1e6:.1f} us/step (wall), "
-        f"{tflops:.1f} TFLOP/s, {gbs:.0f} GB/s")
+        f"{tflops:.1f} TFLOP/s, {gbs:.0f} GB/s; per launch median {fwd['warm'][len(fwd['warm']) // 2] * 1e6:.1f} us "
+        f"warm, {fwd['cold'][len(fwd['cold']) // 2] * 1e6:.1f} us with the last-level cache evicted")
     if args.only == "fwd":
         return
     traffic = read_traffic("chunk_fwd_b8h16t2048d128_bf16_traffic.txt", KERNEL_SRC)
@@ -435,6 +463,12 @@ def main():
                      "algorithmic_bytes_per_launch": fwd["bytes"],
                      "algorithmic_flops_per_launch": fwd["flops"],
                      "avg_launch_us": t * 1e6},
+        "launch_us": {
+            "warm_median": fwd["warm"][len(fwd["warm"]) // 2] * 1e6, "warm_min": fwd["warm"][0] * 1e6,
+            "cold_llc_median": fwd["cold"][len(fwd["cold"]) // 2] * 1e6,
+            "cold_llc_min": fwd["cold"][0] * 1e6,
+            "cold_llc_frac_of_hbm": fwd["bytes"] / fwd["cold"][len(fwd["cold"]) // 2] / 1e9 / HBM_PEAK_GBS,
+            "note": "per-launch HIP events, 50 warm launches; 20 launches each after a 1 GiB fill"},
     }
     if not args.no_decode:
         dec = bench_decode(args, torch, gla, inputs)
