@@ -684,9 +684,11 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
     float qd[NS][4];   // q~ * (dq before its 2^Delta factor), for dg
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      // the next chunk's inputs are requested half-way through this one: early
-      // enough to arrive, late enough to keep the first half's registers free
-      if (s == NS / 2 && u > u_lo) prefetch(u - 1);
+      // the next chunk's inputs are requested at the second sub-chunk: early enough
+      // to arrive, and before most of this sweep's dq stores.  (Loads and stores
+      // share vmcnt and may complete out of order, so a load whose registers
+      // earlier stores read waits for every outstanding store.)
+      if (s == 1 && u > u_lo) prefetch(u - 1);
       if (sw) {   // Ht holds H^ of sub-chunk s
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
