@@ -99,7 +99,8 @@ size_t gla_chunk_fwd_workspace_size(int num_seqs, int B, int H, int T, int dk, i
  * gla_chunk_fwd with a sequence split for inputs whose (sequence, head, 64-column
  * slice) work items do not fill the device: each sequence is cut into segments
  * of whole 64-token chunks, at least 512 tokens long, so that there are about
- * as many work items as compute units.  The recurrence is linear in the state
+ * as many work items as compute units (bf16 work items of a split cover 128
+ * columns of d_v when d_v is a multiple of 128, else 64).  The recurrence is linear in the state
  * with a diagonal transition, so over one segment S_end = diag(a) S_start +
  * S_zero, with a = exp(sum of the segment's g) and S_zero the state reached
  * from zero (page "Gated Linear Attention (GLA) ...", section "The Gated
