@@ -13,10 +13,10 @@
 //    64-token chunk (bf16, one dk x dv slot per chunk, element order
 //    chunk_state_index) into the workspace.
 //  * when the sequences are split into segments (few units, long sequences):
-//    seg_bstates_kernel, a pass run backwards over each segment but one on
-//    q 2^Gamma and dO, gives the state gradient a segment sends to its start
-//    from its own outputs (and its total decay); the reverse segment scan turns
-//    those into each segment's incoming gradient.
+//    the same pipelined kernel in its segment-gradient mode, run backwards over
+//    each segment but one on q 2^Gamma and dO, gives the state gradient a
+//    segment sends to its start from its own outputs (and its total decay); the
+//    reverse segment scan turns those into each segment's incoming gradient.
 //  * chunk_bwd_kernel: one workgroup (8 waves) per (sequence, head) walks the
 //    chunks from last to first.  Per chunk, with 16-token sub-chunks s:
 //      - a forward sweep s = 0..3 carries the state H (fp32 MFMA accumulators,
@@ -71,9 +71,10 @@ __device__ __forceinline__ void barrier_lds() {
 // 64 banks, 16-byte reads in passes that pair lane quads of equal parity of
 // lane bits 2-4, and 8- and 16-byte writes 16 and 8 consecutive lanes per pass
 // over 32 banks (all measured with rocprofv3's SQ_LDS_BANK_CONFLICT).  With
-// this swz every access shape of the kernels below is free of bank conflicts:
+// this swz every access shape of the kernel below is free of bank conflicts:
 // 8- and 16-byte fragment reads on 16 consecutive rows, transposing reads on
-// 8 rows (4 consecutive rows per 16 lanes, also 8-row strided pairs), the
+// 8 rows (4 consecutive rows per 16 lanes, also 8-row strided pairs of the
+// state tile), the
 // gating writes to rows 4t + a (t = 0..7) and the row-wise copies.  The one
 // exception is the state tile's 8-byte writes, 2-way by their lane shape.
 // swz is linear over the row bits: for row and unit parts with disjoint bits an
@@ -102,35 +103,13 @@ __host__ __device__ constexpr unsigned ca(unsigned cr, unsigned cu, unsigned RB 
 //    transposing read: in each 16-lane group, lane i reads 4 consecutive m of
 //    row k0 + 4 grp + i / 4 at m0 + 4 (i % 4) and receives element m0 + i of
 //    rows k0 + 4 grp + 0..3.
-__device__ __forceinline__ s16x4 row16(const unsigned short* base, int pitch, int m0, int k0, int m, int grp) {
-  return *reinterpret_cast<const s16x4*>(base + (m0 + m) * pitch + k0 + 4 * grp);
-}
-__device__ __forceinline__ s16x8 row32(const unsigned short* base, int pitch, int m0, int k0, int m, int grp) {
-  return *reinterpret_cast<const s16x8*>(base + (m0 + m) * pitch + k0 + 8 * grp);
-}
 __device__ __forceinline__ s16x4 tr_read(const unsigned short* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-}
-__device__ __forceinline__ s16x4 tr16(const unsigned short* base, int pitch, int k0, int m0, int m, int grp) {
-  return tr_read(base + (k0 + 4 * grp + (m >> 2)) * pitch + m0 + 4 * (m & 3));
-}
-__device__ __forceinline__ s16x8 tr32(const unsigned short* base, int pitch, int k0, int m0, int m, int grp) {
-  const s16x4 lo = tr_read(base + (k0 + 8 * grp + (m >> 2)) * pitch + m0 + 4 * (m & 3));
-  const s16x4 hi = tr_read(base + (k0 + 8 * grp + 4 + (m >> 2)) * pitch + m0 + 4 * (m & 3));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 // 16-deep contraction: the 16x16x32 instruction with the second half of both
 // operands zero (slots 4-7 pair with slots 4-7, so they add exactly 0).  The
 // legacy 16x16x16 bf16 instruction is not used: its results were read back too
 // early by the generated code on gfx950 (wrong values, no fault).
-// The same from a swizzled tile: lane part ln, compile-time row r0 and unit u0;
-// the second half reads 4 rows further on.
-__device__ __forceinline__ s16x4 trs(const char* tile, unsigned ln, unsigned r0, unsigned u0) {
-  return tr_read(reinterpret_cast<const unsigned short*>(tile + ((ln ^ cx(r0, u0)) + ca(r0, u0))));
-}
-__device__ __forceinline__ s16x8 tr32s(const char* tile, unsigned ln, unsigned r0, unsigned u0) {
-  return __builtin_shufflevector(trs(tile, ln, r0, u0), trs(tile, ln, r0 + 4, u0), 0, 1, 2, 3, 4, 5, 6, 7);
-}
 __device__ __forceinline__ void mma16(f32x4& acc, s16x4 a, s16x4 b) {
   const s16x4 z = {0, 0, 0, 0};
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -154,10 +133,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const void* base, lon
   return __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(static_cast<const void*>(static_cast<const unsigned short*>(base) + first_elem)),
       (short)0, bytes, kBufferFlags);
-}
-__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t rs, unsigned off) {
-  const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
-  return uint4{x[0], x[1], x[2], x[3]};
 }
 // per-lane byte offset plus a wave-uniform one (kept in a scalar register)
 __device__ __forceinline__ uint4 ld16s(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned soff) {
@@ -200,187 +175,6 @@ __device__ __forceinline__ Seq seq_of(const BwdParams& prm, int n, int h) {
 }
 
 }  // namespace bwd
-
-// ============================================================================
-// Segment state gradients of the sequence split.  One workgroup (4 waves) per
-// (sequence, head, segment > 0, 64-column slice) walks the segment's chunks
-// backwards from B = 0: B <- diag(2^Gamma_last) B + (q 2^Gamma)^T dO.  The
-// result and the segment's decay exp(sum of its log-gates) go to the split
-// workspace.  Wave w owns state columns [16w, 16w+16) of the slice for all d_k
-// rows as transposed tiles (MFMA accumulators: lane holds 4 columns x 1 channel).
-// (The chunk-start states come from the forward's pipelined kernel in its
-// chunk-state mode.)
-// ============================================================================
-template <int DK>
-__global__ __launch_bounds__(256, 2) void seg_bstates_kernel(BwdParams prm) {
-  using namespace bwd;
-  constexpr int NCG = DK / 8;      // 8-channel groups
-  constexpr int NGL = 16 * NCG;    // gating lanes
-  constexpr int CB = DK / 16;      // 16-channel blocks
-  // two buffers: the gating of chunk u+1 overlaps the products of chunk u;
-  // k-bar [token][channel] and v [token][column] tiles, swizzled 256-byte rows
-  __shared__ __attribute__((aligned(256))) char kbs[2][C * 256];
-  __shared__ __attribute__((aligned(256))) char vss[2][C * 256];
-  __shared__ float decs[2][DK];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, m = lane & 15, grp = lane >> 4;
-  const int bid = blockIdx.x, nblk = gridDim.x;
-  const int lin = prm.xcd_remap ? (bid & 7) * (nblk >> 3) + (bid >> 3) : bid;
-  const int item = lin / prm.nvt, vt = lin - item * prm.nvt;
-  int unit = item, seg = 0;
-  {   // item = (unit, segment 1 .. nseg-1)
-    unit = item / (prm.nseg - 1);
-    seg = 1 + item - unit * (prm.nseg - 1);
-  }
-  const int n = unit / prm.H, h = unit - n * prm.H;
-  const int DV = prm.DV, vcol0 = vt * 64;
-  const Seq sq = seq_of(prm, n, h);
-  const int nch = (int)((sq.len + C - 1) / C);
-  // chunks [u_lo, u_hi) of this work item
-  const int u_lo = seg * (prm.seg_len / C);
-  const int u_hi = min(nch, (seg + 1) * (prm.seg_len / C));
-
-  // q and dO take the places of k and v in the state recurrence
-  const __amdgpu_buffer_rsrc_t rs_k = seq_rsrc(prm.q, sq.r0 * DK, (int)(sq.len * DK * 2));
-  const __amdgpu_buffer_rsrc_t rs_g = seq_rsrc(prm.g, sq.r0 * DK, (int)(sq.len * DK * 2));
-  const __amdgpu_buffer_rsrc_t rs_v = seq_rsrc(prm.dout, sq.r0 * DV, (int)(sq.len * DV * 2));
-
-  // gating lane: tokens 4tg..4tg+3 x channels 8cg..8cg+7
-  const bool gl = tid < NGL;
-  const int tg = m, cg = tid >> 4;
-  const unsigned qk_lane = (unsigned)((4 * tg) * DK + 8 * cg) * 2u;
-  uint4 rk[4], rg[4], rv[2];
-  auto prefetch = [&](int u) __attribute__((always_inline)) {
-    if (gl) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        rk[a] = ld16(rs_k, qk_lane + (unsigned)(u * C + a) * DK * 2u);
-        rg[a] = ld16(rs_g, qk_lane + (unsigned)(u * C + a) * DK * 2u);
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int idx = tid + 256 * it, row = idx >> 3, un = idx & 7;
-      rv[it] = ld16(rs_v, (unsigned)((u * C + row) * DV + vcol0 + 8 * un) * 2u);
-    }
-  };
-
-  // state tiles: (nb = wave, cb = i)
-  f32x4 Ht[CB];
-  const int nb = wave;
-  float dsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // the segment's log2 decay
-#pragma unroll
-  for (int i = 0; i < CB; ++i) Ht[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (u_hi > u_lo) prefetch(u_hi - 1);
-
-  // stage chunk u (its raw inputs are in registers) into buffer b
-  auto stage = [&](int b) __attribute__((always_inline)) {
-    char* const kb = kbs[b];
-    char* const vs = vss[b];
-    float* const dec = decs[b];
-    if (gl) {
-      float pp[4][8];
-      const unsigned* gw[4] = {&rg[0].x, &rg[1].x, &rg[2].x, &rg[3].x};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const unsigned w = gw[a][i >> 1];
-          const float y = fmaxf(((i & 1) ? hi_bf16(w) : lo_bf16(w)) * kLog2e, -256.f);
-          pp[a][i] = a ? pp[a - 1][i] + y : y;
-        }
-      }
-      float last[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float x = pp[3][i];
-        x += dpp<kRowShr1>(x);
-        x += dpp<kRowShr2>(x);
-        x += dpp<kRowShr4>(x);
-        x += dpp<kRowShr8>(x);
-        const float ex = x - pp[3][i];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) pp[a][i] += ex;   // Gamma of token 4tg + a
-        last[i] = __shfl(x, lane | 15);                // Gamma of the chunk's last row
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dsum[i] += last[i];
-      const unsigned* kw[4] = {&rk[0].x, &rk[1].x, &rk[2].x, &rk[3].x};
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        float kbv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const unsigned w = kw[a][i >> 1];
-          kbv[i] = ((i & 1) ? hi_bf16(w) : lo_bf16(w)) * fast_exp2(pp[a][i]);
-        }
-        *reinterpret_cast<uint4*>(kb + ((toff(4 * tg, cg, 0) ^ cx(a, 0)) + ca(a, 0))) =
-            uint4{pack_bf16x2(kbv[0], kbv[1]), pack_bf16x2(kbv[2], kbv[3]), pack_bf16x2(kbv[4], kbv[5]),
-                  pack_bf16x2(kbv[6], kbv[7])};
-      }
-      if (tg == 15) {
-        *reinterpret_cast<float4*>(dec + 8 * cg) =
-            make_float4(fast_exp2(last[0]), fast_exp2(last[1]), fast_exp2(last[2]), fast_exp2(last[3]));
-        *reinterpret_cast<float4*>(dec + 8 * cg + 4) =
-            make_float4(fast_exp2(last[4]), fast_exp2(last[5]), fast_exp2(last[6]), fast_exp2(last[7]));
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it)   // row (tid >> 3) + 32 it, unit tid & 7
-      *reinterpret_cast<uint4*>(vs + ((toff(tid >> 3, tid & 7, 0) ^ cx(32 * it, 0)) + ca(32 * it, 0))) = rv[it];
-  };
-
-  const int nit = u_hi - u_lo;
-  if (nit > 0) {
-    stage(0);
-    if (nit > 1) prefetch(u_hi - 2);
-    barrier_lds();
-  }
-  for (int it_u = 0; it_u < nit; ++it_u) {
-    const int u = u_hi - 1 - it_u;
-    const int b = it_u & 1;
-    // chunk u+1 (in processing order) is staged into the other buffer while
-    // chunk u's products run
-    if (it_u + 1 < nit) {
-      stage(b ^ 1);
-      if (it_u + 2 < nit) prefetch(u - 2);
-    }
-    // B <- diag(2^Gamma_last) B + (q 2^Gamma)^T dO
-    const char* const kb = kbs[b];
-    const char* const vs = vss[b];
-    const float* const dec = decs[b];
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const float d = dec[16 * i + m];
-      Ht[i] = Ht[i] * d;
-    }
-    // transposing reads: rows 32 ks + 8 grp + (m >> 2) (+ 4), columns 16 j + 4 (m & 3)
-    const unsigned trl = toff(8 * grp + (m >> 2), (m & 3) >> 1, 8 * (m & 1));
-    const unsigned trv = toff(8 * grp + (m >> 2), 2 * nb + ((m & 3) >> 1), 8 * (m & 1));
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const s16x8 x = tr32s(vs, trv, 32 * ks, 0);
-#pragma unroll
-      for (int i = 0; i < CB; ++i) mma32(Ht[i], x, tr32s(kb, trl, 32 * ks, 2 * i));
-    }
-    barrier_lds();
-  }
-  {
-    const long it = (long)unit * prm.nseg + seg;
-    float* const bz = prm.seg_state + it * DK * DV;
-#pragma unroll
-    for (int i = 0; i < CB; ++i)
-      *reinterpret_cast<float4*>(bz + (16 * i + m) * DV + vcol0 + 16 * nb + 4 * grp) =
-          make_float4(Ht[i][0], Ht[i][1], Ht[i][2], Ht[i][3]);
-    if (gl && tg == 15 && vt == 0) {
-      float* const dz = prm.seg_decay + it * DK + 8 * cg;
-      *reinterpret_cast<float4*>(dz) =
-          make_float4(fast_exp2(dsum[0]), fast_exp2(dsum[1]), fast_exp2(dsum[2]), fast_exp2(dsum[3]));
-      *reinterpret_cast<float4*>(dz + 4) =
-          make_float4(fast_exp2(dsum[4]), fast_exp2(dsum[5]), fast_exp2(dsum[6]), fast_exp2(dsum[7]));
-    }
-  }
-}
 
 // ============================================================================
 // Backward main kernel: one workgroup (8 waves) per (sequence, head).
@@ -813,16 +607,6 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
       *reinterpret_cast<float4*>(prm.ds0 + ((long)unit * DK + c0 + m) * DV + 16 * b + 4 * grp) =
           make_float4(Bt[b][0], Bt[b][1], Bt[b][2], Bt[b][3]);
   }
-}
-
-int launch_chunk_bstates(const BwdParams& prm, int dk, int nblocks, hipStream_t stream) {
-  if (dk == 128)
-    hipLaunchKernelGGL((seg_bstates_kernel<128>), dim3(nblocks), dim3(256), 0, stream, prm);
-  else if (dk == 64)
-    hipLaunchKernelGGL((seg_bstates_kernel<64>), dim3(nblocks), dim3(256), 0, stream, prm);
-  else
-    return -2;
-  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_chunk_bwd(const BwdParams& prm, int dk, int dv, int nblocks, hipStream_t stream) {

@@ -135,6 +135,9 @@ __device__ __forceinline__ int srow(int rb, int m) {
 // MODE kFull: the forward pass (outputs, and the final state of unsplit sequences).
 // MODE kChunkStates: no outputs; the state entering every chunk, in bf16, to
 // prm.hs (the backward pass's recomputed states).
+// MODE kSegGrad: the state-gradient pass of the backward's sequence split (k and v
+// hold q and dO): chunks from last to first, B <- 2^Gamma_last B + (q 2^Gamma)^T dO
+// from B = 0 over segments 1 .. nseg-1, to seg_state, with the segment's decay.
 // MODE kStateOnly: the state a segment reaches from S = 0 and the segment's total
 // gate decay, for the sequence split (no queries read, no outputs written).
 template <int DK, int MODE, int NT>
@@ -142,7 +145,9 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
   using namespace pipe;
   constexpr bool FULL = MODE == kFull;
   constexpr bool STATES = MODE == kChunkStates;
+  constexpr bool REV = MODE == kSegGrad;
   static_assert(!STATES || NT == 1, "chunk states come from 64-column slices");
+  static_assert(!REV || NT == 1, "the gradient pass runs on 64-column slices");
   using BufT = Buf<DK, NT>;
   constexpr int DVT = BufT::DVT;
   constexpr int PQ = BufT::PQ;
@@ -189,8 +194,10 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     const int lin = prm.xcd_remap ? (bid & 7) * (nblk >> 3) + (bid >> 3) : bid;
     item = lin / prm.nvt;
     vt = lin - item * prm.nvt;
-    const int u0 = item / prm.nseg;
-    seg = item - u0 * prm.nseg;
+    const int nsg = REV ? prm.nseg - 1 : prm.nseg;   // the gradient pass skips segment 0
+    const int u0 = item / nsg;
+    seg = item - u0 * nsg + (REV ? 1 : 0);
+    item = u0 * prm.nseg + seg;
     n = u0 / prm.H;
     h = u0 - n * prm.H;
   }
@@ -359,230 +366,276 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       }
       __builtin_amdgcn_sched_barrier(0);
       load_v(un);
-      // log2 gates: pp = inclusive prefix over this lane's 4 tokens, inc =
-      // inclusive prefix over the chunk at this lane's last token (a 16-lane
-      // DPP scan of the lane totals).  Gates are <= 0, so |Gamma| is largest
-      // at the chunk's last row; the chunk is a fast one for this wave when
-      // every |Gamma| of its slice stays within 2^kFastLimit.  A -inf gate
-      // (alpha = 0) makes Gamma infinite and the chunk a safe one.
-      float pp[4][CPL], inc[CPL];
-      float mx = 0.f;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        pp[0][i] = el(rg[0], i) * kLog2e;
-#pragma unroll
-        for (int a = 1; a < 4; ++a) pp[a][i] = fmaf(el(rg[a], i), kLog2e, pp[a - 1][i]);
-        float x = pp[3][i];
-        x += dpp<kRowShr1>(x);
-        x += dpp<kRowShr2>(x);
-        x += dpp<kRowShr4>(x);
-        x += dpp<kRowShr8>(x);
-        inc[i] = x;
-        mx = fmaxf(mx, fabsf(x));
-      }
-      const bool fastw = __ballot(!(mx <= kFastLimit)) == 0ull;
-      if (!fastw) {
-        // the safe path works from gates floored at -256 (log2), so that an
-        // alpha = 0 gate cannot produce inf - inf (laundering keeps the
-        // compiler from speculating this rare work into the fast path)
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int j = 0; j < NWR; ++j) launder(rg[a][j]);
+      if constexpr (REV) {
+        // Gamma from gates floored at -256 (log2), so that an alpha = 0 gate
+        // cannot produce inf - inf; the state keys q 2^Gamma never exceed |q|,
+        // and B <- 2^Gamma_last B + KT^T dO (pre = 2^Gamma_last, post = 1)
+        float gf[4][CPL], tot[CPL];
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
 #pragma unroll
           for (int a = 0; a < 4; ++a) {
             const float y = fmaxf(el(rg[a], i) * kLog2e, -256.f);
-            pp[a][i] = a ? pp[a - 1][i] + y : y;
+            gf[a][i] = a ? gf[a - 1][i] + y : y;
           }
+          float x = gf[3][i];
+          x += dpp<kRowShr1>(x);
+          x += dpp<kRowShr2>(x);
+          x += dpp<kRowShr4>(x);
+          x += dpp<kRowShr8>(x);
+          const float ex = x - gf[3][i];
+#pragma unroll
+          for (int a = 0; a < 4; ++a) gf[a][i] += ex;   // Gamma of token 4tg + a
+          tot[i] = x;                                     // the chunk's total at tg == 15
         }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      load_g(un);
-      if (fastw) {
-        // ---- single pivot at the chunk start ----
-        float ex[CPL];   // Gamma before this lane's first token
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) ex[i] = inc[i] - pp[3][i];
-        unsigned kw[4][NWR];   // packed key operand words, token a
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          float qe[CPL], ke[CPL];
-#pragma unroll
-          for (int i = 0; i < CPL; ++i) {
-            const float gm = ex[i] + pp[a][i];   // Gamma of token 4tg+a
-            if constexpr (FULL) qe[i] = el(rq[a], i) * fast_exp2(gm);
-            ke[i] = el(rk[a], i) * fast_exp2(-gm);
-          }
-#pragma unroll
-          for (int j = 0; j < NWR; ++j) kw[a][j] = pack_bf16x2(ke[2 * j], ke[2 * j + 1]);
-          if constexpr (FULL) {
-            lds_store_n<BF16, CPL>(slot(kQ, a), qe);
-            st(slot(kK, a), kw[a]);
-          }
-        }
-        // state keys = the same bf16 values, [channel][token]: channel 2j (2j+1)
-        // is the low (high) half of word j of the four token rows
-#pragma unroll
-        for (int j = 0; j < NWR; ++j) {
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb) {
-            const unsigned sel = hb ? 0x07060302u : 0x05040100u;
-            const unsigned lo = __builtin_amdgcn_perm(kw[1][j], kw[0][j], sel);
-            const unsigned hi = __builtin_amdgcn_perm(kw[3][j], kw[2][j], sel);
-            *reinterpret_cast<uint2*>(kt_slot(2 * j + hb)) = uint2{lo, hi};
-          }
-        }
-        if (tg == 15) {   // this lane's last token is the chunk's last row
-          float e[CPL];
-#pragma unroll
-          for (int i = 0; i < CPL; ++i) {
-            e[i] = fast_exp2(inc[i]);
-            if constexpr (!FULL) dsum[i] += inc[i];
-          }
-          store_f32<CPL>(&B.post[ch0], e);
-          // the safe-path factors of this slice are ones; they stay so in this
-          // buffer until a safe chunk overwrites them
-          if (!(ones & (1 << bi))) {
-            float one[CPL];
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) one[i] = 1.f;
-            store_f32<CPL>(&B.pre[ch0], one);
-#pragma unroll
-            for (int p = 0; p < 4; ++p) store_f32<CPL>(&B.bq[p][ch0], one);
-#pragma unroll
-            for (int e2 = 0; e2 < 7; ++e2) store_f32<CPL>(&B.w[e2][ch0], one);
-          }
-        }
-        ones |= 1 << bi;
-        if (lane == 0) B.flag[w] = 0;
-      } else {
-        // ---- 16-token sub-chunk pivots ----
-        // loc = Gamma relative to the start of the token's sub-chunk, tot = the
-        // sub-chunk's total: a 4-lane scan of the lane totals within each quad
+        __builtin_amdgcn_sched_barrier(0);
+        load_g(un);
+        float kte[4][CPL];
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-          for (int i = 0; i < CPL; ++i) launder(pp[a][i]);
-        float loc[4][CPL], tot[CPL];
-        bool ext = false;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-          float u4 = pp[3][i];
-          const float t1 = dpp<kRowShr1>(u4);
-          u4 += (tg & 3) >= 1 ? t1 : 0.f;
-          const float t2 = dpp<kRowShr2>(u4);
-          u4 += (tg & 3) >= 2 ? t2 : 0.f;
-          const float ex = u4 - pp[3][i];
-#pragma unroll
-          for (int a = 0; a < 4; ++a) loc[a][i] = ex + pp[a][i];
-          const float tt = quad_bcast_c<3>(u4);
-          tot[i] = tt;
-          ext |= !(fabsf(tt) <= kExtremeLimit);
-        }
-        const bool extw = __ballot(ext) != 0ull;
-        // sub-chunk prefixes: s1 = total of sub-chunk p-1, s2 = of p-2, B_p = Gamma at
-        // the row before sub-chunk p, b4 = Gamma at the chunk's last row; identical in
-        // the four lanes of a quad, so each lane writes CPL/4 channels' factors
-        float fke[CPL];
-        {
-          float s1v[CPL], s2v[CPL], Bp[CPL], b4[CPL];
-#pragma unroll
-          for (int i = 0; i < CPL; ++i) {
-            const float tt = tot[i];
-            const float a1 = dpp<kRowShr4>(tt), a2 = dpp<kRowShr8>(tt), a3 = dpp<kRowShr12>(tt);
-            s1v[i] = a1;
-            s2v[i] = a2;
-            Bp[i] = (a1 + a2) + a3;
-            const float bn = Bp[i] + tt;
-            const float r4 = dpp<kRowRor4>(bn), r8 = dpp<kRowRor8>(bn), r12 = dpp<kRowRor12>(bn);
-            b4[i] = sub == 3 ? bn : sub == 0 ? r4 : sub == 1 ? r8 : r12;
-            fke[i] = fast_exp2(b4[i] - bn);   // 2^(Gamma_last - B_{p+1})
-            if constexpr (!FULL) dsum[i] += b4[i];
-          }
-          constexpr int NPL = CPL / 4;
-          const int qd = tg & 3;
-          auto pick = [&](const float (&x)[CPL], int j) __attribute__((always_inline)) -> float {
-            return qd == 0 ? x[j] : qd == 1 ? x[NPL + j] : qd == 2 ? x[2 * NPL + j] : x[3 * NPL + j];
-          };
-#pragma unroll
-          for (int j = 0; j < NPL; ++j) {
-            const int c = ch0 + qd * NPL + j;
-            const float s1 = pick(s1v, j);
-            const float ebq = fast_exp2(pick(Bp, j));
-            // an extreme slice's diagonal blocks come from the exact partials alone
-            const float ew = extw ? 0.f : fast_exp2(-pick(tot, j));
-            const float e1 = fast_exp2(s1);
-            const float e12 = fast_exp2(s1 + pick(s2v, j));
-            const float epre = fast_exp2(pick(b4, j));
-            B.bq[sub][c] = ebq;
-            B.w[sub][c] = ew;
-            if (sub == 2) B.w[4][c] = e1;
-            if (sub == 3) {
-              B.w[5][c] = e1;
-              B.w[6][c] = e12;
-            }
-            if (sub == 0) {
-              B.pre[c] = epre;
-              B.post[c] = 1.f;
-            }
-          }
-        }
-        if (FULL && extw) {
-          // exact diagonal partials, one (row a, key pair jj) at a time: sum over this
-          // lane's channels, then over the wave's four lane rows (its whole slice)
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const int irow = (tg & 3) * 4 + a;
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-              __builtin_amdgcn_sched_barrier(0);
-              float dd[2];
-#pragma unroll
-              for (int h2 = 0; h2 < 2; ++h2) {
-                const int j = 2 * jj + h2, src = j >> 2, b = j & 3;
-                float acc = 0.f;
-#pragma unroll
-                for (int i2 = 0; i2 < NWR; ++i2) {
-                  const unsigned kw = __builtin_bit_cast(unsigned, quad_bcast(__builtin_bit_cast(float, rk[b][i2]), src));
-                  const float l0 = quad_bcast(loc[b][2 * i2], src);
-                  const float l1 = quad_bcast(loc[b][2 * i2 + 1], src);
-                  acc += el(rq[a], 2 * i2) * __uint_as_float(kw << 16) * fast_exp2(loc[a][2 * i2] - l0);
-                  acc += el(rq[a], 2 * i2 + 1) * __uint_as_float(kw & 0xffff0000u) *
-                         fast_exp2(loc[a][2 * i2 + 1] - l1);
-                }
-                acc = j <= irow ? acc : 0.f;
-                acc += __shfl_xor(acc, 16);
-                acc += __shfl_xor(acc, 32);
-                dd[h2] = acc;
-              }
-              if (gq == 0)
-                *reinterpret_cast<unsigned*>(&B.diag[w][sub][irow][2 * jj]) = pack_bf16x2(dd[0], dd[1]);
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        float kte[4][CPL];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          float qh[CPL], kt[CPL];
-#pragma unroll
-          for (int i = 0; i < CPL; ++i) {
-            if constexpr (FULL) qh[i] = el(rq[a], i) * fast_exp2(loc[a][i]);   // Q 2^(Gamma - B_p)
-            kt[i] = el(rk[a], i) * fast_exp2(tot[i] - loc[a][i]);   // K 2^(B_{p+1} - Gamma)
-            kte[a][i] = kt[i] * fke[i];                          // K 2^(Gamma_last - Gamma)
-          }
-          if constexpr (FULL) {
-            lds_store_n<BF16, CPL>(slot(kQ, a), qh);
-            lds_store_n<BF16, CPL>(slot(kK, a), kt);
-          }
-        }
+          for (int i = 0; i < CPL; ++i) kte[a][i] = el(rk[a], i) * fast_exp2(gf[a][i]);
 #pragma unroll
         for (int i = 0; i < CPL; ++i)
           store4<BF16>(kt_slot(i), kte[0][i], kte[1][i], kte[2][i], kte[3][i]);
-        if (lane == 0) B.flag[w] = 1 | (extw ? 2 : 0);
-        ones &= ~(1 << bi);
+        if (tg == 15) {
+          float e[CPL], one[CPL];
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) {
+            e[i] = fast_exp2(tot[i]);
+            one[i] = 1.f;
+            dsum[i] += tot[i];
+          }
+          store_f32<CPL>(&B.pre[ch0], e);
+          store_f32<CPL>(&B.post[ch0], one);
+        }
+        if (lane == 0) B.flag[w] = 1;
+      } else {
+        // log2 gates: pp = inclusive prefix over this lane's 4 tokens, inc =
+        // inclusive prefix over the chunk at this lane's last token (a 16-lane
+        // DPP scan of the lane totals).  Gates are <= 0, so |Gamma| is largest
+        // at the chunk's last row; the chunk is a fast one for this wave when
+        // every |Gamma| of its slice stays within 2^kFastLimit.  A -inf gate
+        // (alpha = 0) makes Gamma infinite and the chunk a safe one.
+        float pp[4][CPL], inc[CPL];
+        float mx = 0.f;
+  #pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          pp[0][i] = el(rg[0], i) * kLog2e;
+  #pragma unroll
+          for (int a = 1; a < 4; ++a) pp[a][i] = fmaf(el(rg[a], i), kLog2e, pp[a - 1][i]);
+          float x = pp[3][i];
+          x += dpp<kRowShr1>(x);
+          x += dpp<kRowShr2>(x);
+          x += dpp<kRowShr4>(x);
+          x += dpp<kRowShr8>(x);
+          inc[i] = x;
+          mx = fmaxf(mx, fabsf(x));
+        }
+        const bool fastw = __ballot(!(mx <= kFastLimit)) == 0ull;
+        if (!fastw) {
+          // the safe path works from gates floored at -256 (log2), so that an
+          // alpha = 0 gate cannot produce inf - inf (laundering keeps the
+          // compiler from speculating this rare work into the fast path)
+  #pragma unroll
+          for (int a = 0; a < 4; ++a)
+  #pragma unroll
+            for (int j = 0; j < NWR; ++j) launder(rg[a][j]);
+  #pragma unroll
+          for (int i = 0; i < CPL; ++i) {
+  #pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              const float y = fmaxf(el(rg[a], i) * kLog2e, -256.f);
+              pp[a][i] = a ? pp[a - 1][i] + y : y;
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_g(un);
+        if (fastw) {
+          // ---- single pivot at the chunk start ----
+          float ex[CPL];   // Gamma before this lane's first token
+  #pragma unroll
+          for (int i = 0; i < CPL; ++i) ex[i] = inc[i] - pp[3][i];
+          unsigned kw[4][NWR];   // packed key operand words, token a
+  #pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            float qe[CPL], ke[CPL];
+  #pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+              const float gm = ex[i] + pp[a][i];   // Gamma of token 4tg+a
+              if constexpr (FULL) qe[i] = el(rq[a], i) * fast_exp2(gm);
+              ke[i] = el(rk[a], i) * fast_exp2(-gm);
+            }
+  #pragma unroll
+            for (int j = 0; j < NWR; ++j) kw[a][j] = pack_bf16x2(ke[2 * j], ke[2 * j + 1]);
+            if constexpr (FULL) {
+              lds_store_n<BF16, CPL>(slot(kQ, a), qe);
+              st(slot(kK, a), kw[a]);
+            }
+          }
+          // state keys = the same bf16 values, [channel][token]: channel 2j (2j+1)
+          // is the low (high) half of word j of the four token rows
+  #pragma unroll
+          for (int j = 0; j < NWR; ++j) {
+  #pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+              const unsigned sel = hb ? 0x07060302u : 0x05040100u;
+              const unsigned lo = __builtin_amdgcn_perm(kw[1][j], kw[0][j], sel);
+              const unsigned hi = __builtin_amdgcn_perm(kw[3][j], kw[2][j], sel);
+              *reinterpret_cast<uint2*>(kt_slot(2 * j + hb)) = uint2{lo, hi};
+            }
+          }
+          if (tg == 15) {   // this lane's last token is the chunk's last row
+            float e[CPL];
+  #pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+              e[i] = fast_exp2(inc[i]);
+              if constexpr (!FULL) dsum[i] += inc[i];
+            }
+            store_f32<CPL>(&B.post[ch0], e);
+            // the safe-path factors of this slice are ones; they stay so in this
+            // buffer until a safe chunk overwrites them
+            if (!(ones & (1 << bi))) {
+              float one[CPL];
+  #pragma unroll
+              for (int i = 0; i < CPL; ++i) one[i] = 1.f;
+              store_f32<CPL>(&B.pre[ch0], one);
+  #pragma unroll
+              for (int p = 0; p < 4; ++p) store_f32<CPL>(&B.bq[p][ch0], one);
+  #pragma unroll
+              for (int e2 = 0; e2 < 7; ++e2) store_f32<CPL>(&B.w[e2][ch0], one);
+            }
+          }
+          ones |= 1 << bi;
+          if (lane == 0) B.flag[w] = 0;
+        } else {
+          // ---- 16-token sub-chunk pivots ----
+          // loc = Gamma relative to the start of the token's sub-chunk, tot = the
+          // sub-chunk's total: a 4-lane scan of the lane totals within each quad
+  #pragma unroll
+          for (int a = 0; a < 4; ++a)
+  #pragma unroll
+            for (int i = 0; i < CPL; ++i) launder(pp[a][i]);
+          float loc[4][CPL], tot[CPL];
+          bool ext = false;
+  #pragma unroll
+          for (int i = 0; i < CPL; ++i) {
+            float u4 = pp[3][i];
+            const float t1 = dpp<kRowShr1>(u4);
+            u4 += (tg & 3) >= 1 ? t1 : 0.f;
+            const float t2 = dpp<kRowShr2>(u4);
+            u4 += (tg & 3) >= 2 ? t2 : 0.f;
+            const float ex = u4 - pp[3][i];
+  #pragma unroll
+            for (int a = 0; a < 4; ++a) loc[a][i] = ex + pp[a][i];
+            const float tt = quad_bcast_c<3>(u4);
+            tot[i] = tt;
+            ext |= !(fabsf(tt) <= kExtremeLimit);
+          }
+          const bool extw = __ballot(ext) != 0ull;
+          // sub-chunk prefixes: s1 = total of sub-chunk p-1, s2 = of p-2, B_p = Gamma at
+          // the row before sub-chunk p, b4 = Gamma at the chunk's last row; identical in
+          // the four lanes of a quad, so each lane writes CPL/4 channels' factors
+          float fke[CPL];
+          {
+            float s1v[CPL], s2v[CPL], Bp[CPL], b4[CPL];
+  #pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+              const float tt = tot[i];
+              const float a1 = dpp<kRowShr4>(tt), a2 = dpp<kRowShr8>(tt), a3 = dpp<kRowShr12>(tt);
+              s1v[i] = a1;
+              s2v[i] = a2;
+              Bp[i] = (a1 + a2) + a3;
+              const float bn = Bp[i] + tt;
+              const float r4 = dpp<kRowRor4>(bn), r8 = dpp<kRowRor8>(bn), r12 = dpp<kRowRor12>(bn);
+              b4[i] = sub == 3 ? bn : sub == 0 ? r4 : sub == 1 ? r8 : r12;
+              fke[i] = fast_exp2(b4[i] - bn);   // 2^(Gamma_last - B_{p+1})
+              if constexpr (!FULL) dsum[i] += b4[i];
+            }
+            constexpr int NPL = CPL / 4;
+            const int qd = tg & 3;
+            auto pick = [&](const float (&x)[CPL], int j) __attribute__((always_inline)) -> float {
+              return qd == 0 ? x[j] : qd == 1 ? x[NPL + j] : qd == 2 ? x[2 * NPL + j] : x[3 * NPL + j];
+            };
+  #pragma unroll
+            for (int j = 0; j < NPL; ++j) {
+              const int c = ch0 + qd * NPL + j;
+              const float s1 = pick(s1v, j);
+              const float ebq = fast_exp2(pick(Bp, j));
+              // an extreme slice's diagonal blocks come from the exact partials alone
+              const float ew = extw ? 0.f : fast_exp2(-pick(tot, j));
+              const float e1 = fast_exp2(s1);
+              const float e12 = fast_exp2(s1 + pick(s2v, j));
+              const float epre = fast_exp2(pick(b4, j));
+              B.bq[sub][c] = ebq;
+              B.w[sub][c] = ew;
+              if (sub == 2) B.w[4][c] = e1;
+              if (sub == 3) {
+                B.w[5][c] = e1;
+                B.w[6][c] = e12;
+              }
+              if (sub == 0) {
+                B.pre[c] = epre;
+                B.post[c] = 1.f;
+              }
+            }
+          }
+          if (FULL && extw) {
+            // exact diagonal partials, one (row a, key pair jj) at a time: sum over this
+            // lane's channels, then over the wave's four lane rows (its whole slice)
+  #pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              const int irow = (tg & 3) * 4 + a;
+  #pragma unroll
+              for (int jj = 0; jj < 8; ++jj) {
+                __builtin_amdgcn_sched_barrier(0);
+                float dd[2];
+  #pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                  const int j = 2 * jj + h2, src = j >> 2, b = j & 3;
+                  float acc = 0.f;
+  #pragma unroll
+                  for (int i2 = 0; i2 < NWR; ++i2) {
+                    const unsigned kw = __builtin_bit_cast(unsigned, quad_bcast(__builtin_bit_cast(float, rk[b][i2]), src));
+                    const float l0 = quad_bcast(loc[b][2 * i2], src);
+                    const float l1 = quad_bcast(loc[b][2 * i2 + 1], src);
+                    acc += el(rq[a], 2 * i2) * __uint_as_float(kw << 16) * fast_exp2(loc[a][2 * i2] - l0);
+                    acc += el(rq[a], 2 * i2 + 1) * __uint_as_float(kw & 0xffff0000u) *
+                           fast_exp2(loc[a][2 * i2 + 1] - l1);
+                  }
+                  acc = j <= irow ? acc : 0.f;
+                  acc += __shfl_xor(acc, 16);
+                  acc += __shfl_xor(acc, 32);
+                  dd[h2] = acc;
+                }
+                if (gq == 0)
+                  *reinterpret_cast<unsigned*>(&B.diag[w][sub][irow][2 * jj]) = pack_bf16x2(dd[0], dd[1]);
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          float kte[4][CPL];
+  #pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            float qh[CPL], kt[CPL];
+  #pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+              if constexpr (FULL) qh[i] = el(rq[a], i) * fast_exp2(loc[a][i]);   // Q 2^(Gamma - B_p)
+              kt[i] = el(rk[a], i) * fast_exp2(tot[i] - loc[a][i]);   // K 2^(B_{p+1} - Gamma)
+              kte[a][i] = kt[i] * fke[i];                          // K 2^(Gamma_last - Gamma)
+            }
+            if constexpr (FULL) {
+              lds_store_n<BF16, CPL>(slot(kQ, a), qh);
+              lds_store_n<BF16, CPL>(slot(kK, a), kt);
+            }
+          }
+  #pragma unroll
+          for (int i = 0; i < CPL; ++i)
+            store4<BF16>(kt_slot(i), kte[0][i], kte[1][i], kte[2][i], kte[3][i]);
+          if (lane == 0) B.flag[w] = 1 | (extw ? 2 : 0);
+          ones &= ~(1 << bi);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       load_qk(un);
@@ -591,16 +644,18 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     // step i produces chunk i into bufs[i & 1] while the consumers use chunk i-1;
     // the look-ahead index is clamped, so the last step re-reads the last chunk
     // and no load sits behind a branch
+    // chunk processed at step i (the gradient pass walks them from last to first)
+    auto ck = [&](int i) __attribute__((always_inline)) { return REV ? nch - 1 - i : i; };
     if (nch > 0) {
-      load_v(0);
-      load_g(0);
-      load_qk(0);
+      load_v(ck(0));
+      load_g(ck(0));
+      load_qk(ck(0));
     }
     for (int i = 0; i <= nch; ++i) {
-      if (i < nch) produce(bufs[i & 1], i & 1, i + 1 < nch ? i + 1 : i);
+      if (i < nch) produce(bufs[i & 1], i & 1, ck(i + 1 < nch ? i + 1 : i));
       barrier_lds();
     }
-    if constexpr (MODE == kStateOnly) {
+    if constexpr (MODE == kStateOnly || REV) {
       // the segment's decay exp(sum of g) per key channel, once per (unit, segment)
       if (vt == 0 && tg == 15) {
         float e[CPL];
@@ -885,6 +940,17 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
           }
     }
   }
+}
+
+int launch_chunk_seg_grad(const ChunkParams& prm, int dk, int nblocks, hipStream_t stream) {
+  if (prm.dvt != 64 || prm.nvt * 64 != prm.DV || prm.nseg < 2 || prm.cu || prm.sort_units) return -2;
+  if (dk == 128)
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<128, kSegGrad, 1>), dim3(nblocks), dim3(512), 0, stream, prm);
+  else if (dk == 64)
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<64, kSegGrad, 1>), dim3(nblocks), dim3(512), 0, stream, prm);
+  else
+    return -2;
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_chunk_fwd_states(const ChunkParams& prm, int dk, int nblocks, hipStream_t stream) {

@@ -418,8 +418,19 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
     const long long nb2 = units * (nseg - 1) * nvt;
     if (!fits_i32(nb2) || !fits_i32(units * nseg))
       return fail(GLA_ERR_INVALID_ARG, "%s: %lld work items", fn, nb2);
-    prm.xcd_remap = (nb2 % 8 == 0) ? 1 : 0;
-    rc = gla::launch_chunk_bstates(prm, dk, (int)nb2, s);
+    // the pipelined kernel again, chunks last to first, q and dO in the key and
+    // value places, B = 0 at each segment's end
+    gla::ChunkParams gp = fp;
+    gp.k = q;
+    gp.v = d_o;
+    gp.s0 = nullptr;
+    gp.hs = nullptr;
+    gp.nseg = nseg;
+    gp.seg_len = seg_len;
+    gp.seg_state = prm.seg_state;
+    gp.seg_decay = prm.seg_decay;
+    gp.xcd_remap = (nb2 % 8 == 0) ? 1 : 0;
+    rc = gla::launch_chunk_seg_grad(gp, dk, (int)nb2, s);
     if (rc != 0) return launch_status(fn, rc, dk, dtype);
     gla::SegScanParams sp;
     sp.s0 = d_final_state;

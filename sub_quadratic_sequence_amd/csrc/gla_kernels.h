@@ -44,6 +44,7 @@ constexpr int kMaxSortSeqs = 64;
 constexpr int kFull = 0;       // outputs (and the final state of unsplit sequences)
 constexpr int kStateOnly = 1;  // a segment's state from zero and its total decay
 constexpr int kChunkStates = 2;  // the state entering every chunk, to ChunkParams::hs
+constexpr int kSegGrad = 3;      // the backward split's segment state gradients (k, v = q, dO)
 
 // Element (row c, column n) of a chunk-state slot (dk x dv, bf16).  The order
 // follows the forward consumer's accumulators (column slice n / 64, its 16-column
@@ -131,8 +132,8 @@ int launch_chunk_fwd(const ChunkParams& prm, int dk, int dtype, int nblocks, hip
 int launch_chunk_fwd_pipe(const ChunkParams& prm, int dk, bool state_only, int nblocks,
                           hipStream_t stream);
 int launch_chunk_fwd_states(const ChunkParams& prm, int dk, int nblocks, hipStream_t stream);
+int launch_chunk_seg_grad(const ChunkParams& prm, int dk, int nblocks, hipStream_t stream);
 int launch_seg_scan(const SegScanParams& prm, int units, hipStream_t stream);
-int launch_chunk_bstates(const BwdParams& prm, int dk, int nblocks, hipStream_t stream);
 int launch_chunk_bwd(const BwdParams& prm, int dk, int dv, int nblocks, hipStream_t stream);
 int launch_gdn_chunk_fwd(const GdnParams& prm, int dk, int nblocks, hipStream_t stream);
 int launch_recurrent_step(const StepParams& prm, int units, int dk, int dv, int dtype,
