@@ -1,0 +1,82 @@
+"""Host-side checks of bench.py and of the committed rocprofv3 summaries it reads
+(no GPU needed: nothing here launches a kernel)."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+TRAFFIC_SUMMARIES = [
+    ("chunk_fwd_b8h16t2048d128_bf16_traffic.txt", bench.KERNEL_SRC),
+    ("recurrent_step_n256h16d128_bf16_traffic.txt", bench.STEP_SRC),
+    ("gdn_fwd_b8h16t2048d128_bf16.txt", bench.GDN_SRC),
+]
+
+
+def _fields(path):
+    kv = {}
+    for line in open(path):
+        line = line.strip()
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    return kv
+
+
+@pytest.mark.parametrize("gpus", ["2", "8"])
+def test_bench_refuses_more_than_one_gpu(gpus):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", gpus],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
+
+
+def test_bench_refuses_a_multi_rank_launch():
+    env = dict(os.environ, WORLD_SIZE="2")
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")], capture_output=True,
+                       text=True, timeout=120, cwd=ROOT, env=env)
+    assert r.returncode == 2
+    assert "WORLD_SIZE=2" in r.stderr
+
+
+@pytest.mark.parametrize("name,src", TRAFFIC_SUMMARIES)
+def test_traffic_summaries_are_well_formed(name, src):
+    kv = _fields(os.path.join(bench.PROFILES, name))
+    for key in ("kernel", "fetch_size_kib_per_dispatch", "write_size_kib_per_dispatch",
+                "fetch_scale", "write_scale", "kernel_source_sha256", "hbm_bytes_per_launch",
+                "algorithmic_bytes_per_launch", "traffic_over_algorithmic"):
+        assert key in kv, key
+    fetch = float(kv["fetch_size_kib_per_dispatch"]) * float(kv["fetch_scale"])
+    write = float(kv["write_size_kib_per_dispatch"]) * float(kv["write_scale"])
+    hbm = float(kv["hbm_bytes_per_launch"])
+    # the printed scale factors carry four decimals
+    assert hbm == pytest.approx((fetch + write) * 1024, rel=1e-4)
+    ratio = hbm / float(kv["algorithmic_bytes_per_launch"])
+    assert ratio == pytest.approx(float(kv["traffic_over_algorithmic"]), abs=1e-3)
+    # the counters can only read at least the bytes the kernel must move, and far
+    # more would mean a mis-scaled calibration
+    assert 0.99 < ratio < 1.5
+    assert len(kv["kernel_source_sha256"]) == 64
+
+
+def test_read_traffic_follows_the_kernel_source(tmp_path):
+    src = tmp_path / "k.hip"
+    src.write_text("// kernel v1\n")
+    prof = tmp_path / "p.txt"
+    prof.write_text("# header = ignored\nkernel_source_sha256 = %s\nhbm_bytes_per_launch = 1234\n"
+                    % bench.sha256(str(src)))
+    old = bench.PROFILES
+    try:
+        bench.PROFILES = str(tmp_path)
+        assert bench.read_traffic("p.txt", str(src)) == 1234.0
+        src.write_text("// kernel v2\n")   # the source changed since the counters were taken
+        assert bench.read_traffic("p.txt", str(src)) is None
+        assert bench.read_traffic("missing.txt", str(src)) is None
+    finally:
+        bench.PROFILES = old
