@@ -333,17 +333,11 @@ def bench_gdn(args, torch, gla, inputs):
     return res
 
 
-def cpu_baseline(fwd, min_seconds=12.0, max_passes=64):
-    """The fp64 oracle as it stands, on the host, on the forward workload's own
-    inputs: whole sequences (all heads, all tokens) of the batch are run, cycling
-    through the batch, until at least min_seconds of oracle time have passed."""
-    import oracle
-
-    w, d = fwd["w"], fwd["d"]
-    threads = min(16, os.cpu_count() or 1)
-    oracle.build(force=False)
+def _time_oracle(oracle, w, d, threads, min_seconds, max_runs):
+    """Whole sequences of the batch through the fp64 oracle, cycling through the
+    batch, until at least min_seconds of oracle time (and one sequence) have passed."""
     done_tokens, elapsed, used, n = 0, 0.0, 0, 0
-    while elapsed < min_seconds and n < max_passes * w.B:
+    while (elapsed < min_seconds or n == 0) and n < max_runs:
         b = n % w.B
         sl = slice(b, b + 1)
         t0 = time.perf_counter()
@@ -352,11 +346,30 @@ def cpu_baseline(fwd, min_seconds=12.0, max_passes=64):
         elapsed += time.perf_counter() - t0
         done_tokens += w.T
         n += 1
+    return done_tokens, elapsed, used, n
+
+
+def cpu_baseline(fwd, min_seconds=12.0, max_passes=64, one_thread_seconds=3.0):
+    """The fp64 oracle as it stands, on the host, on the forward workload's own
+    inputs: whole sequences (all heads, all tokens) of the batch are run, cycling
+    through the batch, until at least min_seconds of oracle time have passed; then
+    the same on one thread for at least one_thread_seconds."""
+    import oracle
+
+    w, d = fwd["w"], fwd["d"]
+    threads = min(16, os.cpu_count() or 1)
+    oracle.build(force=False)
+    done_tokens, elapsed, used, n = _time_oracle(oracle, w, d, threads, min_seconds,
+                                                 max_passes * w.B)
     sample = (f"{n} sequence runs ({n / w.B:.2f} passes over the {w.B}-sequence batch) x {w.H} "
               f"heads x {w.T} tokens of the same workload (fp64 token recurrence, OpenMP over "
               f"heads, final state kept)")
+    t1, e1, u1, n1 = _time_oracle(oracle, w, d, 1, one_thread_seconds, max_passes * w.B)
     return {"value": done_tokens / elapsed, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": sample, "seconds": round(elapsed, 3)}
+            "sample": sample, "seconds": round(elapsed, 3),
+            "one_thread": {"value": t1 / e1, "unit": "tokens/s", "cores": u1,
+                           "sample": f"{n1} sequence runs x {w.H} heads x {w.T} tokens",
+                           "seconds": round(e1, 3)}}
 
 
 def main():
@@ -547,7 +560,8 @@ def main():
         log("[bench] timing the fp64 oracle on the host")
         out["cpu_baseline"] = cpu_baseline(fwd)
         log(f"[bench] oracle: {out['cpu_baseline']['value']:.3g} tokens/s on "
-            f"{out['cpu_baseline']['cores']} threads")
+            f"{out['cpu_baseline']['cores']} threads, "
+            f"{out['cpu_baseline']['one_thread']['value']:.3g} tokens/s on one")
     print(json.dumps(out), flush=True)
 
 
