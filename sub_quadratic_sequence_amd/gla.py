@@ -80,11 +80,13 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _check_gpu(name, t, dtype=None, shape=None):
+def _check_gpu(name, t, dtype=None, shape=None, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on the GPU (got {t.device}); there is no CPU path")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other arguments on {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
@@ -122,25 +124,26 @@ def gla_chunk_fwd(q, k, v, g, initial_state=None, output_final_state=False, cu_s
     dv = v.shape[-1]
     _check_gpu("q", q)
     dt = q.dtype
-    _check_gpu("k", k, dt, q.shape)
-    _check_gpu("g", g, dt, q.shape)
-    _check_gpu("v", v, dt, (B, H, T, dv))
+    _check_gpu("k", k, dt, q.shape, device=q.device)
+    _check_gpu("g", g, dt, q.shape, device=q.device)
+    _check_gpu("v", v, dt, (B, H, T, dv), device=q.device)
     nseq = B
     num_seqs = 0
     if cu_seqlens is not None:
-        _check_gpu("cu_seqlens", cu_seqlens, torch.int32)
+        _check_gpu("cu_seqlens", cu_seqlens, torch.int32, device=q.device)
         num_seqs = cu_seqlens.numel() - 1
         nseq = num_seqs
     if initial_state is not None:
-        _check_gpu("initial_state", initial_state, torch.float32, (nseq, H, dk, dv))
+        _check_gpu("initial_state", initial_state, torch.float32, (nseq, H, dk, dv),
+                   device=q.device)
     if out is None:
         out = torch.empty((B, H, T, dv), dtype=dt, device=q.device)
     else:
-        _check_gpu("out", out, dt, (B, H, T, dv))
+        _check_gpu("out", out, dt, (B, H, T, dv), device=q.device)
     if final_state is None and output_final_state:
         final_state = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
     elif final_state is not None:
-        _check_gpu("final_state", final_state, torch.float32, (nseq, H, dk, dv))
+        _check_gpu("final_state", final_state, torch.float32, (nseq, H, dk, dv), device=q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -153,7 +156,7 @@ def gla_chunk_fwd(q, k, v, g, initial_state=None, output_final_state=False, cu_s
                 workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
             ws_ptr, ws_bytes = None, 0
             if workspace is not None:
-                _check_gpu("workspace", workspace, torch.uint8)
+                _check_gpu("workspace", workspace, torch.uint8, device=q.device)
                 base = workspace.data_ptr()
                 off = (-base) % 256
                 ws_ptr, ws_bytes = ctypes.c_void_p(base + off), max(0, workspace.numel() - off)
@@ -173,9 +176,9 @@ def bwd_workspace_size(q, v, cu_seqlens=None, chunk_size: int = 64) -> int:
                                                            int(chunk_size), _dtype_code(q)))
 
 
-def _aligned_workspace(workspace):
+def _aligned_workspace(workspace, device):
     """(pointer, bytes) of the 256-byte aligned part of a uint8 GPU tensor."""
-    _check_gpu("workspace", workspace, torch.uint8)
+    _check_gpu("workspace", workspace, torch.uint8, device=device)
     base = workspace.data_ptr()
     off = (-base) % 256
     return ctypes.c_void_p(base + off), max(0, workspace.numel() - off)
@@ -198,18 +201,18 @@ def gla_chunk_bwd(q, k, v, g, do, initial_state=None, d_final_state=None, cu_seq
     dv = v.shape[-1]
     _check_gpu("q", q)
     dt = q.dtype
-    _check_gpu("k", k, dt, q.shape)
-    _check_gpu("g", g, dt, q.shape)
-    _check_gpu("v", v, dt, (B, H, T, dv))
-    _check_gpu("do", do, dt, (B, H, T, dv))
+    _check_gpu("k", k, dt, q.shape, device=q.device)
+    _check_gpu("g", g, dt, q.shape, device=q.device)
+    _check_gpu("v", v, dt, (B, H, T, dv), device=q.device)
+    _check_gpu("do", do, dt, (B, H, T, dv), device=q.device)
     nseq, num_seqs = B, 0
     if cu_seqlens is not None:
-        _check_gpu("cu_seqlens", cu_seqlens, torch.int32)
+        _check_gpu("cu_seqlens", cu_seqlens, torch.int32, device=q.device)
         num_seqs = cu_seqlens.numel() - 1
         nseq = num_seqs
     for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
         if t is not None:
-            _check_gpu(name, t, torch.float32, (nseq, H, dk, dv))
+            _check_gpu(name, t, torch.float32, (nseq, H, dk, dv), device=q.device)
     if want_d_initial_state is None:
         want_d_initial_state = initial_state is not None
     if out is None:
@@ -218,7 +221,7 @@ def gla_chunk_bwd(q, k, v, g, do, initial_state=None, d_final_state=None, cu_seq
     else:
         dq, dk_, dv_, dg = out
         for name, t, ref in (("dq", dq, q), ("dk", dk_, k), ("dv", dv_, v), ("dg", dg, g)):
-            _check_gpu(name, t, dt, tuple(ref.shape))
+            _check_gpu(name, t, dt, tuple(ref.shape), device=q.device)
     ds0 = (torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
            if want_d_initial_state else None)
     lib = load_library()
@@ -227,7 +230,7 @@ def gla_chunk_bwd(q, k, v, g, do, initial_state=None, d_final_state=None, cu_seq
         if workspace is None:
             need = bwd_workspace_size(q, v, cu_seqlens, chunk_size)
             workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
-        ws_ptr, ws_bytes = _aligned_workspace(workspace)
+        ws_ptr, ws_bytes = _aligned_workspace(workspace, q.device)
         rc = lib.gla_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(initial_state), _ptr(do),
                                _ptr(d_final_state), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg),
                                _ptr(ds0), _ptr(cu_seqlens), num_seqs, B, H, T, dk, dv,
@@ -266,14 +269,14 @@ def gla_recurrent_step(q, k, v, g, state, out=None):
     dv = v.shape[-1]
     _check_gpu("q", q)
     dt = q.dtype
-    _check_gpu("k", k, dt, q.shape)
-    _check_gpu("g", g, dt, q.shape)
-    _check_gpu("v", v, dt, (N, H, dv))
-    _check_gpu("state", state, torch.float32, (N, H, dk, dv))
+    _check_gpu("k", k, dt, q.shape, device=q.device)
+    _check_gpu("g", g, dt, q.shape, device=q.device)
+    _check_gpu("v", v, dt, (N, H, dv), device=q.device)
+    _check_gpu("state", state, torch.float32, (N, H, dk, dv), device=q.device)
     if out is None:
         out = torch.empty((N, H, dv), dtype=dt, device=q.device)
     else:
-        _check_gpu("out", out, dt, (N, H, dv))
+        _check_gpu("out", out, dt, (N, H, dv), device=q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -299,26 +302,27 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=False
     dv = v.shape[-1]
     _check_gpu("q", q)
     dt = q.dtype
-    _check_gpu("k", k, dt, q.shape)
-    _check_gpu("v", v, dt, (B, H, T, dv))
-    _check_gpu("g", g, torch.float32, (B, H, T))
-    _check_gpu("beta", beta, torch.float32, (B, H, T))
+    _check_gpu("k", k, dt, q.shape, device=q.device)
+    _check_gpu("v", v, dt, (B, H, T, dv), device=q.device)
+    _check_gpu("g", g, torch.float32, (B, H, T), device=q.device)
+    _check_gpu("beta", beta, torch.float32, (B, H, T), device=q.device)
     nseq = B
     num_seqs = 0
     if cu_seqlens is not None:
-        _check_gpu("cu_seqlens", cu_seqlens, torch.int32)
+        _check_gpu("cu_seqlens", cu_seqlens, torch.int32, device=q.device)
         num_seqs = cu_seqlens.numel() - 1
         nseq = num_seqs
     if initial_state is not None:
-        _check_gpu("initial_state", initial_state, torch.float32, (nseq, H, dk, dv))
+        _check_gpu("initial_state", initial_state, torch.float32, (nseq, H, dk, dv),
+                   device=q.device)
     if out is None:
         out = torch.empty((B, H, T, dv), dtype=dt, device=q.device)
     else:
-        _check_gpu("out", out, dt, (B, H, T, dv))
+        _check_gpu("out", out, dt, (B, H, T, dv), device=q.device)
     if final_state is None and output_final_state:
         final_state = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
     elif final_state is not None:
-        _check_gpu("final_state", final_state, torch.float32, (nseq, H, dk, dv))
+        _check_gpu("final_state", final_state, torch.float32, (nseq, H, dk, dv), device=q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
