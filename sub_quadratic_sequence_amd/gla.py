@@ -131,6 +131,8 @@ def gla_chunk_fwd(q, k, v, g, initial_state=None, output_final_state=False, cu_s
     num_seqs = 0
     if cu_seqlens is not None:
         _check_gpu("cu_seqlens", cu_seqlens, torch.int32, device=q.device)
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be 1-D with num_seqs + 1 >= 2 offsets")
         num_seqs = cu_seqlens.numel() - 1
         nseq = num_seqs
     if initial_state is not None:
@@ -208,6 +210,8 @@ def gla_chunk_bwd(q, k, v, g, do, initial_state=None, d_final_state=None, cu_seq
     nseq, num_seqs = B, 0
     if cu_seqlens is not None:
         _check_gpu("cu_seqlens", cu_seqlens, torch.int32, device=q.device)
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be 1-D with num_seqs + 1 >= 2 offsets")
         num_seqs = cu_seqlens.numel() - 1
         nseq = num_seqs
     for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
@@ -310,6 +314,8 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=False
     num_seqs = 0
     if cu_seqlens is not None:
         _check_gpu("cu_seqlens", cu_seqlens, torch.int32, device=q.device)
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be 1-D with num_seqs + 1 >= 2 offsets")
         num_seqs = cu_seqlens.numel() - 1
         nseq = num_seqs
     if initial_state is not None:
