@@ -26,7 +26,8 @@
 //    Gamma * Q K^T;
 //  * consumer wave 4 + c owns state columns [16c, 16c+16) for all d_k rows in
 //    MFMA accumulators and, for chunk u: the inverse T_cc of M's diagonal block
-//    c (fp32, shared with the other consumers through LDS), K S and
+//    c (fp32 MFMA products of the nilpotent factorisation, shared with the other
+//    consumers through LDS), K S and
 //    O = gamma Q S, R = beta (V - gamma K S), then the 16-token block forward
 //    substitution U_p = T_pp (R_p - sum_{r<p} M_pr U_r) (M^{-1} is never
 //    formed), O += P U, and the state update.
@@ -374,25 +375,39 @@ __global__ __launch_bounds__(512, 1) void gdn_chunk_fwd_kernel(GdnParams prm) {
     unsigned short* og = reinterpret_cast<unsigned short*>(prm.o) + rowbase * DV + vcol0 + cw * 16;
 
     auto consume = [&](BufT& B, int u) __attribute__((always_inline)) {
-      // ---- inverse of diagonal block cw of M, one row per lane, fp32:
-      // T (I + L) = I, so row i of T from its last column to its first is
-      // T[i][c] = [c == i] - sum_{j > c} T[i][j] L[j][c], L[j][c] = mdt[cw][c][j] ----
+      // ---- inverse of diagonal block cw of M, fp32: M's diagonal block is I + L
+      // with L strictly lower (16 x 16), hence nilpotent, so
+      // (I + L)^-1 = (I - L)(I + L^2)(I + L^4)(I + L^8), eight 16 x 16 x 16
+      // products on the 16x16x4 fp32 MFMA.  For a product X Y the operands are
+      // X^T and Y as they sit in accumulator layout (lane (gq, m), value s: row
+      // 4gq + s, column m): product step s and lane group gq contract index
+      // 4gq + s.  L[j][c] = mdt[cw][c][j]. ----
       {
-        const int i = m;
-        float t[16];
+        auto prod = [&](const f32x4& xt, const f32x4& y) __attribute__((always_inline)) {
+          f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 15; c >= 0; --c) {
-          float acc = (c == i) ? 1.f : 0.f;
+          for (int s = 0; s < 4; ++s) d = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[s], y[s], d, 0, 0, 0);
+          return d;
+        };
+        const float4 l4 = *reinterpret_cast<const float4*>(&B.mdt[cw][m][4 * gq]);
+        const f32x4 Lc = f32x4{l4.x, l4.y, l4.z, l4.w};   // L
+        f32x4 LTc, Ic;                                      // L^T, I
 #pragma unroll
-          for (int j = 15; j > c; --j) acc -= t[j] * B.mdt[cw][c][j];
-          t[c] = acc;
+        for (int s = 0; s < 4; ++s) {
+          LTc[s] = B.mdt[cw][4 * gq + s][m];
+          Ic[s] = (4 * gq + s == m) ? 1.f : 0.f;
         }
-        if (gq == 0) {
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4)
-            *reinterpret_cast<uint2*>(&B.tinv[cw][i][4 * c4]) =
-                uint2{pack_bf16x2(t[4 * c4], t[4 * c4 + 1]), pack_bf16x2(t[4 * c4 + 2], t[4 * c4 + 3])};
-        }
+        const f32x4 L2 = prod(LTc, Lc), L2T = prod(Lc, LTc);
+        const f32x4 L4 = prod(L2T, L2), L4T = prod(L2, L2T);
+        const f32x4 L8 = prod(L4T, L4);
+        // T^T = (I + L^8)^T (I + L^4)^T (I + L^2)^T (I - L)^T, from the right
+        f32x4 z = Ic - LTc;
+        z = prod(Ic + L2, z);
+        z = prod(Ic + L4, z);
+        z = prod(Ic + L8, z);
+        // z is T^T in accumulator layout: lane (gq, m) holds T[m][4gq .. 4gq + 3]
+        *reinterpret_cast<uint2*>(&B.tinv[cw][m][4 * gq]) =
+            uint2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
       }
       // ---- K S (tokens x columns), then R ----
       f32x4 r_acc[4], o_acc[4];
