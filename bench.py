@@ -27,9 +27,7 @@ METRIC = "GLA fwd tokens/s + TFLOP/s (% MFMA peak), B8 H16 T2048 d128 bf16"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "sub_quadratic_sequence_amd", "csrc", "chunk_fwd_pipe.hip")
-STEP_SRC = os.path.join(ROOT, "sub_quadratic_sequence_amd", "csrc", "recurrent_step.hip")
-GDN_SRC = os.path.join(ROOT, "sub_quadratic_sequence_amd", "csrc", "gdn_fwd.hip")
+CSRC = os.path.join(ROOT, "sub_quadratic_sequence_amd", "csrc")
 
 
 def log(*a):
@@ -81,14 +79,24 @@ def decode_work(N, H, dk, dv, esz):
     return units * 5 * dk * dv, units * (8 * dk * dv + esz * (3 * dk + 2 * dv))
 
 
-def sha256(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def sources_sha256(csrc=None, header=None):
+    """One digest over every source a launch depends on: the HIP kernels, their
+    device headers and host-side dispatch (csrc/*.hip, csrc/*.h) and the C
+    header, each file's name and bytes in name order."""
+    csrc = csrc or CSRC
+    header = header or os.path.join(ROOT, "include", "gla.h")
+    h = hashlib.sha256()
+    files = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
+    for p in [os.path.join(csrc, f) for f in files] + [header]:
+        h.update(os.path.basename(p).encode() + b"\0")
+        with open(p, "rb") as f:
+            h.update(f.read())
+        h.update(b"\0")
+    return h.hexdigest()
 
 
-def read_traffic(name, src):
-    """HBM traffic per launch measured by rocprofv3 PMC counters, from the
-    committed summary, if it was taken on the current kernel source."""
+def read_summary(name):
+    """key = value lines of a committed profile summary (None if absent)."""
     path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
@@ -98,7 +106,15 @@ def read_traffic(name, src):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != sha256(src):
+    return kv
+
+
+def read_traffic(name):
+    """HBM traffic per launch measured by rocprofv3 PMC counters, from the
+    committed summary, if it was taken on the current sources (null otherwise:
+    the counters describe another build)."""
+    kv = read_summary(name)
+    if kv is None or kv.get("sources_sha256") != sources_sha256():
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -130,14 +146,20 @@ def time_launches(fn, steps, warmup, torch, preroll_s=0.0):
     return (t1 - t0) / steps, ev0.elapsed_time(ev1) / 1e3 / steps
 
 
-def per_launch(fn, n, torch, flush=None):
-    """Per-launch HIP-event times (s) of n calls of fn.  With `flush` (a device
-    buffer larger than the last-level cache), the buffer is overwritten before
-    each call, so every call starts with its inputs evicted from that cache."""
+def per_launch(fn, n, torch, flush=None, dirty=False):
+    """Per-launch HIP-event times (s) of n calls of fn.  With `flush` (an int32
+    device buffer four times the size of the 256 MB last-level cache), the buffer
+    is read before each call, so that every call starts with its inputs evicted
+    from that cache; with dirty=True it is overwritten instead, which also leaves
+    the cache full of modified lines that must be written back while the call
+    runs."""
     evs = []
     for i in range(n):
         if flush is not None:
-            flush.fill_(i & 0xFF)
+            if dirty:
+                flush.fill_(i)
+            else:
+                flush.sum()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -165,14 +187,15 @@ def bench_forward(args, torch, gla, inputs):
     flops, nbytes = fwd_work(w.B, w.H, w.T, w.dk, w.dv, 64, 2)
     # launch-time distribution, warm and with the 256 MB last-level cache evicted
     # by a 1 GiB fill before each launch (outside the timed steps above)
-    warm = cold = [gpu]
+    warm = cold = dirty = [gpu]
     if args.only != "pmc":   # counter runs keep to the timed launches
         warm = per_launch(step, 50, torch)
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        flush = torch.zeros(1 << 28, dtype=torch.int32, device=dev)
         cold = per_launch(step, 20, torch, flush)
+        dirty = per_launch(step, 20, torch, flush, dirty=True)
         del flush
     return dict(w=w, d=d, wall=wall, gpu=gpu, flops=flops, bytes=nbytes, tokens=w.B * w.T,
-                warm=warm, cold=cold)
+                warm=warm, cold=cold, dirty=dirty)
 
 
 def bench_decode(args, torch, gla, inputs):
@@ -191,25 +214,38 @@ def bench_decode(args, torch, gla, inputs):
         it[0] += 1
 
     wall, gpu = time_launches(step, w.steps, min(args.warmup, w.steps), torch)
-    # cold variant: evict the state from the 256 MB last-level cache between steps
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    evs = []
-    for t in range(w.steps):
-        flush.fill_(t & 0xFF)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        gla.gla_recurrent_step(q[t], k[t], v[t], g[t], st, out=o)
-        e1.record()
-        evs.append((e0, e1))
-    torch.cuda.synchronize()
-    cold = sum(a.elapsed_time(b) for a, b in evs) / 1e3 / w.steps
+    flops, nbytes = decode_work(w.N, w.H, w.dk, w.dv, 2)
+    if args.pmc:   # counter runs keep to the timed steps
+        return dict(w=w, wall=wall, gpu=gpu, flops=flops, bytes=nbytes)
+    # cold variants: the state evicted from the 256 MB last-level cache before every
+    # step, by reading a 1 GiB buffer (clean eviction) or by overwriting it (dirty)
+    flush = torch.zeros(1 << 28, dtype=torch.int32, device=dev)
+
+    def cold_run(dirty):
+        evs = []
+        for t in range(w.steps):
+            if dirty:
+                flush.fill_(t)
+            else:
+                flush.sum()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            gla.gla_recurrent_step(q[t], k[t], v[t], g[t], st, out=o)
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) / 1e3 for a, b in evs)
+
+    cold_steps = cold_run(False)
+    dirty_steps = cold_run(True)
+    cold = sum(cold_steps) / w.steps
     # reference for a read-modify-write stream of the state's size: a device copy of
     # the same number of bytes (read once, written once), after the same eviction
     src = torch.empty_like(st)
     cps = []
     for t in range(8):
-        flush.fill_(t & 0xFF)
+        flush.sum()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -220,8 +256,9 @@ def bench_decode(args, torch, gla, inputs):
     copy_t = sum(a.elapsed_time(b) for a, b in cps) / 1e3 / len(cps)
     copy_gbs = 2 * st.numel() * 4 / copy_t / 1e9
     del src, flush
-    flops, nbytes = decode_work(w.N, w.H, w.dk, w.dv, 2)
-    return dict(w=w, wall=wall, gpu=gpu, cold=cold, flops=flops, bytes=nbytes, copy_gbs=copy_gbs)
+    return dict(w=w, wall=wall, gpu=gpu, cold=cold, cold_median=cold_steps[len(cold_steps) // 2],
+                cold_min=cold_steps[0], dirty_median=dirty_steps[len(dirty_steps) // 2],
+                flops=flops, bytes=nbytes, copy_gbs=copy_gbs)
 
 
 def bench_long(args, torch, gla, inputs):
@@ -237,12 +274,13 @@ def bench_long(args, torch, gla, inputs):
     o = torch.empty(w.B, w.H, w.T, w.dv, dtype=torch.bfloat16, device=dev)
     sf = torch.empty(w.B, w.H, w.dk, w.dv, dtype=torch.float32, device=dev)
     ws = torch.empty(gla.workspace_size(q, v) + 256, dtype=torch.uint8, device=dev)
-    res = {}
-    for split in (True, False):
+    res = {False: None}
+    for split in ((True,) if args.pmc else (True, False)):
         def step():
             gla.gla_chunk_fwd(q, k, v, g, initial_state=s0, out=o, final_state=sf, split=split,
                               workspace=ws)
-        _, t = time_launches(step, 10, 2, torch, 0.3)
+        _, t = time_launches(step, 3 if args.pmc else 10, 1 if args.pmc else 2, torch,
+                             0.0 if args.pmc else 0.3)
         res[split] = t
     flops, nbytes = fwd_work(w.B, w.H, w.T, w.dk, w.dv, 64, 2)
     nbytes += w.B * w.H * w.dk * w.dv * 4          # the initial state is read too
@@ -265,7 +303,8 @@ def bench_varlen(args, torch, gla, inputs):
     def step():
         gla.gla_chunk_fwd(q, k, v, g, cu_seqlens=cu, out=o, final_state=sf)
 
-    _, t = time_launches(step, 20, 3, torch, 0.3)
+    _, t = time_launches(step, 3 if args.pmc else 20, 1 if args.pmc else 3, torch,
+                         0.0 if args.pmc else 0.3)
     flops, nbytes = fwd_work(1, w.H, T, w.dk, w.dv, 64, 2)
     nbytes += (nseq - 1) * w.H * w.dk * w.dv * 4   # one final state per sequence
     return dict(w=w, t=t, flops=flops, bytes=nbytes, tokens=T)
@@ -316,35 +355,70 @@ def bench_gdn(args, torch, gla, inputs):
     if not args.no_cpu_baseline:
         from oracle import gdn as ogdn
 
-        threads = min(16, os.cpu_count() or 1)
+        threads = host_threads()
         el, runs, used = 0.0, 0, 0
-        while el < 3.0 and runs < 8 * w.B:   # whole sequences, cycling through the batch
-            b = runs % w.B
+        per = w.B if threads > w.H else 1   # whole batch per call when the heads alone leave threads idle
+        while el < 3.0 and runs < 8 * w.B // per:   # cycling through the batch
+            b = (runs * per) % w.B
             t0 = time.perf_counter()
-            _, _, used = ogdn.recurrence(d["q"][b:b + 1], d["k"][b:b + 1], d["v"][b:b + 1],
-                                         d["g"][b:b + 1], d["beta"][b:b + 1], nthreads=threads,
+            _, _, used = ogdn.recurrence(d["q"][b:b + per], d["k"][b:b + per], d["v"][b:b + per],
+                                         d["g"][b:b + per], d["beta"][b:b + per], nthreads=threads,
                                          return_threads=True)
             el += time.perf_counter() - t0
             runs += 1
-        res["oracle"] = {"value": runs * w.T / el, "unit": "tokens/s", "cores": used, "kind": "oracle",
-                         "sample": f"{runs} sequence runs x {w.H} heads x {w.T} tokens of the same "
-                                   "batch (fp64 GDN token recurrence, OpenMP over heads)",
-                         "seconds": round(el, 3)}
+        res["oracle"] = {"value": runs * per * w.T / el, "unit": "tokens/s", "cores": used,
+                         "kind": "oracle",
+                         "sample": f"{runs} calls x {per} sequences x {w.H} heads x {w.T} tokens of "
+                                   "the same batch (fp64 GDN token recurrence, OpenMP over units)",
+                         "seconds": round(el, 3), "host": host_info()}
     return res
 
 
-def _time_oracle(oracle, w, d, threads, min_seconds, max_runs):
-    """Whole sequences of the batch through the fp64 oracle, cycling through the
-    batch, until at least min_seconds of oracle time (and one sequence) have passed."""
+def host_threads():
+    """CPU threads this process may use: the CPUs it is allowed to run on,
+    capped by OMP_NUM_THREADS when the environment sets it (the host's share
+    of CPUs for this job)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def host_info():
+    """The host CPU model and counts, reported beside the oracle's rate."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"cpu_model": model, "host_cpus": os.cpu_count(), "cpus_allowed": affinity,
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
+
+
+def _time_oracle(oracle, w, d, threads, min_seconds, max_runs, per_call):
+    """Groups of per_call whole sequences of the batch (all heads) through the
+    fp64 oracle, cycling through the batch, until at least min_seconds of
+    oracle time (and one call) have passed."""
     done_tokens, elapsed, used, n = 0, 0.0, 0, 0
     while (elapsed < min_seconds or n == 0) and n < max_runs:
-        b = n % w.B
-        sl = slice(b, b + 1)
+        b = (n * per_call) % w.B
+        sl = slice(b, b + per_call)
         t0 = time.perf_counter()
         _, _, used = oracle.recurrence(d["q"][sl], d["k"][sl], d["v"][sl], d["g"][sl],
                                        nthreads=threads, return_threads=True)
         elapsed += time.perf_counter() - t0
-        done_tokens += w.T
+        done_tokens += w.T * per_call
         n += 1
     return done_tokens, elapsed, used, n
 
@@ -357,16 +431,17 @@ def cpu_baseline(fwd, min_seconds=12.0, max_passes=64, one_thread_seconds=3.0):
     import oracle
 
     w, d = fwd["w"], fwd["d"]
-    threads = min(16, os.cpu_count() or 1)
+    threads = host_threads()
     oracle.build(force=False)
+    # the whole batch per call (B x H independent units), so every thread has work
     done_tokens, elapsed, used, n = _time_oracle(oracle, w, d, threads, min_seconds,
-                                                 max_passes * w.B)
-    sample = (f"{n} sequence runs ({n / w.B:.2f} passes over the {w.B}-sequence batch) x {w.H} "
-              f"heads x {w.T} tokens of the same workload (fp64 token recurrence, OpenMP over "
-              f"heads, final state kept)")
-    t1, e1, u1, n1 = _time_oracle(oracle, w, d, 1, one_thread_seconds, max_passes * w.B)
+                                                 max_passes, w.B)
+    sample = (f"{n} passes over the whole batch ({w.B} sequences x {w.H} heads x {w.T} tokens) of "
+              f"the same workload (fp64 token recurrence, OpenMP over the {w.B * w.H} units, "
+              f"final state kept)")
+    t1, e1, u1, n1 = _time_oracle(oracle, w, d, 1, one_thread_seconds, max_passes * w.B, 1)
     return {"value": done_tokens / elapsed, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": sample, "seconds": round(elapsed, 3),
+            "sample": sample, "seconds": round(elapsed, 3), "host": host_info(),
             "one_thread": {"value": t1 / e1, "unit": "tokens/s", "cores": u1,
                            "sample": f"{n1} sequence runs x {w.H} heads x {w.T} tokens",
                            "seconds": round(e1, 3)}}
@@ -386,11 +461,11 @@ def main():
                     help="skip the long-context and packed-sequence legs")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-gdn", action="store_true", help="skip the Gated DeltaNet leg")
-    ap.add_argument("--only", choices=["fwd", "decode", "long", "bwd", "gdn", "copy", "pmc", "gdnpmc"],
+    ap.add_argument("--only", choices=["fwd", "decode", "long", "bwd", "gdn", "copy", "pmc"],
                     default=None,
                     help="profiling runs: launch only this part (copy = 512 MiB calibration "
-                         "copy; pmc = copy, then forward, then decode, a few launches each; "
-                         "gdnpmc = copy, then a few Gated DeltaNet launches)")
+                         "copy; pmc = copy, then a few launches of every leg: forward, decode, "
+                         "long context split, packed sequences, backward, Gated DeltaNet)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -403,7 +478,8 @@ def main():
     from sub_quadratic_sequence_amd import gla, inputs
 
     gla.load_library()
-    if args.only in ("copy", "pmc", "gdnpmc"):
+    args.pmc = args.only == "pmc"
+    if args.only in ("copy", "pmc"):
         src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)
         for _ in range(5):
@@ -413,15 +489,17 @@ def main():
         log("[bench] copy calibration: 5 x 512 MiB device-to-device copies done")
         if args.only == "copy":
             return
+        # a few launches of every leg, in order: forward, decode, long context (split),
+        # packed sequences, backward, Gated DeltaNet
         args.steps, args.warmup, args.preroll = 5, 1, 0.0
-        if args.only == "gdnpmc":
-            args.no_cpu_baseline = True
-            args.steps = 10
-            bench_gdn(args, torch, gla, inputs)
-            log("[bench] gdn pmc launches done")
-            return
+        args.no_cpu_baseline = True
         bench_forward(args, torch, gla, inputs)
         bench_decode(args, torch, gla, inputs)
+        bench_long(args, torch, gla, inputs)
+        bench_varlen(args, torch, gla, inputs)
+        args.steps = 12   # the backward and GDN legs run steps/4 and steps/2 launches
+        bench_backward(args, torch, gla, inputs)
+        bench_gdn(args, torch, gla, inputs)
         log("[bench] pmc launches done")
         return
     if args.only == "long":
@@ -451,7 +529,7 @@ def main():
         f"warm, {fwd['cold'][len(fwd['cold']) // 2] * 1e6:.1f} us with the last-level cache evicted")
     if args.only == "fwd":
         return
-    traffic = read_traffic("chunk_fwd_b8h16t2048d128_bf16_traffic.txt", KERNEL_SRC)
+    traffic = read_traffic("chunk_fwd_b8h16t2048d128_bf16_traffic.txt")
     out = {
         "metric": METRIC,
         "value": fwd["tokens"] / fwd["wall"],
@@ -481,7 +559,12 @@ def main():
             "cold_llc_median": fwd["cold"][len(fwd["cold"]) // 2] * 1e6,
             "cold_llc_min": fwd["cold"][0] * 1e6,
             "cold_llc_frac_of_hbm": fwd["bytes"] / fwd["cold"][len(fwd["cold"]) // 2] / 1e9 / HBM_PEAK_GBS,
-            "note": "per-launch HIP events, 50 warm launches; 20 launches each after a 1 GiB fill"},
+            "cold_dirty_llc_median": fwd["dirty"][len(fwd["dirty"]) // 2] * 1e6,
+            "cold_dirty_llc_min": fwd["dirty"][0] * 1e6,
+            "note": "per-launch HIP events: 50 warm launches; 20 launches each after reading a 1 GiB "
+                    "buffer (cold_llc: inputs evicted from the 256 MB last-level cache, which holds "
+                    "clean lines); 20 launches each after overwriting it (cold_dirty_llc: the cache "
+                    "also holds 256 MB of modified lines written back during the launch)"},
     }
     if not args.no_decode:
         dec = bench_decode(args, torch, gla, inputs)
@@ -492,11 +575,14 @@ def main():
         out["decode"] = {
             "workload": dec["w"].name, "tokens_per_s": dec["w"].N / dec["wall"],
             "us_per_step": dec["gpu"] * 1e6, "us_per_step_cold_llc": dec["cold"] * 1e6,
+            "us_per_step_cold_llc_median": dec["cold_median"] * 1e6,
+            "us_per_step_cold_llc_min": dec["cold_min"] * 1e6,
+            "us_per_step_cold_dirty_llc_median": dec["dirty_median"] * 1e6,
             "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": dgbs / HBM_PEAK_GBS, "achieved_cold_llc": cgbs,
                          "frac_cold_llc": cgbs / HBM_PEAK_GBS,
                          "device_copy_same_bytes_cold_gbs": dec["copy_gbs"],
-                         "traffic": read_traffic("recurrent_step_n256h16d128_bf16_traffic.txt", STEP_SRC),
+                         "traffic": read_traffic("recurrent_step_n256h16d128_bf16_traffic.txt"),
                          "kernel": "gla::recurrent_step_kernel<128, 128, BF16>",
                          "algorithmic_bytes_per_launch": dec["bytes"]},
         }
@@ -551,7 +637,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": gd["bytes"],
                          "algorithmic_flops_per_call": gd["flops"],
-                         "traffic": read_traffic("gdn_fwd_b8h16t2048d128_bf16.txt", GDN_SRC),
+                         "traffic": read_traffic("gdn_fwd_b8h16t2048d128_bf16.txt"),
                          "kernel": "gla::gdn_chunk_fwd_kernel<128>"},
         }
         if "oracle" in gd:

@@ -158,6 +158,11 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
   constexpr int NWR = CPL / 2;   // 32-bit words per lane per token (q, k, g)
 
   __shared__ __attribute__((aligned(256))) BufT bufs[2];
+  // outputs of the 64-column full pass go out through LDS, so that every global
+  // store instruction writes whole 128-byte rows: chunk u's [token][column] bf16
+  // tile in ostage[u & 1], its 8-byte units XOR-permuted by the row
+  constexpr bool OSTAGE = FULL && NT == 1;
+  __shared__ __attribute__((aligned(256))) unsigned short ostage[OSTAGE ? 2 : 1][OSTAGE ? C * 64 : 4];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, m = lane & 15, gq = lane >> 4;
@@ -846,14 +851,14 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
           }
         }
         if constexpr (NT == 1) {
-          const long t0 = bos + (long)u * C;
+          // token 16p + m, columns 16cw + 4gq .. +3: 8-byte unit 4cw + gq of the row
+          unsigned so = (unsigned)(m * 128 + (((4 * cw + gq) ^ m) << 3));
+          launder(so);
+          char* const ob = reinterpret_cast<char*>(ostage[u & 1]);
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const long tk = t0 + 16 * p + m;
-            if (tk < eos)
-              store4<BF16>(og + tk * DV + cw * 16 + gq * 4, oacc[0][p][0], oacc[0][p][1], oacc[0][p][2],
-                           oacc[0][p][3]);
-          }
+          for (int p = 0; p < 4; ++p)
+            *reinterpret_cast<uint2*>(ob + so + p * 16 * 128) =
+                uint2{pack_bf16x2(oacc[0][p][0], oacc[0][p][1]), pack_bf16x2(oacc[0][p][2], oacc[0][p][3])};
         }
       }
 
@@ -912,11 +917,31 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         }
       }
     };
+    // staged outputs of chunk u: wave cw stores rows 16cw .. 16cw+15, 8 rows of
+    // 128 bytes per instruction
+    auto flush_out = [&](int u) __attribute__((always_inline)) {
+      const char* const ob = reinterpret_cast<const char*>(ostage[u & 1]);
+      const int j = lane & 7;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int r = 16 * cw + 8 * hh + (lane >> 3);
+        // 8-byte units 2j and 2j + 1 of row r sit in the 16-byte block j ^ ((r & 15) >> 1),
+        // in swapped order when r is odd
+        const uint4 x = *reinterpret_cast<const uint4*>(ob + r * 128 + ((j ^ ((r & 15) >> 1)) << 4));
+        const bool sw = r & 1;
+        const uint4 y = sw ? uint4{x.z, x.w, x.x, x.y} : x;
+        const long tk = bos + (long)u * C + r;
+        if (tk < eos) *reinterpret_cast<uint4*>(og + tk * DV + 8 * j) = y;
+      }
+    };
     using T_ = std::integral_constant<bool, true>;
     using F_ = std::integral_constant<bool, false>;
     for (int i = 0; i <= nch; ++i) {
       if (i > 0) {
         const int u = i - 1;
+        if constexpr (OSTAGE) {
+          if (u > 0) flush_out(u - 1);
+        }
         const BufT& B = bufs[u & 1];
         const int fl = B.flag[0] | B.flag[1] | B.flag[2] | B.flag[3];
         if (fl == 0)
@@ -927,6 +952,9 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
           consume(B, u, T_{}, T_{});
       }
       barrier_lds();
+    }
+    if constexpr (OSTAGE) {
+      if (nch > 0) flush_out(nch - 1);
     }
     if (s_out) {
 #pragma unroll

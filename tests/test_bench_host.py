@@ -12,9 +12,9 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
 TRAFFIC_SUMMARIES = [
-    ("chunk_fwd_b8h16t2048d128_bf16_traffic.txt", bench.KERNEL_SRC),
-    ("recurrent_step_n256h16d128_bf16_traffic.txt", bench.STEP_SRC),
-    ("gdn_fwd_b8h16t2048d128_bf16.txt", bench.GDN_SRC),
+    "chunk_fwd_b8h16t2048d128_bf16_traffic.txt",
+    "recurrent_step_n256h16d128_bf16_traffic.txt",
+    "gdn_fwd_b8h16t2048d128_bf16.txt",
 ]
 
 
@@ -45,11 +45,11 @@ def test_bench_refuses_a_multi_rank_launch():
     assert "WORLD_SIZE=2" in r.stderr
 
 
-@pytest.mark.parametrize("name,src", TRAFFIC_SUMMARIES)
-def test_traffic_summaries_are_well_formed(name, src):
+@pytest.mark.parametrize("name", TRAFFIC_SUMMARIES)
+def test_traffic_summaries_are_well_formed(name):
     kv = _fields(os.path.join(bench.PROFILES, name))
     for key in ("kernel", "fetch_size_kib_per_dispatch", "write_size_kib_per_dispatch",
-                "fetch_scale", "write_scale", "kernel_source_sha256", "hbm_bytes_per_launch",
+                "fetch_scale", "write_scale", "sources_sha256", "hbm_bytes_per_launch",
                 "algorithmic_bytes_per_launch", "traffic_over_algorithmic"):
         assert key in kv, key
     fetch = float(kv["fetch_size_kib_per_dispatch"]) * float(kv["fetch_scale"])
@@ -62,21 +62,29 @@ def test_traffic_summaries_are_well_formed(name, src):
     # the counters can only read at least the bytes the kernel must move, and far
     # more would mean a mis-scaled calibration
     assert 0.99 < ratio < 1.5
-    assert len(kv["kernel_source_sha256"]) == 64
+    assert len(kv["sources_sha256"]) == 64
 
 
-def test_read_traffic_follows_the_kernel_source(tmp_path):
-    src = tmp_path / "k.hip"
-    src.write_text("// kernel v1\n")
-    prof = tmp_path / "p.txt"
-    prof.write_text("# header = ignored\nkernel_source_sha256 = %s\nhbm_bytes_per_launch = 1234\n"
-                    % bench.sha256(str(src)))
-    old = bench.PROFILES
+@pytest.mark.parametrize("changed", ["kernel.hip", "dispatch.h", "gla.h"])
+def test_read_traffic_follows_every_source(tmp_path, changed):
+    csrc = tmp_path / "csrc"
+    csrc.mkdir()
+    (csrc / "kernel.hip").write_text("// kernel v1\n")
+    (csrc / "dispatch.h").write_text("// header v1\n")
+    (tmp_path / "gla.h").write_text("// abi v1\n")
+    old = (bench.PROFILES, bench.CSRC, bench.ROOT)
     try:
-        bench.PROFILES = str(tmp_path)
-        assert bench.read_traffic("p.txt", str(src)) == 1234.0
-        src.write_text("// kernel v2\n")   # the source changed since the counters were taken
-        assert bench.read_traffic("p.txt", str(src)) is None
-        assert bench.read_traffic("missing.txt", str(src)) is None
+        bench.PROFILES, bench.CSRC, bench.ROOT = str(tmp_path), str(csrc), str(tmp_path)
+        header = str(tmp_path / "gla.h")
+        os.makedirs(tmp_path / "include", exist_ok=True)
+        os.replace(header, tmp_path / "include" / "gla.h")
+        digest = bench.sources_sha256()
+        (tmp_path / "p.txt").write_text(
+            "# header = ignored\nsources_sha256 = %s\nhbm_bytes_per_launch = 1234\n" % digest)
+        assert bench.read_traffic("p.txt") == 1234.0
+        path = tmp_path / "include" / "gla.h" if changed == "gla.h" else csrc / changed
+        path.write_text(path.read_text() + "// changed\n")   # a source changed since the counters
+        assert bench.read_traffic("p.txt") is None
+        assert bench.read_traffic("missing.txt") is None
     finally:
-        bench.PROFILES = old
+        bench.PROFILES, bench.CSRC, bench.ROOT = old
