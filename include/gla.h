@@ -24,7 +24,8 @@
  *   - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent) owned
  *     by the caller; the library keeps no pointer after the call returns and
  *     allocates no device memory.  Only gla_chunk_fwd_ws and gla_chunk_bwd
- *     take a workspace, which the caller allocates.
+ *     take a workspace, which the caller allocates; gla_chunk_fwd_noalloc uses
+ *     a scratch array the library holds (see there).
  *   - Layouts are row-major, last index fastest, densely packed, and every
  *     tensor pointer must be 16-byte aligned.
  *   - dtype selects the element type of q, k, v, g and o: GLA_BF16 (bfloat16)
@@ -126,6 +127,38 @@ int gla_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* g,
                      const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk,
                      int dv, int chunk_size, int dtype, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/* Size, in bytes, of the scratch array behind gla_chunk_fwd_noalloc. */
+#define GLA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * gla_chunk_fwd_ws for callers that cannot allocate device memory and cannot
+ * bring a workspace: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.  The same plan, kernels and results as
+ * gla_chunk_fwd_ws, bitwise; the split's scratch (segment states and decays)
+ * lives in a file-scope device array of GLA_NOALLOC_SCRATCH_BYTES owned by the
+ * library, one copy per device, held from the library's load until the process
+ * ends.  The call itself allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine); its first call on a device looks the array's device address
+ * up once (hipGetSymbolAddress).
+ *
+ * Every call on one device shares that device's array, and the kernels of one
+ * call use it until they complete: calls that overlap on one device (on
+ * different streams, or from different threads without ordering) race and give
+ * wrong results.  Calls on one stream are ordered and safe.  The array keeps the
+ * last call's contents; no call depends on them (every element a call reads, an
+ * earlier kernel of the same call wrote).
+ *
+ * Arguments, layouts and errors as for gla_chunk_fwd.  Shapes whose split would
+ * need more scratch than GLA_NOALLOC_SCRATCH_BYTES (the sizes of
+ * gla_chunk_fwd_workspace_size) give GLA_ERR_INVALID_ARG with nothing enqueued;
+ * shapes that run unsplit need none.  A failed address lookup gives
+ * GLA_ERR_LAUNCH.
+ */
+int gla_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* g,
+                          const float* initial_state, void* o, float* final_state,
+                          const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk,
+                          int dv, int chunk_size, int dtype, void* stream);
 
 /*
  * Device workspace, in bytes, that gla_chunk_bwd needs for this shape (the bf16

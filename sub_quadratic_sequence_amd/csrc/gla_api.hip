@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "gla.h"
 #include "gla_kernels.h"
@@ -186,6 +187,71 @@ size_t split_bytes(long long units, int nseg, int dk, int dv) {
   return ((st + 255) / 256) * 256 + ((dec + 255) / 256) * 256;
 }
 
+// The three kernels of a split forward (prm filled by check_chunk_args; nseg > 1)
+// with the segment states and decays in ws (split_bytes(...) bytes, 256-aligned).
+int run_split(const char* fn, gla::ChunkParams& prm, long long units, int nseg, int seg_len,
+              int dk, int dv, int dtype, const float* initial_state, float* final_state, char* ws,
+              hipStream_t s) {
+  const long long nblocks = units * nseg * prm.nvt;
+  if (!fits_i32(nblocks)) return fail(GLA_ERR_INVALID_ARG, "%s: %lld work items", fn, nblocks);
+  const size_t st_bytes = ((size_t)units * nseg * dk * dv * sizeof(float) + 255) / 256 * 256;
+  prm.nseg = nseg;
+  prm.seg_len = seg_len;
+  prm.seg_state = reinterpret_cast<float*>(ws);
+  prm.seg_decay = reinterpret_cast<float*>(ws + st_bytes);
+  prm.xcd_remap = (nblocks % 8 == 0) ? 1 : 0;
+  // 1. each segment's state from zero and its total decay
+  int rc = gla::launch_chunk_fwd_pipe(prm, dk, true, (int)nblocks, s);
+  if (rc != 0) return launch_status(fn, rc, dk, dtype);
+  // 2. incoming state of every segment, and the final states
+  gla::SegScanParams sp;
+  sp.s0 = initial_state;
+  sp.sT = final_state;
+  sp.seg_state = prm.seg_state;
+  sp.seg_decay = prm.seg_decay;
+  sp.dk = dk;
+  sp.dv = dv;
+  sp.nseg = nseg;
+  sp.reverse = 0;
+  rc = gla::launch_seg_scan(sp, (int)units, s);
+  if (rc != 0) return launch_status(fn, rc, dk, dtype);
+  // 3. the forward pass of every segment from its incoming state
+  rc = gla::launch_chunk_fwd_pipe(prm, dk, false, (int)nblocks, s);
+  return launch_status(fn, rc, dk, dtype);
+}
+
+// Library-owned scratch of gla_chunk_fwd_noalloc: one copy per device, alive
+// until the process ends.  In host code `scratch` only names the symbol; the
+// device address comes from hipGetSymbolAddress, looked up once per device.
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+static_assert(kNoallocScratchBytes == GLA_NOALLOC_SCRATCH_BYTES, "gla.h states the scratch size");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (nullptr with the message set).
+void* scratch_for_current_device(const char* fn) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    fail(GLA_ERR_LAUNCH, "%s: no current HIP device (or device index >= %d)", fn, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      fail(GLA_ERR_LAUNCH, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", fn, dev,
+           hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -249,34 +315,43 @@ int gla_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* g,
                 workspace ? workspace_bytes : (size_t)0, need);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(GLA_ERR_INVALID_ARG, "gla_chunk_fwd_ws: workspace is not 256-byte aligned");
-  const long long nblocks = units * nseg * prm.nvt;
-  if (!fits_i32(nblocks))
-    return fail(GLA_ERR_INVALID_ARG, "gla_chunk_fwd_ws: %lld work items", nblocks);
-  char* ws = static_cast<char*>(workspace);
-  const size_t st_bytes = ((size_t)units * nseg * dk * dv * sizeof(float) + 255) / 256 * 256;
-  prm.nseg = nseg;
-  prm.seg_len = seg_len;
-  prm.seg_state = reinterpret_cast<float*>(ws);
-  prm.seg_decay = reinterpret_cast<float*>(ws + st_bytes);
-  prm.xcd_remap = (nblocks % 8 == 0) ? 1 : 0;
-  // 1. each segment's state from zero and its total decay
-  int rc = gla::launch_chunk_fwd_pipe(prm, dk, true, (int)nblocks, s);
-  if (rc != 0) return launch_status("gla_chunk_fwd_ws", rc, dk, dtype);
-  // 2. incoming state of every segment, and the final states
-  gla::SegScanParams sp;
-  sp.s0 = initial_state;
-  sp.sT = final_state;
-  sp.seg_state = prm.seg_state;
-  sp.seg_decay = prm.seg_decay;
-  sp.dk = dk;
-  sp.dv = dv;
-  sp.nseg = nseg;
-  sp.reverse = 0;
-  rc = gla::launch_seg_scan(sp, (int)units, s);
-  if (rc != 0) return launch_status("gla_chunk_fwd_ws", rc, dk, dtype);
-  // 3. the forward pass of every segment from its incoming state
-  rc = gla::launch_chunk_fwd_pipe(prm, dk, false, (int)nblocks, s);
-  return launch_status("gla_chunk_fwd_ws", rc, dk, dtype);
+  return run_split("gla_chunk_fwd_ws", prm, units, nseg, seg_len, dk, dv, dtype, initial_state,
+                   final_state, static_cast<char*>(workspace), s);
+}
+
+int gla_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* g,
+                          const float* initial_state, void* o, float* final_state,
+                          const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk,
+                          int dv, int chunk_size, int dtype, void* stream) {
+  g_last_error[0] = '\0';
+  const char* fn = "gla_chunk_fwd_noalloc";
+  gla::ChunkParams prm;
+  long long units = 0;
+  bool nothing = false;
+  const int st = check_chunk_args(fn, q, k, v, g, initial_state, o, final_state, cu_seqlens,
+                                  num_seqs, B, H, T, dk, dv, chunk_size, dtype, prm, units, nothing);
+  if (st != GLA_OK || nothing) return st;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int seg_len = T;
+  const int nseg = fwd_split_plan(cu_seqlens != nullptr, dtype, units, dv, T, seg_len);
+  if (nseg == 1) {   // no scratch needed: the plain forward
+    choose_slice(prm, units, dtype);
+    const int rc = gla::launch_chunk_fwd(prm, dk, dtype, (int)(units * prm.nvt), s);
+    return launch_status(fn, rc, dk, dtype);
+  }
+  if (dtype == GLA_BF16 && dv % 128 == 0) {   // as in gla_chunk_fwd_ws
+    prm.dvt = 128;
+    prm.nvt = dv / 128;
+  }
+  const size_t need = split_bytes(units, nseg, dk, dv);
+  if (need > kNoallocScratchBytes)
+    return fail(GLA_ERR_INVALID_ARG,
+                "%s: this shape's sequence split needs %zu bytes of scratch, more than the %zu of "
+                "the library's scratch array; use gla_chunk_fwd_ws with a workspace",
+                fn, need, kNoallocScratchBytes);
+  char* ws = static_cast<char*>(scratch_for_current_device(fn));
+  if (!ws) return GLA_ERR_LAUNCH;
+  return run_split(fn, prm, units, nseg, seg_len, dk, dv, dtype, initial_state, final_state, ws, s);
 }
 
 size_t gla_chunk_bwd_workspace_size(int num_seqs, int B, int H, int T, int dk, int dv,

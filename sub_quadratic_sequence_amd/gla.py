@@ -41,6 +41,8 @@ def load_library():
         lib.gla_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P]
         lib.gla_chunk_fwd_workspace_size.restype = ctypes.c_size_t
         lib.gla_chunk_fwd_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
+        lib.gla_chunk_fwd_noalloc.restype = I
+        lib.gla_chunk_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P]
         lib.gla_chunk_fwd_ws.restype = I
         lib.gla_chunk_fwd_ws.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P,
                                          ctypes.c_size_t, P]
@@ -105,7 +107,7 @@ def workspace_size(q, v, cu_seqlens=None, chunk_size: int = 64) -> int:
 
 def gla_chunk_fwd(q, k, v, g, initial_state=None, output_final_state=False, cu_seqlens=None,
                   chunk_size: int = 64, out=None, final_state=None, split: bool = True,
-                  workspace=None):
+                  workspace=None, noalloc: bool = False):
     """Chunkwise GLA forward.
 
     q, k, g: [B, H, T, dk]; v: [B, H, T, dv] (bfloat16 or float32, same dtype);
@@ -118,7 +120,9 @@ def gla_chunk_fwd(q, k, v, g, initial_state=None, output_final_state=False, cu_s
     which cuts long sequences into segments when the inputs have too few
     (sequence, head) units to fill the device; the workspace it needs is a
     torch allocation (or ``workspace``, a uint8 GPU tensor).  ``split=False``
-    calls ``gla_chunk_fwd``, which never splits.
+    calls ``gla_chunk_fwd``, which never splits.  ``noalloc=True`` calls
+    ``gla_chunk_fwd_noalloc`` (the same split, its scratch in the library's own
+    device array; see ``gla_chunk_fwd_noalloc`` below).
     """
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -152,7 +156,9 @@ def gla_chunk_fwd(q, k, v, g, initial_state=None, output_final_state=False, cu_s
         args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(initial_state), _ptr(out),
                 _ptr(final_state), _ptr(cu_seqlens), num_seqs, B, H, T, dk, dv, int(chunk_size),
                 _dtype_code(q))
-        if split:
+        if noalloc:
+            rc = lib.gla_chunk_fwd_noalloc(*args, ctypes.c_void_p(stream))
+        elif split:
             need = workspace_size(q, v, cu_seqlens, chunk_size)
             if need and workspace is None:
                 workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
@@ -168,6 +174,18 @@ def gla_chunk_fwd(q, k, v, g, initial_state=None, output_final_state=False, cu_s
     if rc != GLA_OK:
         raise GLAError(rc, last_error())
     return out, final_state
+
+
+def gla_chunk_fwd_noalloc(q, k, v, g, initial_state=None, output_final_state=False,
+                          cu_seqlens=None, chunk_size: int = 64, out=None, final_state=None):
+    """``gla_chunk_fwd`` through the C entry point ``gla_chunk_fwd_noalloc``: the
+    sequence split of ``gla_chunk_fwd_ws`` with its scratch in a device array the
+    library holds, so the C call allocates nothing.  Pass ``out`` (and
+    ``final_state``) to keep this wrapper from allocating them with torch.  Calls
+    that overlap on one device race on that array."""
+    return gla_chunk_fwd(q, k, v, g, initial_state=initial_state,
+                         output_final_state=output_final_state, cu_seqlens=cu_seqlens,
+                         chunk_size=chunk_size, out=out, final_state=final_state, noalloc=True)
 
 
 def bwd_workspace_size(q, v, cu_seqlens=None, chunk_size: int = 64) -> int:

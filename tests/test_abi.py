@@ -33,8 +33,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     assert names == ["gdn_chunk_fwd", "gla_chunk_bwd", "gla_chunk_bwd_workspace_size", "gla_chunk_fwd",
-                     "gla_chunk_fwd_workspace_size", "gla_chunk_fwd_ws", "gla_last_error",
-                     "gla_recurrent_step", "gla_status_string"]
+                     "gla_chunk_fwd_noalloc", "gla_chunk_fwd_workspace_size", "gla_chunk_fwd_ws",
+                     "gla_last_error", "gla_recurrent_step", "gla_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -61,14 +61,14 @@ def test_status_strings(lib):
 FAKE = 0x10000  # a 16-byte aligned address; never dereferenced (every call below is rejected)
 
 
-def _chunk(lib, **kw):
+def _chunk(lib, entry="gla_chunk_fwd", **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, s0=None, o=FAKE, sT=None, cu=None, num_seqs=0, B=1,
              H=2, T=64, dk=128, dv=128, C=64, dtype=0)
     a.update(kw)
     P = ctypes.c_void_p
-    return lib.gla_chunk_fwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["s0"]), P(a["o"]),
-                             P(a["sT"]), P(a["cu"]), a["num_seqs"], a["B"], a["H"], a["T"],
-                             a["dk"], a["dv"], a["C"], a["dtype"], None)
+    return getattr(lib, entry)(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["s0"]), P(a["o"]),
+                               P(a["sT"]), P(a["cu"]), a["num_seqs"], a["B"], a["H"], a["T"],
+                               a["dk"], a["dv"], a["C"], a["dtype"], None)
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -88,17 +88,20 @@ def _chunk(lib, **kw):
     (dict(cu=FAKE, num_seqs=0), 1, "num_seqs"),
     (dict(B=4096, H=4096, T=4096), 1, "int32"),
 ])
-def test_chunk_fwd_rejects(lib, kw, status, needle):
+@pytest.mark.parametrize("entry", ["gla_chunk_fwd", "gla_chunk_fwd_noalloc"])
+def test_chunk_fwd_rejects(lib, entry, kw, status, needle):
     from sub_quadratic_sequence_amd import gla
 
-    rc = _chunk(lib, **kw)
+    rc = _chunk(lib, entry, **kw)
     assert rc == status
     assert needle in gla.last_error()
+    assert entry in gla.last_error()
 
 
-def test_chunk_fwd_zero_tokens_without_outputs_is_a_noop(lib):
+@pytest.mark.parametrize("entry", ["gla_chunk_fwd", "gla_chunk_fwd_noalloc"])
+def test_chunk_fwd_zero_tokens_without_outputs_is_a_noop(lib, entry):
     # T == 0 and no final state: nothing to do, returns OK without touching the GPU
-    assert _chunk(lib, q=None, k=None, v=None, g=None, o=None, T=0) == 0
+    assert _chunk(lib, entry, q=None, k=None, v=None, g=None, o=None, T=0) == 0
 
 
 @pytest.mark.parametrize("kw,status,needle", [
