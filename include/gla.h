@@ -78,8 +78,8 @@ typedef enum { GLA_BF16 = 0, GLA_F32 = 1 } gla_dtype;
  * restart at each sequence start, and a sequence may be empty (its final state
  * is its initial state).
  *
- * Supported: chunk_size == 64; dk in {64, 128} for GLA_BF16 and dk == 64 for
- * GLA_F32; dv a positive multiple of 64 up to 512.  T >= 0 (T == 0 only writes
+ * Supported: chunk_size == 64; dk in {64, 128}; dv a positive multiple of 64 up
+ * to 512 (both dtypes).  T >= 0 (T == 0 only writes
  * final_state).  B * H * T and all index products must fit in int32 per tensor.
  */
 int gla_chunk_fwd(const void* q, const void* k, const void* v, const void* g,

@@ -120,10 +120,18 @@ __device__ __forceinline__ float clamp_gate(float x) {
 
 template <int DK, typename E>
 __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkParams prm) {
-  using Cfg = ChunkCfg<DK, E>;
+  // The chunk is processed in NH passes of 64 key channels each (DK = 64: one
+  // pass).  Scores and the inter-chunk term are sums over channels, so each
+  // pass adds its channels' share to the same accumulators; the state rows of
+  // a pass's channels are updated in that pass.  P V and the output store
+  // follow the last pass.  The LDS tiles are sized for one pass.
+  constexpr int DKH = 64, NH = DK / DKH;
+  static_assert(DK % DKH == 0, "d_k is a multiple of 64");
+  using Cfg = ChunkCfg<DKH, E>;
   using S = typename E::storage;
-  constexpr int C = Cfg::C, CPL = Cfg::CPL, WCH = Cfg::WCH, KS = Cfg::KS, RB = Cfg::RB;
+  constexpr int C = Cfg::C, CPL = Cfg::CPL, WCH = Cfg::WCH, KS = Cfg::KS;
   constexpr int PQ = Cfg::PQ, PT = Cfg::PT;
+  static_assert(Cfg::RB == 1, "one 16-row state block per wave and pass");
 
   __shared__ __attribute__((aligned(16))) S s_qe[Cfg::SZ_QE];
   __shared__ __attribute__((aligned(16))) S s_kp[Cfg::SZ_KP];
@@ -131,7 +139,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkParams prm) {
   __shared__ __attribute__((aligned(16))) S s_kt[Cfg::SZ_KT];
   __shared__ __attribute__((aligned(16))) S s_vt[Cfg::SZ_VT];
   __shared__ __attribute__((aligned(16))) S s_sb[Cfg::SZ_SB];
-  __shared__ float s_dec[DK];                 // 2^Gamma_last per key channel
+  __shared__ float s_dec[DKH];                // 2^Gamma_last per key channel of the pass
   __shared__ float s_diag[4][4][16][16];      // [sub-chunk][wave][i][j] exact diagonal partials
   __shared__ int s_flag[2][4];
 
@@ -143,16 +151,16 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkParams prm) {
   const int bid = blockIdx.x;
   const int lin = prm.xcd_remap ? (bid & 7) * (nblk >> 3) + (bid >> 3) : bid;
   const int unit = lin / prm.nvt, vt = lin - unit * prm.nvt;
-  const int n = unit / prm.H, h = unit - n * prm.H;
+  const int n = unit / prm.H, hd = unit - n * prm.H;
   long bos, eos, rowbase;
   if (prm.cu) {
     bos = prm.cu[n];
     eos = prm.cu[n + 1];
-    rowbase = (long)h * prm.T;
+    rowbase = (long)hd * prm.T;
   } else {
     bos = 0;
     eos = prm.T;
-    rowbase = ((long)n * prm.H + h) * prm.T;
+    rowbase = ((long)n * prm.H + hd) * prm.T;
   }
   const int DV = prm.DV;
   const S* qg = reinterpret_cast<const S*>(prm.q) + rowbase * DK;
@@ -163,25 +171,25 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkParams prm) {
   const int vcol0 = vt * Cfg::DVT;
   const long sbase = (long)unit * DK * DV;
 
-  // ---- state slice: wave w owns key channels [w*WCH, (w+1)*WCH) x 64 columns --
-  f32x4 sacc[RB][4];
+  // ---- state slice: in pass ph, wave w owns key channels 64 ph + [w*WCH, (w+1)*WCH) x 64 columns
+  f32x4 sacc[NH][4];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+  for (int ph = 0; ph < NH; ++ph)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int c = w * WCH + rb * 16 + gq * 4 + s;
-        sacc[rb][cb][s] = prm.s0 ? prm.s0[sbase + (long)c * DV + vcol0 + cb * 16 + m] : 0.f;
+        const int c = DKH * ph + w * WCH + gq * 4 + s;
+        sacc[ph][cb][s] = prm.s0 ? prm.s0[sbase + (long)c * DV + vcol0 + cb * 16 + m] : 0.f;
       }
 
   // ---- gating lane geometry -----------------------------------------------------
   const int tg = m;                       // token group: tokens 4tg..4tg+3 of the chunk
-  const int ch0 = w * WCH + gq * CPL;     // first key channel of this lane
+  const int ch0 = w * WCH + gq * CPL;     // first key channel of this lane within a pass
   const int sub = tg >> 2;                // 16-token sub-chunk of these tokens
   const int vc0 = w * 16 + gq * 4;        // first of this lane's 4 V columns (of the slice)
 
-  Raw<Cfg::NW_QKG> rq[4], rk[4], rg[4];
+  Raw<Cfg::NW_QKG> rq[NH][4], rk[NH][4], rg[NH][4];
   Raw<Cfg::NW_V> rv[4];
 
   auto prefetch = [&](long t0) {
@@ -189,12 +197,19 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkParams prm) {
     for (int a = 0; a < 4; ++a) {
       const long t = t0 + 4 * tg + a;
       if (t < eos) {
-        raw_load(rq[a], qg + t * DK + ch0);
-        raw_load(rk[a], kg + t * DK + ch0);
-        raw_load(rg[a], gg + t * DK + ch0);
+#pragma unroll
+        for (int ph = 0; ph < NH; ++ph) {
+          raw_load(rq[ph][a], qg + t * DK + DKH * ph + ch0);
+          raw_load(rk[ph][a], kg + t * DK + DKH * ph + ch0);
+          raw_load(rg[ph][a], gg + t * DK + DKH * ph + ch0);
+        }
         raw_load(rv[a], vg + t * DV + vcol0 + vc0);
       } else {
-        raw_zero(rq[a]); raw_zero(rk[a]); raw_zero(rg[a]); raw_zero(rv[a]);
+#pragma unroll
+        for (int ph = 0; ph < NH; ++ph) {
+          raw_zero(rq[ph][a]); raw_zero(rk[ph][a]); raw_zero(rg[ph][a]);
+        }
+        raw_zero(rv[a]);
       }
     }
   };
@@ -203,15 +218,26 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkParams prm) {
   const int nchunks = (int)((len + C - 1) / C);
   if (nchunks > 0) prefetch(bos);
 
+  const int p = w;  // this wave's query sub-chunk in the contractions
   for (int u = 0; u < nchunks; ++u) {
     const long t0 = bos + (long)u * C;
+    f32x4 pacc[4];   // transposed score blocks P^T(r, p), summed over the passes
+    f32x4 oacc[4];   // O^T of the wave's 16 queries, 4 blocks of 16 columns
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pacc[r] = oacc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float vv[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) raw_unpack<E, 4>(rv[a], vv[a]);
+
+#pragma unroll
+    for (int ph = 0; ph < NH; ++ph) {
     // ===================== 1. gating: scan (registers only) =====================
     float loc[4][CPL];      // Gamma relative to the start of the lane's sub-chunk (log2)
     float tot[CPL], Bp[CPL], B4[CPL], s1v[CPL], s2v[CPL];
     {
       float x[4][CPL];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) raw_unpack<E, CPL>(rg[a], x[a]);
+      for (int a = 0; a < 4; ++a) raw_unpack<E, CPL>(rg[ph][a], x[a]);
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
         float p0 = clamp_gate(x[0][i] * kLog2e);
@@ -245,8 +271,10 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkParams prm) {
         B4[i] = sub == 3 ? bn : sub == 0 ? r4 : sub == 1 ? r8 : r12;
       }
     }
+    const int fslot = (u * NH + ph) & 1;
     {
-      // path flags: bit0 = the single-pivot form is unsafe, bit1 = exact diagonal needed
+      // path flags of this pass: bit0 = the single-pivot form is unsafe, bit1 = exact
+      // diagonal needed
       bool big = false, extreme = false;
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
@@ -254,10 +282,10 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkParams prm) {
         extreme |= !(fabsf(tot[i]) <= 100.f);
       }
       const unsigned long long bb = __ballot(big), be = __ballot(extreme);
-      if (lane == 0) s_flag[u & 1][w] = (bb ? 1 : 0) | (be ? 2 : 0);
+      if (lane == 0) s_flag[fslot][w] = (bb ? 1 : 0) | (be ? 2 : 0);
     }
-    __syncthreads();  // (A) previous chunk's MFMA reads are done; flags visible
-    const int fl = s_flag[u & 1][0] | s_flag[u & 1][1] | s_flag[u & 1][2] | s_flag[u & 1][3];
+    __syncthreads();  // (A) previous pass's MFMA reads are done; flags visible
+    const int fl = s_flag[fslot][0] | s_flag[fslot][1] | s_flag[fslot][2] | s_flag[fslot][3];
     const bool fast = (fl & 1) == 0;
     const bool exact_diag = (fl & 2) != 0;
 
@@ -266,8 +294,8 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkParams prm) {
       float qv[4][CPL], kv[4][CPL];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        raw_unpack<E, CPL>(rq[a], qv[a]);
-        raw_unpack<E, CPL>(rk[a], kv[a]);
+        raw_unpack<E, CPL>(rq[ph][a], qv[a]);
+        raw_unpack<E, CPL>(rk[ph][a], kv[a]);
       }
       float fBp[CPL], fKe[CPL], fKP[CPL];
 #pragma unroll
@@ -318,13 +346,11 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkParams prm) {
             for (int j = 0; j < 16; ++j) s_diag[sub][w][(tg & 3) * 4 + a][j] = d[a][j];
         }
       }
-      // S_prev (this chunk's inter-term operand) as SBT[col][channel]
+      // S_prev rows of this pass (its inter-term operand) as SBT[col][channel]
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-          store4<E>(s_sb + (cb * 16 + m) * PQ + w * WCH + rb * 16 + gq * 4, sacc[rb][cb][0],
-                    sacc[rb][cb][1], sacc[rb][cb][2], sacc[rb][cb][3]);
+      for (int cb = 0; cb < 4; ++cb)
+        store4<E>(s_sb + (cb * 16 + m) * PQ + w * WCH + gq * 4, sacc[ph][cb][0], sacc[ph][cb][1],
+                  sacc[ph][cb][2], sacc[ph][cb][3]);
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int row = 4 * tg + a;
@@ -364,11 +390,8 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkParams prm) {
 #pragma unroll
       for (int i = 0; i < CPL; ++i)
         store4<E>(s_kt + (ch0 + i) * PT + 4 * tg, kv[0][i], kv[1][i], kv[2][i], kv[3][i]);
-      // V as VT[column][token]
-      {
-        float vv[4][4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) raw_unpack<E, 4>(rv[a], vv[a]);
+      // V as VT[column][token], once per chunk (no later pass writes it)
+      if (ph == 0) {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
           store4<E>(s_vt + (vc0 + c) * PT + 4 * tg, vv[0][c], vv[1][c], vv[2][c], vv[3][c]);
@@ -378,15 +401,11 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkParams prm) {
         for (int i = 0; i < CPL; ++i) s_dec[ch0 + i] = fast_exp2(B4[i]);
       }
     }
-    // next chunk's inputs are in flight during the contractions
-    if (u + 1 < nchunks) prefetch(t0 + C);
+    // next chunk's inputs are in flight during the last pass's contractions
+    if (ph == NH - 1 && u + 1 < nchunks) prefetch(t0 + C);
     __syncthreads();  // (B) operand tiles complete
 
     // ===================== 3. contractions on MFMA =====================
-    const int p = w;  // this wave's query sub-chunk
-    f32x4 pacc[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pacc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (r <= p) {
@@ -406,40 +425,13 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkParams prm) {
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             const int j = gq * 4 + s;
-            pacc[r][s] = ((s_diag[p][0][m][j] + s_diag[p][1][m][j]) + s_diag[p][2][m][j]) +
-                         s_diag[p][3][m][j];
+            pacc[r][s] += ((s_diag[p][0][m][j] + s_diag[p][1][m][j]) + s_diag[p][2][m][j]) +
+                          s_diag[p][3][m][j];
           }
         }
-        if (r == p) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            if (gq * 4 + s > m) pacc[r][s] = 0.f;   // causal: key j after query i
-        }
       }
     }
-
-    f32x4 oacc[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) oacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // O^T += V^T P^T over keys 32ks..32ks+31 (score blocks 2ks, 2ks+1)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (2 * ks <= p) {
-        float pv[8] = {pacc[2 * ks][0],     pacc[2 * ks][1],     pacc[2 * ks][2],
-                       pacc[2 * ks][3],     pacc[2 * ks + 1][0], pacc[2 * ks + 1][1],
-                       pacc[2 * ks + 1][2], pacc[2 * ks + 1][3]};
-        Frag<E> fb;
-        frag_from_f32(fb, pv);
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          Frag<E> fa;
-          const S* vrow = s_vt + (cb * 16 + m) * PT + ks * 32 + gq * 4;
-          frag_ld4x2(fa, vrow, vrow + 16);
-          mma(oacc[cb], fa, fb);
-        }
-      }
-    }
-    // O^T += S_prev^T (Q 2^Gamma)^T
+    // O^T += S_prev^T (Q 2^Gamma)^T over this pass's channels
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       Frag<E> fb;
@@ -451,8 +443,30 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkParams prm) {
         mma(oacc[cb], fa, fb);
       }
     }
-    // store the wave's 16 output rows: lane holds token 16p+m, columns 16cb+4gq..+3
-    {
+    if (ph == NH - 1) {
+      // causal mask of the diagonal block (key j after query i), then
+      // O^T += V^T P^T over keys 32ks..32ks+31 (score blocks 2ks, 2ks+1)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (gq * 4 + s > m) pacc[p][s] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if (2 * ks <= p) {
+          float pv[8] = {pacc[2 * ks][0],     pacc[2 * ks][1],     pacc[2 * ks][2],
+                         pacc[2 * ks][3],     pacc[2 * ks + 1][0], pacc[2 * ks + 1][1],
+                         pacc[2 * ks + 1][2], pacc[2 * ks + 1][3]};
+          Frag<E> fb;
+          frag_from_f32(fb, pv);
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            Frag<E> fa;
+            const S* vrow = s_vt + (cb * 16 + m) * PT + ks * 32 + gq * 4;
+            frag_ld4x2(fa, vrow, vrow + 16);
+            mma(oacc[cb], fa, fb);
+          }
+        }
+      }
+      // store the wave's 16 output rows: lane holds token 16p+m, columns 16cb+4gq..+3
       const long t = t0 + 16 * p + m;
       if (t < eos) {
 #pragma unroll
@@ -461,40 +475,36 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkParams prm) {
                     oacc[cb][2], oacc[cb][3]);
       }
     }
-    // state: S = diag(2^Gamma_last) S + (K 2^(Gamma_last - Gamma))^T V
+    // state rows of this pass: S = diag(2^Gamma_last) S + (K 2^(Gamma_last - Gamma))^T V
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int s = 0; s < 4; ++s) {
+      const float f = s_dec[w * WCH + gq * 4 + s];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const float f = s_dec[w * WCH + rb * 16 + gq * 4 + s];
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) sacc[rb][cb][s] *= f;
-      }
+      for (int cb = 0; cb < 4; ++cb) sacc[ph][cb][s] *= f;
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      Frag<E> fa[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        frag_ld8(fa[rb], s_kt + (w * WCH + rb * 16 + m) * PT + ks * 32 + gq * 8);
+      Frag<E> fa;
+      frag_ld8(fa, s_kt + (w * WCH + m) * PT + ks * 32 + gq * 8);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         Frag<E> fb;
         frag_ld8(fb, s_vt + (cb * 16 + m) * PT + ks * 32 + gq * 8);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) mma(sacc[rb][cb], fa[rb], fb);
+        mma(sacc[ph][cb], fa, fb);
       }
     }
+    }   // passes
   }
 
   if (prm.sT) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int ph = 0; ph < NH; ++ph)
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const int c = w * WCH + rb * 16 + gq * 4 + s;
-          prm.sT[sbase + (long)c * DV + vcol0 + cb * 16 + m] = sacc[rb][cb][s];
+          const int c = DKH * ph + w * WCH + gq * 4 + s;
+          prm.sT[sbase + (long)c * DV + vcol0 + cb * 16 + m] = sacc[ph][cb][s];
         }
   }
 }
@@ -509,6 +519,7 @@ int launch_chunk_fwd(const ChunkParams& prm, int dk, int dtype, int nblocks, hip
   // bf16: the pipelined producer/consumer kernel; fp32: the single-phase kernel above
   if (dtype == 0) return launch_chunk_fwd_pipe(prm, dk, false, nblocks, stream);
   if (dtype == 1 && dk == 64) return launch<64, F32>(prm, nblocks, stream);
+  if (dtype == 1 && dk == 128) return launch<128, F32>(prm, nblocks, stream);
   return -2;
 }
 

@@ -64,9 +64,8 @@ int check_chunk_args(const char* fn, const void* q, const void* k, const void* v
                 B, H, T, dk, dv);
   if (chunk_size != 64)
     return fail(GLA_ERR_UNSUPPORTED, "%s: chunk_size %d (only 64 is implemented)", fn, chunk_size);
-  if (dtype == GLA_BF16 ? (dk != 64 && dk != 128) : dk != 64)
-    return fail(GLA_ERR_UNSUPPORTED, "%s: dk=%d is not implemented for %s", fn, dk,
-                dtype == GLA_BF16 ? "GLA_BF16 (64 or 128)" : "GLA_F32 (64)");
+  if (dk != 64 && dk != 128)
+    return fail(GLA_ERR_UNSUPPORTED, "%s: dk=%d is not implemented (64 or 128)", fn, dk);
   if (dv % 64 != 0 || dv > 512)
     return fail(GLA_ERR_UNSUPPORTED, "%s: dv=%d must be a multiple of 64 up to 512", fn, dv);
   int nseq = B;

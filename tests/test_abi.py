@@ -81,7 +81,7 @@ def _chunk(lib, entry="gla_chunk_fwd", **kw):
     (dict(dtype=7), 1, "dtype"),
     (dict(C=128), 2, "chunk_size"),
     (dict(dk=96), 2, "dk=96"),
-    (dict(dk=128, dtype=1), 2, "dk=128"),
+    (dict(dk=256, dtype=1), 2, "dk=256"),
     (dict(dv=96), 2, "dv=96"),
     (dict(dv=1024), 2, "dv=1024"),
     (dict(cu=FAKE, B=2, num_seqs=2), 1, "B == 1"),

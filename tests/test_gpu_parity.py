@@ -123,23 +123,25 @@ FP32_CASES = [
 ]
 
 
+@pytest.mark.parametrize("dk", [64, 128])
 @pytest.mark.parametrize("label,B,H,T,dv,gate,s0", FP32_CASES, ids=[c[0] for c in FP32_CASES])
-def test_fp32_cases(dev, label, B, H, T, dv, gate, s0):
-    w = I.ChunkWorkload("fp32_edge", B=B, H=H, T=T, dk=64, dv=dv, dtype="f32", seed=101,
+def test_fp32_cases(dev, label, B, H, T, dv, gate, s0, dk):
+    w = I.ChunkWorkload("fp32_edge", B=B, H=H, T=T, dk=dk, dv=dv, dtype="f32", seed=101,
                         k_scaled=True)
-    say(f"fp32 {label}: B={B} H={H} T={T} dk=64 dv={dv} gate={gate} s0={s0}")
+    say(f"fp32 {label}: B={B} H={H} T={T} dk={dk} dv={dv} gate={gate} s0={s0}")
     d = I.chunk_inputs(w, gate=gate, s0=s0)
     o, sf = _fwd(dev, d, s0=d["s0"])
     _check_fixed(d, o, sf, d["s0"], TOL_F32, label)
 
 
-def test_fp32_extreme_gates_exact_diagonal(dev):
+@pytest.mark.parametrize("dk", [64, 128])
+def test_fp32_extreme_gates_exact_diagonal(dev, dk):
     """Some channels decay by far more than 2^100 inside one 16-token sub-chunk
     (and a few gates are -inf, alpha = 0): the diagonal score blocks are then
     evaluated element by element."""
-    w = I.ChunkWorkload("fp32_extreme", B=1, H=2, T=192, dk=64, dv=64, dtype="f32", seed=7,
+    w = I.ChunkWorkload("fp32_extreme", B=1, H=2, T=192, dk=dk, dv=64, dtype="f32", seed=7,
                         k_scaled=True)
-    say("fp32 extreme gates: B=1 H=2 T=192 dk=64 dv=64, g down to -80 and -inf")
+    say(f"fp32 extreme gates: B=1 H=2 T=192 dk={dk} dv=64, g down to -80 and -inf")
     d = I.chunk_inputs(w, s0=True)
     gen = torch.Generator().manual_seed(3)
     mask = torch.rand(d["g"].shape, generator=gen) < 0.3
@@ -147,7 +149,35 @@ def test_fp32_extreme_gates_exact_diagonal(dev):
     g[0, 0, 70, 5] = float("-inf")
     d["g"] = g
     o, sf = _fwd(dev, d, s0=d["s0"])
-    _check_fixed(d, o, sf, d["s0"], TOL_F32, "extreme")
+    _check_fixed(d, o, sf, d["s0"], TOL_F32, f"extreme dk={dk}")
+
+
+def test_fp32_tiny_recipe_at_dk128(dev):
+    """The tiny fp32 workload's recipe at d_k = d_v = 128 (B1 H2 T256, k scaled
+    by d_k^-1/2, weak gates): two 64-channel passes per chunk."""
+    w = I.ChunkWorkload("fp32_tiny_d128", B=1, H=2, T=256, dk=128, dv=128, dtype="f32", seed=1,
+                        k_scaled=True)
+    say("fp32 tiny recipe at dk=dv=128: B=1 H=2 T=256")
+    d = I.chunk_inputs(w)
+    o, sf = _fwd(dev, d)
+    _check_fixed(d, o, sf, None, TOL_F32, "fp32 tiny d128")
+
+
+def test_fp32_dk128_passes_in_different_modes(dev):
+    """d_k = 128 in fp32: strong gates on channels 64..127 only, so within a chunk
+    the first 64-channel pass takes the single pivot and the second the
+    sub-chunk pivots (and one channel of the second decays beyond 2^100)."""
+    w = I.ChunkWorkload("fp32_mixed", B=2, H=2, T=200, dk=128, dv=64, dtype="f32", seed=29,
+                        k_scaled=True)
+    say("fp32 dk=128 mixed passes: weak gates on channels 0..63, strong on 64..127")
+    d = I.chunk_inputs(w, s0=True)
+    strong = I.chunk_inputs(w, gate="strong", s0=True)["g"]
+    g = d["g"].clone()
+    g[..., 64:] = strong[..., 64:]
+    g[0, 1, 40:56, 100] = -20.0
+    d["g"] = g
+    o, sf = _fwd(dev, d, s0=d["s0"])
+    _check_fixed(d, o, sf, d["s0"], TOL_F32, "fp32 mixed passes")
 
 
 @pytest.mark.parametrize("dk", [128, 64])
@@ -184,11 +214,12 @@ def test_bf16_mixed_fast_and_safe_slices(dev):
     _check_fixed(d, o, sf, d["s0"], TOL_BF16, "bf16 mixed")
 
 
-def test_fp32_varlen_with_empty_and_short(dev):
+@pytest.mark.parametrize("dk", [64, 128])
+def test_fp32_varlen_with_empty_and_short(dev, dk):
     lengths = [5, 0, 64, 1, 130, 0, 77]
-    w = I.ChunkWorkload("fp32_varlen", B=1, H=2, T=0, dk=64, dv=64, dtype="f32", seed=11,
+    w = I.ChunkWorkload("fp32_varlen", B=1, H=2, T=0, dk=dk, dv=64, dtype="f32", seed=11,
                         k_scaled=True)
-    say(f"fp32 varlen lengths={lengths} with initial state")
+    say(f"fp32 varlen dk={dk} lengths={lengths} with initial state")
     d = I.chunk_inputs(w, lengths=lengths, s0=True)
     o, sf = _fwd(dev, d, s0=d["s0"], cu=d["cu_seqlens"])
     o_ref, s_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], s0=d["s0"],
@@ -322,6 +353,33 @@ def test_decode_fp32_small(dev):
         torch.cuda.synchronize()
         assert unit_err_fixed(o, o_ref) <= TOL_F32
     assert unit_err_fixed(st, s_ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(a, b) for a in (64, 128, 256) for b in (64, 128, 256)])
+def test_decode_every_accepted_shape(dev, dk, dv, dtype):
+    """Every (d_k, d_v, dtype) that gla_recurrent_step accepts, against the oracle
+    over a few steps (each shape is its own kernel instantiation: rows per lane,
+    row groups and the cross-row reduction differ)."""
+    from sub_quadratic_sequence_amd import gla
+
+    w = I.DecodeWorkload(f"dec_{dtype}", N=3, H=2, dk=dk, dv=dv, steps=4, seed=11 + dk + dv,
+                         dtype=dtype)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    say(f"gla_recurrent_step {dtype} N=3 H=2 dk={dk} dv={dv} x4")
+    d = I.decode_inputs(w)
+    st = d["s0"].to(dev).clone()
+    s_ref = d["s0"].double().numpy()
+    for t in range(w.steps):
+        o = gla.gla_recurrent_step(*(d[n][t].to(dev) for n in "qkvg"), st)
+        o_ref, s_ref = oracle.decode_step(*(d[n][t] for n in "qkvg"), s_ref)
+        torch.cuda.synchronize()
+        e_o = unit_err_fixed(o, o_ref)
+        assert np.all(np.isfinite(to64(o)))
+        assert e_o <= tol, (t, e_o)
+    e_s = unit_err_fixed(st, s_ref)
+    print(f"decode {dtype} dk={dk} dv={dv}: O err {e_o:.3e} S err {e_s:.3e}", flush=True)
+    assert e_s <= tol
 
 
 def test_decode_steps_equal_chunk_fwd(dev):
