@@ -181,3 +181,26 @@ def test_nan_stays_in_its_sequence(dev):
     ok[100:250] = False
     assert torch.isfinite(o[0, :, ok]).all() and torch.isfinite(o[0, 0]).all()
     assert torch.isfinite(sf[[0, 2]]).all() and torch.isfinite(sf[1, 0]).all()
+
+
+@pytest.mark.parametrize("noise", [0.2, 0.0])
+def test_correlated_keys(dev, noise):
+    """Unit keys that all share one direction (random signs, a little noise or
+    none), beta = 0.5 and no decay: the strictly lower part L of each 16-token
+    diagonal block of M has entries of magnitude near 0.5, so every factor of the
+    block inverse (I - L)(I + L^2)(I + L^4)(I + L^8) contributes (L^8 alone
+    reaches about 13).  With beta near 1 the same keys make the chunk form
+    ill-conditioned for bf16 intermediates: the error then approaches 2e-2 (the
+    design notes give the measured values and their source)."""
+    say(f"gdn correlated unit keys (shared direction, noise {noise}), beta 0.5, g 0, B1 H2 T200 d128")
+    d = I.gdn_inputs(W, B=1, H=2, T=200, s0=True, seed=31)
+    gen = torch.Generator().manual_seed(32)
+    base = torch.randn(1, 2, 1, W.dk, generator=gen)
+    sign = torch.where(torch.rand(1, 2, 200, 1, generator=gen) < 0.5, -1.0, 1.0)
+    k = sign * base + noise * torch.randn(1, 2, 200, W.dk, generator=gen)
+    k = k / k.norm(dim=-1, keepdim=True)
+    d["k"] = k.to(torch.bfloat16)
+    d["beta"] = torch.full_like(d["beta"], 0.5)
+    d["g"] = torch.zeros_like(d["g"])
+    o, sf = _run(dev, d, s0=d["s0"])
+    _check(d, o, sf, d["s0"], f"correlated keys noise {noise}")
