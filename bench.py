@@ -122,6 +122,24 @@ def read_traffic(name):
         return None
 
 
+def read_counters(name):
+    """Diagnostic MFMA and instruction counters of the forward kernel from the
+    committed rocprofv3 summary, if it was taken on the current sources (null
+    otherwise): the MFMA-busy fraction of the SIMDs' cycles, the executed bf16
+    MFMA work over the algorithmic FLOPs, and the waves' waiting share."""
+    kv = read_summary(name)
+    if kv is None or kv.get("sources_sha256") != sources_sha256():
+        return None
+    try:
+        return {"mfma_busy_frac": float(kv["mfma_busy_frac"]),
+                "mfma_flop_executed_over_algorithmic": float(kv["executed_over_algorithmic"]),
+                "wait_inst_any_over_wave_cycles": float(kv["wait_inst_any_over_wave_cycles"]),
+                "lds_bank_conflict_over_active_lds": float(kv["lds_bank_conflict_over_active_lds"]),
+                "source": "profiles/" + name}
+    except (KeyError, ValueError):
+        return None
+
+
 def time_launches(fn, steps, warmup, torch, preroll_s=0.0):
     """Untimed: fn() repeated for preroll_s seconds (the GPU leaves its idle
     clocks), then `warmup` calls.  Timed: exactly `steps` calls, bracketed by
@@ -548,6 +566,7 @@ def main():
                    "chunk": 64, "final_state": True, "initial_state": False},
         "tflop_s": tflops,
         "mfma_peak_frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+        "mfma_counters": read_counters("chunk_fwd_b8h16t2048d128_bf16_counters.txt"),
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "gla::chunk_fwd_pipe_kernel<128, kFull, 1> (64-column d_v slice)",

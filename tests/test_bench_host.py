@@ -88,3 +88,13 @@ def test_read_traffic_follows_every_source(tmp_path, changed):
         assert bench.read_traffic("missing.txt") is None
     finally:
         bench.PROFILES, bench.CSRC, bench.ROOT = old
+
+
+def test_counter_summary_is_well_formed_and_read():
+    kv = _fields(os.path.join(bench.PROFILES, "chunk_fwd_b8h16t2048d128_bf16_counters.txt"))
+    for key in ("mfma_busy_frac", "executed_over_algorithmic", "wait_inst_any_over_wave_cycles",
+                "lds_bank_conflict_over_active_lds", "sources_sha256"):
+        assert key in kv, key
+    assert 0.0 < float(kv["mfma_busy_frac"]) < 1.0
+    # the executed MFMA work covers at least the algorithmic FLOPs
+    assert float(kv["executed_over_algorithmic"]) >= 1.0
