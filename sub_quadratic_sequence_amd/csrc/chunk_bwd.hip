@@ -106,15 +106,24 @@ __host__ __device__ constexpr unsigned ca(unsigned cr, unsigned cu, unsigned RB 
 __device__ __forceinline__ s16x4 tr_read(const unsigned short* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
-// 16-deep contraction: the 16x16x32 instruction with the second half of both
-// operands zero (slots 4-7 pair with slots 4-7, so they add exactly 0).  The
-// legacy 16x16x16 bf16 instruction is not used: its results were read back too
-// early by the generated code on gfx950 (wrong values, no fault).
+// 16-deep contraction on the 16x16x16 bf16 instruction (on gfx950 it issues at
+// the rate of the 32-deep one, so it saves no matrix-core time, only the moves
+// that would build zero-padded 32-deep operands).  Rule: its accumulator input
+// is never a register that a 16x16x32 instruction has just written.  The
+// compiler separates that dependence by 0-5 wait states on gfx950, and the
+// 16-deep instruction then adds to a stale accumulator (wrong values, no
+// fault; with 16 wait states in front of it the results are right).  A sum of
+// 32-deep and 16-deep products therefore takes the 16-deep one in a fresh
+// accumulator (mma16_add); chains of 16-deep products on one accumulator, with
+// VALU scalings between them, are fine.
 __device__ __forceinline__ void mma16(f32x4& acc, s16x4 a, s16x4 b) {
-  const s16x4 z = {0, 0, 0, 0};
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-      __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, z, 0, 1, 2, 3, 4, 5, 6, 7)),
-      __builtin_bit_cast(bf16x8, __builtin_shufflevector(b, z, 0, 1, 2, 3, 4, 5, 6, 7)), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+}
+// acc += A B (16-deep) where acc comes from 16x16x32 products
+__device__ __forceinline__ void mma16_add(f32x4& acc, s16x4 a, s16x4 b) {
+  f32x4 t = {0.f, 0.f, 0.f, 0.f};
+  mma16(t, a, b);
+  acc += t;
 }
 __device__ __forceinline__ void mma32(f32x4& acc, s16x8 a, s16x8 b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
@@ -491,7 +500,7 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
                 cat(rd8(oO + at(r16, 16 * s, 4 * kk)), rd8(oO + at(r16, 16 * s, 4 * kk + 2))));
         // k~^T[c][j] A[i][j] over j in the sub-chunk
         const s16x4 kt = rdt(oK + at(tW, 16 * s, 0));
-        mma16(acc, kt, rd8(oA + s * L * LP * 2 + r16L));
+        mma16_add(acc, kt, rd8(oA + s * L * LP * 2 + r16L));
         // lane: channels c0 + 4 grp + r at token 16 s + m
         const float4 d = *reinterpret_cast<const float4*>(lds + oD + ((eD ^ cx(16 * s, 0)) + ca(16 * s, 0, RD)));
         const uint2 qv = *reinterpret_cast<const uint2*>(lds + oQ + at(eQ, 16 * s, 0));
@@ -552,7 +561,7 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
                 cat(rd8(oV + at(r16, 16 * s, 4 * kk)), rd8(oV + at(r16, 16 * s, 4 * kk + 2))));
         // q~^T[c][i] A[i][j] over i in the sub-chunk
         const s16x4 qt = rdt(oQ + at(tW, 16 * s, 0));
-        mma16(acc, qt, rdt(oA + s * L * LP * 2 + tL));
+        mma16_add(acc, qt, rdt(oA + s * L * LP * 2 + tL));
         const float4 d = *reinterpret_cast<const float4*>(lds + oD + ((eD ^ cx(16 * s, 0)) + ca(16 * s, 0, RD)));
         const uint2 kv = *reinterpret_cast<const uint2*>(lds + oK + at(eQ, 16 * s, 0));
         float x[4] = {qd[s][0] - lo_bf16(kv.x) * acc[0], qd[s][1] - hi_bf16(kv.x) * acc[1],
@@ -592,7 +601,7 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
           mma32(acc, cat(rdt(oS + at(tS, 32 * kk, 0)), rdt(oS + at(tS, 32 * kk + 4, 0))),
                 rd16(oK + at(r32, 16 * s, 4 * kk)));
         // dO^T[n][i] P[i][j] over i in the sub-chunk
-        mma16(acc, rdt(oO + at(tW, 16 * s, 0)), rdt(oP + s * L * LP * 2 + tL));
+        mma16_add(acc, rdt(oO + at(tW, 16 * s, 0)), rdt(oP + s * L * LP * 2 + tL));
         const long t = row0 + 16 * s + m;
         if (t < sq.len)
           *reinterpret_cast<uint2*>(dv_out + t * DV + n0 + 4 * grp) = pack4(acc[0], acc[1], acc[2], acc[3]);
