@@ -99,9 +99,9 @@ size_t gla_chunk_fwd_workspace_size(int num_seqs, int B, int H, int T, int dk, i
 /*
  * gla_chunk_fwd with a sequence split for inputs whose (sequence, head, 64-column
  * slice) work items do not fill the device: each sequence is cut into segments
- * of whole 64-token chunks, at least 512 tokens long, so that there are about
- * as many work items as compute units (bf16 work items of a split cover 128
- * columns of d_v when d_v is a multiple of 128, else 64).  The recurrence is linear in the state
+ * of whole 64-token chunks, the segment count chosen by gla_split_plan (bf16
+ * work items of a split cover 128 columns of d_v when d_v is a multiple of 128,
+ * else 64).  The recurrence is linear in the state
  * with a diagonal transition, so over one segment S_end = diag(a) S_start +
  * S_zero, with a = exp(sum of the segment's g) and S_zero the state reached
  * from zero (page "Gated Linear Attention (GLA) ...", section "The Gated
@@ -159,6 +159,55 @@ int gla_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const voi
                           const float* initial_state, void* o, float* final_state,
                           const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk,
                           int dv, int chunk_size, int dtype, void* stream);
+
+/*
+ * The segment count that gla_chunk_fwd_ws, gla_chunk_fwd_noalloc and the size
+ * query gla_chunk_fwd_workspace_size use for fixed-length bf16 inputs of units
+ * = B x H (sequence, head) pairs of T tokens and d_v = dv columns on a device
+ * with num_cus compute units; 1 means the call runs unsplit.  *seg_len (if not
+ * NULL) receives the segment length in tokens, a multiple of 64 (T when
+ * unsplit); the last segment may be shorter.  Host-only: no GPU is touched.
+ *
+ * The choice minimises a cost model (page "Qwen Team Releases FlashQLA for
+ * High-Performance Linear Attention", section "Core Technical Principles"): in
+ * the "one wave" case a split's per-segment passes cost lambda_1 per chunk of
+ * segment length L and its scan across segments lambda_2 per segment, so
+ * T = lambda_1 L + lambda_2 N / L for N chunks; plus lambda_0 per split call,
+ * against mu_1 N + mu_0 unsplit.  The constants are fitted on MI355X.  Splits
+ * are considered only when units x dv / 64 < num_cus, and only for segment
+ * counts whose work items fit one wave.  dtype other than GLA_BF16, T <= 0,
+ * units <= 0 or dv not a positive multiple of 64 give 1.
+ */
+int gla_split_plan(long long units, int T, int dv, int dtype, int num_cus, int* seg_len);
+
+/*
+ * Device workspace, in bytes, that gla_chunk_fwd_segments needs: 0 when
+ * num_segments gives one segment, else (segment states B x H x segments x dk x dv
+ * fp32 and decays B x H x segments x dk fp32, each rounded up to 256 bytes).
+ * Invalid shapes or num_segments outside [1, ceil(T / 64)] give 0.
+ */
+size_t gla_chunk_fwd_segments_workspace_size(int B, int H, int T, int dk, int dv, int num_segments);
+
+/*
+ * The sequence split of gla_chunk_fwd_ws with a segment count the caller
+ * chooses (as a fixed context-parallel degree is chosen by hand across GPUs),
+ * for fixed-length inputs (no cu_seqlens).  Each sequence is cut into segments
+ * of L = ceil(ceil(T / 64) / num_segments) whole chunks; the segment count used
+ * is ceil(ceil(T / 64) / L), at most num_segments.  One segment runs unsplit as
+ * gla_chunk_fwd (any dtype); more need bf16 (else GLA_ERR_UNSUPPORTED).
+ *
+ *   num_segments    1 .. ceil(T / 64), else GLA_ERR_INVALID_ARG.
+ *   workspace       device buffer of at least
+ *                   gla_chunk_fwd_segments_workspace_size(...) bytes, 256-byte
+ *                   aligned, as for gla_chunk_fwd_ws.
+ *
+ * Other arguments, layouts and errors as for gla_chunk_fwd_ws.  Results equal
+ * gla_chunk_fwd's up to rounding for every segment count.
+ */
+int gla_chunk_fwd_segments(const void* q, const void* k, const void* v, const void* g,
+                           const float* initial_state, void* o, float* final_state, int B, int H,
+                           int T, int dk, int dv, int chunk_size, int dtype, int num_segments,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Device workspace, in bytes, that gla_chunk_bwd needs for this shape (the bf16

@@ -11,6 +11,7 @@
 
 #include "gla.h"
 #include "gla_kernels.h"
+#include "split_model.h"
 
 namespace {
 
@@ -149,10 +150,10 @@ void choose_slice(gla::ChunkParams& prm, long long units, int dtype) {
 }
 
 
-// Sequence split: fixed-length bf16 inputs whose work items do not fill the
-// device are cut into segments of at least kMinSegChunks chunks, about enough to
-// give every compute unit one work item.  Returns the segment count (1 = none)
-// and the segment length in tokens.
+// Sequence split of the backward: fixed-length bf16 inputs whose work items do
+// not fill the device are cut into segments of at least kMinSegChunks chunks,
+// about enough to give every compute unit one work item.  Returns the segment
+// count (1 = none) and the segment length in tokens.
 constexpr int kMinSegChunks = 8;
 
 int split_plan(bool varlen, int dtype, long long items, int T, int& seg_len) {
@@ -170,14 +171,41 @@ int split_plan(bool varlen, int dtype, long long items, int T, int& seg_len) {
   return (T + seg_len - 1) / seg_len;
 }
 
-// Segment plan of the forward: split only when the 64-column work items do not
-// fill the device; a split then uses the 128-column slice when d_v allows it
-// (bf16), so the plan cuts each sequence into about twice as many segments.
-int fwd_split_plan(bool varlen, int dtype, long long units, int dv, int T, int& seg_len) {
+// Segment plan of the forward (fixed-length bf16 inputs), from the split cost
+// model of split_model.h: a split is considered only when the unsplit call's
+// 64-column work items leave compute units idle (the page "Qwen Team Releases
+// FlashQLA ...", section "Core Technical Principles": trigger when the device is
+// clearly underused), and only for segment counts whose work items (128 columns
+// of d_v when d_v allows) fit one wave.  Among those and the unsplit call it
+// takes the least modelled time; ties keep fewer segments.  Returns the segment
+// count (1 = unsplit) and the segment length in tokens (whole 64-token chunks).
+int model_split_plan(bool varlen, int dtype, long long units, int dv, int T, int ncu, int& seg_len) {
+  using namespace gla::split_model;
   seg_len = T;
-  if (units * (dv / 64) >= device_cus()) return 1;
-  const long long items = units * ((dtype == GLA_BF16 && dv % 128 == 0) ? dv / 128 : dv / 64);
-  return split_plan(varlen, dtype, items, T, seg_len);
+  if (varlen || dtype != GLA_BF16 || T <= 0 || units <= 0 || dv <= 0 || dv % 64 != 0 || ncu <= 0)
+    return 1;
+  if (units * (dv / 64) >= ncu) return 1;
+  const long long nch = ((long long)T + 63) / 64;
+  const double t_unsplit = kMu1 * (double)nch + kMu0;   // one wave (the guard above)
+  const long long items = units * ((dv % 128 == 0) ? dv / 128 : dv / 64);
+  double best = t_unsplit;
+  long long best_l = nch;
+  for (long long n = 2; n <= nch && items * n <= ncu; ++n) {
+    const long long l = (nch + n - 1) / n;    // chunks per segment
+    const long long ns = (nch + l - 1) / l;   // segments that length gives
+    const double t = kLambda1 * (double)l + kLambda2 * (double)ns + kLambda0;
+    if (t < best) {
+      best = t;
+      best_l = l;
+    }
+  }
+  if (best_l == nch) return 1;
+  seg_len = (int)(best_l * 64);
+  return (int)((nch + best_l - 1) / best_l);
+}
+
+int fwd_split_plan(bool varlen, int dtype, long long units, int dv, int T, int& seg_len) {
+  return model_split_plan(varlen, dtype, units, dv, T, device_cus(), seg_len);
 }
 
 size_t split_bytes(long long units, int nseg, int dk, int dv) {
@@ -351,6 +379,72 @@ int gla_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const voi
   char* ws = static_cast<char*>(scratch_for_current_device(fn));
   if (!ws) return GLA_ERR_LAUNCH;
   return run_split(fn, prm, units, nseg, seg_len, dk, dv, dtype, initial_state, final_state, ws, s);
+}
+
+int gla_split_plan(long long units, int T, int dv, int dtype, int num_cus, int* seg_len) {
+  int len = T;
+  const int n = model_split_plan(false, dtype, units, dv, T, num_cus, len);
+  if (seg_len) *seg_len = len;
+  return n;
+}
+
+namespace {
+// segment length (whole chunks) and count for a caller-chosen segment count
+int forced_plan(int T, int num_segments, int& seg_len) {
+  const long long nch = ((long long)T + 63) / 64;
+  const long long l = (nch + num_segments - 1) / num_segments;
+  seg_len = (int)(l * 64);
+  return (int)((nch + l - 1) / l);
+}
+}  // namespace
+
+size_t gla_chunk_fwd_segments_workspace_size(int B, int H, int T, int dk, int dv, int num_segments) {
+  if (B <= 0 || H <= 0 || T <= 0 || dk <= 0 || dv <= 0 || num_segments < 1) return 0;
+  const long long nch = ((long long)T + 63) / 64;
+  if (num_segments > nch) return 0;
+  int seg_len = 0;
+  const int nseg = forced_plan(T, num_segments, seg_len);
+  return nseg > 1 ? split_bytes((long long)B * H, nseg, dk, dv) : 0;
+}
+
+int gla_chunk_fwd_segments(const void* q, const void* k, const void* v, const void* g,
+                           const float* initial_state, void* o, float* final_state, int B, int H,
+                           int T, int dk, int dv, int chunk_size, int dtype, int num_segments,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  const char* fn = "gla_chunk_fwd_segments";
+  gla::ChunkParams prm;
+  long long units = 0;
+  bool nothing = false;
+  const int st = check_chunk_args(fn, q, k, v, g, initial_state, o, final_state, nullptr, 0, B, H, T,
+                                  dk, dv, chunk_size, dtype, prm, units, nothing);
+  if (st != GLA_OK || nothing) return st;
+  const long long nch = ((long long)T + 63) / 64;
+  if (num_segments < 1 || num_segments > nch)
+    return fail(GLA_ERR_INVALID_ARG, "%s: num_segments = %d, must be in [1, %lld] (one chunk or more each)",
+                fn, num_segments, nch);
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int seg_len = T;
+  const int nseg = forced_plan(T, num_segments, seg_len);
+  if (nseg == 1) {
+    choose_slice(prm, units, dtype);
+    const int rc = gla::launch_chunk_fwd(prm, dk, dtype, (int)(units * prm.nvt), s);
+    return launch_status(fn, rc, dk, dtype);
+  }
+  if (dtype != GLA_BF16)
+    return fail(GLA_ERR_UNSUPPORTED, "%s: the sequence split runs on bf16 inputs only", fn);
+  if (dv % 128 == 0) {   // split work items take the 128-column slice, as in gla_chunk_fwd_ws
+    prm.dvt = 128;
+    prm.nvt = dv / 128;
+  }
+  const size_t need = split_bytes(units, nseg, dk, dv);
+  if (!workspace || workspace_bytes < need)
+    return fail(GLA_ERR_INVALID_ARG, "%s: workspace of %zu bytes given, %zu needed", fn,
+                workspace ? workspace_bytes : (size_t)0, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(GLA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+  return run_split(fn, prm, units, nseg, seg_len, dk, dv, dtype, initial_state, final_state,
+                   static_cast<char*>(workspace), s);
 }
 
 size_t gla_chunk_bwd_workspace_size(int num_seqs, int B, int H, int T, int dk, int dv,

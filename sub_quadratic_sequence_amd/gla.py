@@ -46,6 +46,12 @@ def load_library():
         lib.gla_chunk_fwd_ws.restype = I
         lib.gla_chunk_fwd_ws.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P,
                                          ctypes.c_size_t, P]
+        lib.gla_split_plan.restype = I
+        lib.gla_split_plan.argtypes = [ctypes.c_longlong, I, I, I, I, ctypes.POINTER(I)]
+        lib.gla_chunk_fwd_segments_workspace_size.restype = ctypes.c_size_t
+        lib.gla_chunk_fwd_segments_workspace_size.argtypes = [I, I, I, I, I, I]
+        lib.gla_chunk_fwd_segments.restype = I
+        lib.gla_chunk_fwd_segments.argtypes = [P] * 7 + [I] * 8 + [P, ctypes.c_size_t, P]
         lib.gla_chunk_bwd_workspace_size.restype = ctypes.c_size_t
         lib.gla_chunk_bwd_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
         lib.gla_chunk_bwd.restype = I
@@ -186,6 +192,62 @@ def gla_chunk_fwd_noalloc(q, k, v, g, initial_state=None, output_final_state=Fal
     return gla_chunk_fwd(q, k, v, g, initial_state=initial_state,
                          output_final_state=output_final_state, cu_seqlens=cu_seqlens,
                          chunk_size=chunk_size, out=out, final_state=final_state, noalloc=True)
+
+
+def split_plan(units: int, T: int, dv: int, dtype=torch.bfloat16, num_cus=None):
+    """``(segments, segment_length)`` that the sequence-split forward uses for
+    fixed-length inputs of ``units`` = B x H (sequence, head) pairs of ``T``
+    tokens and ``dv`` value columns (``gla_split_plan``; host-only).
+    ``num_cus`` defaults to the current GPU's compute-unit count."""
+    if num_cus is None:
+        num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    code = GLA_BF16 if dtype == torch.bfloat16 else GLA_F32
+    seg_len = ctypes.c_int(0)
+    n = load_library().gla_split_plan(int(units), int(T), int(dv), code, int(num_cus),
+                                      ctypes.byref(seg_len))
+    return int(n), int(seg_len.value)
+
+
+def gla_chunk_fwd_segments(q, k, v, g, num_segments: int, initial_state=None,
+                           output_final_state=False, chunk_size: int = 64, out=None,
+                           final_state=None, workspace=None):
+    """The sequence-split forward with a caller-chosen segment count
+    (``gla_chunk_fwd_segments``); fixed-length inputs.  Shapes and results as
+    ``gla_chunk_fwd``; ``workspace`` (uint8 GPU tensor) is allocated with torch
+    when not given."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    _check_gpu("q", q)
+    dt = q.dtype
+    _check_gpu("k", k, dt, q.shape, device=q.device)
+    _check_gpu("g", g, dt, q.shape, device=q.device)
+    _check_gpu("v", v, dt, (B, H, T, dv), device=q.device)
+    if initial_state is not None:
+        _check_gpu("initial_state", initial_state, torch.float32, (B, H, dk, dv), device=q.device)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=dt, device=q.device)
+    else:
+        _check_gpu("out", out, dt, (B, H, T, dv), device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif final_state is not None:
+        _check_gpu("final_state", final_state, torch.float32, (B, H, dk, dv), device=q.device)
+    lib = load_library()
+    need = int(lib.gla_chunk_fwd_segments_workspace_size(B, H, T, dk, dv, int(num_segments)))
+    if need and workspace is None:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _aligned_workspace(workspace, q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.gla_chunk_fwd_segments(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(initial_state),
+                                        _ptr(out), _ptr(final_state), B, H, T, dk, dv,
+                                        int(chunk_size), _dtype_code(q), int(num_segments), ws_ptr,
+                                        ws_bytes, ctypes.c_void_p(stream))
+    if rc != GLA_OK:
+        raise GLAError(rc, last_error())
+    return out, final_state
 
 
 def bwd_workspace_size(q, v, cu_seqlens=None, chunk_size: int = 64) -> int:

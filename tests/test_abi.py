@@ -33,8 +33,10 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     assert names == ["gdn_chunk_fwd", "gla_chunk_bwd", "gla_chunk_bwd_workspace_size", "gla_chunk_fwd",
-                     "gla_chunk_fwd_noalloc", "gla_chunk_fwd_workspace_size", "gla_chunk_fwd_ws",
-                     "gla_last_error", "gla_recurrent_step", "gla_status_string"]
+                     "gla_chunk_fwd_noalloc", "gla_chunk_fwd_segments",
+                     "gla_chunk_fwd_segments_workspace_size", "gla_chunk_fwd_workspace_size",
+                     "gla_chunk_fwd_ws", "gla_last_error", "gla_recurrent_step", "gla_split_plan",
+                     "gla_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -143,7 +145,7 @@ def test_workspace_size_only_for_few_long_fixed_length_sequences(lib):
     assert lib.gla_chunk_fwd_workspace_size(0, 8, 16, 2048, 128, 128, 64, 0) == 0
     assert lib.gla_chunk_fwd_workspace_size(16, 1, 16, 33000, 128, 256, 64, 0) == 0
     assert lib.gla_chunk_fwd_workspace_size(0, 1, 16, 65536, 64, 64, 64, 1) == 0
-    assert lib.gla_chunk_fwd_workspace_size(0, 1, 16, 600, 128, 128, 64, 0) == 0   # too short
+    assert lib.gla_chunk_fwd_workspace_size(0, 1, 16, 256, 128, 128, 64, 0) == 0   # too short
     # 16 units of d_v 128 take the 128-column slice when split: 16 segments fill 256 CUs
     # (the CPU build reads no device and plans for 256), fp32 states plus decays per segment
     assert lib.gla_chunk_fwd_workspace_size(0, 1, 16, 65536, 128, 128, 64, 0) == \
@@ -253,3 +255,104 @@ def test_gdn_chunk_fwd_rejects(lib, kw, status, needle):
 
 def test_gdn_zero_tokens_without_outputs_is_a_noop(lib):
     assert _gdn(lib, q=None, k=None, v=None, g=None, beta=None, o=None, T=0) == 0
+
+
+# ------------------------------------------------------------ sequence-split plan
+def _model_constants():
+    text = open(os.path.join(ROOT, "sub_quadratic_sequence_amd", "csrc", "split_model.h")).read()
+    return {m.group(1): float(m.group(2))
+            for m in re.finditer(r"constexpr double (k\w+) = ([0-9.eE+-]+);", text)}
+
+
+def _plan(lib, units, T, dv, dtype=0, ncu=256):
+    seg = ctypes.c_int(-1)
+    lib.gla_split_plan.restype = ctypes.c_int
+    lib.gla_split_plan.argtypes = [ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    n = lib.gla_split_plan(units, T, dv, dtype, ncu, ctypes.byref(seg))
+    return n, seg.value
+
+
+def _model_best(c, units, T, dv, ncu):
+    """The documented choice, by brute force: the unsplit time mu_1 N + mu_0 against
+    lambda_1 L + lambda_2 segments + lambda_0 for every segment count whose work items
+    fit one wave (ties keep fewer segments)."""
+    nch = -(-T // 64)
+    best_t, best = c["kMu1"] * nch + c["kMu0"], (1, T)
+    items = units * (dv // 128 if dv % 128 == 0 else dv // 64)
+    for n in range(2, nch + 1):
+        if items * n > ncu:
+            break
+        L = -(-nch // n)
+        ns = -(-nch // L)
+        t = c["kLambda1"] * L + c["kLambda2"] * ns + c["kLambda0"]
+        if t < best_t:
+            best_t, best = t, (ns, L * 64)
+    return best
+
+
+@pytest.mark.parametrize("ncu", [256, 80])
+def test_split_plan_minimises_the_model(lib, ncu):
+    c = _model_constants()
+    assert set(c) == {"kLambda1", "kLambda2", "kLambda0", "kMu1", "kMu0"}
+    seen = set()
+    for units in (1, 2, 3, 5, 8, 16, 24, 33, 64, 100):
+        for T in (1, 63, 64, 65, 600, 1025, 2048, 4097, 16384, 65536, 100000):
+            for dv in (64, 128, 192, 256):
+                n, seg = _plan(lib, units, T, dv, ncu=ncu)
+                if units * (dv // 64) >= ncu:
+                    assert (n, seg) == (1, T)   # the unsplit call already fills the device
+                    continue
+                assert (n, seg) == _model_best(c, units, T, dv, ncu), (units, T, dv)
+                if n > 1:
+                    items = units * (dv // 128 if dv % 128 == 0 else dv // 64)
+                    assert seg % 64 == 0 and (n - 1) * seg < T <= n * seg
+                    assert items * n <= ncu
+                seen.add(n > 1)
+    assert seen == {True, False}   # the grid reaches both decisions
+
+
+def test_split_plan_declines_what_it_cannot_split(lib):
+    assert _plan(lib, 4, 65536, 128, dtype=1) == (1, 65536)   # fp32
+    assert _plan(lib, 4, 0, 128) == (1, 0)
+    assert _plan(lib, 0, 4096, 128) == (1, 4096)
+    assert _plan(lib, 4, 4096, 96) == (1, 4096)   # d_v not a multiple of 64
+    assert _plan(lib, 4, 4096, 128, ncu=0) == (1, 4096)
+    # the plan behind the workspace size of gla_chunk_fwd_ws (the CPU build plans for 256 CUs)
+    n, _ = _plan(lib, 16, 65536, 128)
+    assert lib.gla_chunk_fwd_workspace_size(0, 1, 16, 65536, 128, 128, 64, 0) == \
+        n * 16 * (128 * 128 + 128) * 4
+
+
+def test_segments_workspace_size(lib):
+    lib.gla_chunk_fwd_segments_workspace_size.restype = ctypes.c_size_t
+    f = lib.gla_chunk_fwd_segments_workspace_size
+    def rnd(x):
+        return -(-x // 256) * 256
+    assert f(1, 4, 4096, 128, 128, 1) == 0
+    assert f(1, 4, 4096, 128, 128, 7) == rnd(4 * 7 * 128 * 128 * 4) + rnd(4 * 7 * 128 * 4)
+    # 13 requested segments of 64 chunks give L = 5 chunks, 13 segments; 60 give L = 2, 32
+    assert f(2, 3, 4096, 64, 256, 13) == rnd(6 * 13 * 64 * 256 * 4) + rnd(6 * 13 * 64 * 4)
+    assert f(2, 3, 4096, 64, 256, 60) == rnd(6 * 32 * 64 * 256 * 4) + rnd(6 * 32 * 64 * 4)
+    assert f(1, 4, 4096, 128, 128, 0) == 0 and f(1, 4, 4096, 128, 128, 65) == 0
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(num_segments=0), 1, "num_segments = 0"),
+    (dict(num_segments=65), 1, "must be in [1, 64]"),
+    (dict(num_segments=4, dtype=1), 2, "bf16 inputs only"),
+    (dict(num_segments=4), 1, "workspace of 0 bytes"),
+    (dict(num_segments=4, ws=FAKE + 16, nbytes=1 << 30), 1, "256-byte aligned"),
+    (dict(num_segments=4, T=-1), 1, ""),
+])
+def test_chunk_fwd_segments_rejects(lib, kw, status, needle):
+    from sub_quadratic_sequence_amd import gla
+
+    P = ctypes.c_void_p
+    a = dict(B=1, H=4, T=4096, dtype=0, ws=None, nbytes=0)
+    a.update(kw)
+    rc = lib.gla_chunk_fwd_segments(P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, P(FAKE), None, a["B"],
+                                    a["H"], a["T"], 128, 128, 64, a["dtype"], a["num_segments"],
+                                    P(a["ws"]) if a["ws"] else None, a["nbytes"], None)
+    assert rc == status
+    assert needle in gla.last_error()

@@ -494,14 +494,73 @@ def test_sequence_split_matches_oracle(dev, label, B, H, T, dk, dv, gate, s0):
     say(f"sequence split {label}: B={B} H={H} T={T} dk={dk} dv={dv} gate={gate} s0={s0}")
     d = I.chunk_inputs(w, gate=gate, s0=s0)
     args = [d[n].to(dev) for n in "qkvg"]
-    assert gla.workspace_size(args[0], args[2]) > 0   # the split is taken
     s0_dev = None if d["s0"] is None else d["s0"].to(dev)
+    # the planned call (gla_chunk_fwd_ws) and a forced 4-segment split
+    nseg, _ = gla.split_plan(B * H, T, dv)
+    assert (gla.workspace_size(args[0], args[2]) > 0) == (nseg > 1)
     o, sf = gla.gla_chunk_fwd(*args, initial_state=s0_dev, output_final_state=True)
+    o4, s4 = gla.gla_chunk_fwd_segments(*args, 4, initial_state=s0_dev, output_final_state=True)
     o1, s1 = gla.gla_chunk_fwd(*args, initial_state=s0_dev, output_final_state=True, split=False)
     torch.cuda.synchronize()
+    say(f"  planned segments {nseg}")
     _check_fixed(d, o, sf, d["s0"], TOL_BF16, f"split {label}")
+    _check_fixed(d, o4, s4, d["s0"], TOL_BF16, f"4 segments {label}")
     assert unit_err_fixed(o.float(), o1.float()) <= TOL_BF16
     assert unit_err_fixed(sf, s1) <= TOL_BF16
+
+
+SEGMENT_GRID = [
+    # (B, H, T, dv): segment counts 1, 2, 5, 16 and one segment per chunk
+    (1, 1, 1025, 128),
+    (1, 3, 2048, 128),
+    (2, 4, 4100, 256),
+    (1, 8, 3000, 64),
+]
+
+
+@pytest.mark.parametrize("B,H,T,dv", SEGMENT_GRID, ids=[f"B{c[0]}H{c[1]}T{c[2]}dv{c[3]}" for c in SEGMENT_GRID])
+def test_forced_segment_counts_match_oracle(dev, B, H, T, dv):
+    """gla_chunk_fwd_segments at segment counts from 1 to one per chunk (ragged last
+    segments included): every count matches the oracle."""
+    from sub_quadratic_sequence_amd import gla
+
+    w = I.ChunkWorkload("segments", B=B, H=H, T=T, dk=128, dv=dv, dtype="bf16", seed=43)
+    d = I.chunk_inputs(w, gate="weak", s0=True)
+    args = [d[n].to(dev) for n in "qkvg"]
+    o_ref, s_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], s0=d["s0"], nthreads=NTHREADS)
+    nch = -(-T // 64)
+    for n in (1, 2, 5, 16, nch):
+        say(f"forced segments: B={B} H={H} T={T} dv={dv}, {n} requested")
+        o, sf = gla.gla_chunk_fwd_segments(*args, n, initial_state=d["s0"].to(dev),
+                                           output_final_state=True)
+        torch.cuda.synchronize()
+        e_o, e_s = unit_err_fixed(o, o_ref), unit_err_fixed(sf, s_ref)
+        print(f"  O err {e_o:.3e}  S err {e_s:.3e}", flush=True)
+        assert e_o <= TOL_BF16 and e_s <= TOL_BF16, (n, e_o, e_s)
+
+
+PLAN_GRID = [(1, 1, 700), (1, 4, 2048), (2, 8, 4096), (1, 32, 1100), (4, 16, 1536), (8, 16, 640)]
+
+
+@pytest.mark.parametrize("B,H,T", PLAN_GRID, ids=[f"B{c[0]}H{c[1]}T{c[2]}" for c in PLAN_GRID])
+def test_planned_split_across_units_and_lengths(dev, B, H, T):
+    """The cost model's plan across a grid of (B x H, T): the planned call matches
+    the oracle, and its workspace follows the plan."""
+    from sub_quadratic_sequence_amd import gla
+
+    w = I.ChunkWorkload("plan", B=B, H=H, T=T, dk=128, dv=128, dtype="bf16", seed=47)
+    d = I.chunk_inputs(w, gate="weak", s0=True)
+    args = [d[n].to(dev) for n in "qkvg"]
+    nseg, seg_len = gla.split_plan(B * H, T, 128)
+    say(f"planned split: B={B} H={H} T={T} -> {nseg} segments of {seg_len} tokens")
+    need = gla.workspace_size(args[0], args[2])
+    if nseg > 1:
+        assert need == -(-B * H * nseg * 128 * 128 * 4 // 256) * 256 + -(-B * H * nseg * 128 * 4 // 256) * 256
+    else:
+        assert need == 0
+    o, sf = gla.gla_chunk_fwd(*args, initial_state=d["s0"].to(dev), output_final_state=True)
+    torch.cuda.synchronize()
+    _check_fixed(d, o, sf, d["s0"], TOL_BF16, f"plan B{B}H{H}T{T}")
 
 
 def test_sequence_split_extreme_gates(dev):
