@@ -18,6 +18,11 @@ for every independent unit (sequence, head), one token at a time.
   second, independently written evaluation the C code is checked against.
 * ``decode_step`` - one token of the same recurrence per sequence.
 
+Parity unpinned against the pages for the update form: the page prints no
+update equation and no values, so the form above is the plainest reading of
+what it names, and no pin ties it to the page itself.  The pins check that
+this code computes that reading.
+
 Pins (``tests/test_oracle_gdn.py``): beta = 0 closed form, the exact-retrieval
 identity (q_t = k_t, beta_t = 1/|k_t|^2 gives o_t = v_t), an orthonormal-key
 overwrite closed form, the brute-force unrolled product of explicit transition
