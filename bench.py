@@ -328,7 +328,7 @@ def bench_varlen(args, torch, gla, inputs):
     return dict(w=w, t=t, flops=flops, bytes=nbytes, tokens=T)
 
 
-def bench_backward(args, torch, gla, inputs):
+def bench_backward(args, torch, gla, inputs, saved=True):
     """The backward pass on the training shape (B8 H16 T2048 d128, no initial
     state, gradient of the outputs only): one gla_chunk_bwd call = the chunk-state
     pass plus the backward kernel."""
@@ -347,7 +347,28 @@ def bench_backward(args, torch, gla, inputs):
     steps = max(1, args.steps // 4)
     wall, gpu = time_launches(step, steps, max(1, args.warmup // 4), torch, args.preroll * 0.5)
     flops, nbytes = bwd_work(w.B, w.H, w.T, w.dk, w.dv, 16, 2)
-    return dict(w=w, wall=wall, gpu=gpu, flops=flops, bytes=nbytes, tokens=w.B * w.T, steps=steps)
+    res = dict(w=w, wall=wall, gpu=gpu, flops=flops, bytes=nbytes, tokens=w.B * w.T, steps=steps)
+    if not saved:
+        return res
+    # the training step with the forward keeping its chunk states: gla_chunk_fwd_states
+    # (the forward plus the states) and gla_chunk_bwd_saved (no state recomputation),
+    # against gla_chunk_fwd and gla_chunk_bwd
+    o = torch.empty_like(v)
+    gla.gla_chunk_fwd_states(q, k, v, g, out=o, chunk_states=ws)
+
+    def fwd_states():
+        gla.gla_chunk_fwd_states(q, k, v, g, out=o, chunk_states=ws)
+
+    def bwd_saved():
+        gla.gla_chunk_bwd(q, k, v, g, do, workspace=ws, out=outs, states_saved=True)
+
+    def fwd_plain():
+        gla.gla_chunk_fwd(q, k, v, g, out=o)
+
+    _, res["fwd_states_gpu"] = time_launches(fwd_states, steps, 2, torch, 0.0)
+    _, res["bwd_saved_gpu"] = time_launches(bwd_saved, steps, 2, torch, 0.0)
+    _, res["fwd_plain_gpu"] = time_launches(fwd_plain, steps, 2, torch, 0.0)
+    return res
 
 
 def bench_gdn(args, torch, gla, inputs):
@@ -516,7 +537,7 @@ def main():
         bench_long(args, torch, gla, inputs)
         bench_varlen(args, torch, gla, inputs)
         args.steps = 12   # the backward and GDN legs run steps/4 and steps/2 launches
-        bench_backward(args, torch, gla, inputs)
+        bench_backward(args, torch, gla, inputs, saved=False)
         bench_gdn(args, torch, gla, inputs)
         log("[bench] pmc launches done")
         return
@@ -526,7 +547,9 @@ def main():
         return
     if args.only == "bwd":
         bw = bench_backward(args, torch, gla, inputs)
-        log(f"[bench] backward {bw['gpu'] * 1e6:.1f} us/call")
+        log(f"[bench] backward {bw['gpu'] * 1e6:.1f} us/call; saved states: forward "
+            f"{bw['fwd_states_gpu'] * 1e6:.1f} us (plain {bw['fwd_plain_gpu'] * 1e6:.1f}), backward "
+            f"{bw['bwd_saved_gpu'] * 1e6:.1f} us")
         return
     if args.only == "gdn":
         args.no_cpu_baseline = True
@@ -643,6 +666,14 @@ def main():
                          "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": bw["bytes"],
                          "algorithmic_flops_per_call": bw["flops"],
                          "note": "two kernels per call: chunk-state pass, backward"},
+            "saved_states": {
+                "note": "training step with the forward keeping its chunk states "
+                        "(gla_chunk_fwd_states + gla_chunk_bwd_saved) against recomputing them "
+                        "(gla_chunk_fwd + gla_chunk_bwd); HIP-event time per call",
+                "fwd_states_us": bw["fwd_states_gpu"] * 1e6, "bwd_saved_us": bw["bwd_saved_gpu"] * 1e6,
+                "fwd_us": bw["fwd_plain_gpu"] * 1e6, "bwd_us": bw["gpu"] * 1e6,
+                "step_us_saved": (bw["fwd_states_gpu"] + bw["bwd_saved_gpu"]) * 1e6,
+                "step_us_recomputed": (bw["fwd_plain_gpu"] + bw["gpu"]) * 1e6},
         }
     if not args.no_gdn:
         gd = bench_gdn(args, torch, gla, inputs)

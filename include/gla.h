@@ -254,6 +254,43 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
                   void* stream);
 
 /*
+ * The forward of gla_chunk_fwd (unsplit, 64-column d_v slices) that also writes
+ * the bf16 state entering every 64-token chunk, in the layout and place the
+ * backward's chunk-state pass uses: chunk_states is the workspace a later
+ * gla_chunk_bwd_saved call on the same inputs is given (at least
+ * gla_chunk_bwd_workspace_size(...) bytes, 256-byte aligned, owned by the
+ * caller; this call writes its chunk-state part).  The states are the ones
+ * gla_chunk_bwd computes for itself, bitwise; o and final_state are gla_chunk_fwd's,
+ * up to the slice width (bitwise where gla_chunk_fwd also takes 64 columns).
+ * Same recurrence as gla_chunk_fwd (page "Gated Linear Attention (GLA) ...",
+ * section "The Gated Recurrent Update"), one state per chunk boundary.
+ *
+ * Arguments, layouts and errors as for gla_chunk_fwd, with the backward's limits:
+ * dtype GLA_BF16 and dk, dv in {64, 128}, else GLA_ERR_UNSUPPORTED; a missing,
+ * small or misaligned chunk_states buffer gives GLA_ERR_INVALID_ARG.
+ */
+int gla_chunk_fwd_states(const void* q, const void* k, const void* v, const void* g,
+                         const float* initial_state, void* o, float* final_state,
+                         const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk,
+                         int dv, int chunk_size, int dtype, void* chunk_states,
+                         size_t chunk_states_bytes, void* stream);
+
+/*
+ * gla_chunk_bwd for a workspace whose chunk states a gla_chunk_fwd_states call on
+ * the same k, v, g, initial_state and cu_seqlens has already written: the chunk-
+ * state pass is skipped, everything else (the sequence split's passes, the
+ * gradients) runs as in gla_chunk_bwd, with the same results.  Arguments and
+ * errors as for gla_chunk_bwd.  Different inputs, or a workspace written for
+ * another shape, give wrong gradients without an error.
+ */
+int gla_chunk_bwd_saved(const void* q, const void* k, const void* v, const void* g,
+                        const float* initial_state, const void* d_o, const float* d_final_state,
+                        void* d_q, void* d_k, void* d_v, void* d_g, float* d_initial_state,
+                        const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk, int dv,
+                        int chunk_size, int dtype, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
  * One recurrent decode step for N sequences x H heads, in place on the state.
  *
  *   q, k, g  [N, H, dk]  dtype;   v  [N, H, dv]  dtype

@@ -125,6 +125,12 @@ __device__ __forceinline__ void launder(int& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void launder(unsigned& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void launder(float& x) { asm volatile("" : "+v"(x)); }
 
+// x from lane QP-permuted inside each quad of lanes (DPP quad_perm control QP)
+template <int QP>
+__device__ __forceinline__ float quad_perm(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), QP, 0xF, 0xF, false));
+}
+
 // consumer state-row map: accumulator tile rb, row m -> key channel
 __device__ __forceinline__ int srow(int rb, int m) {
   return 32 * (rb >> 1) + 8 * (m >> 2) + 4 * (rb & 1) + (m & 3);
@@ -132,7 +138,9 @@ __device__ __forceinline__ int srow(int rb, int m) {
 
 }  // namespace pipe
 
-// MODE kFull: the forward pass (outputs, and the final state of unsplit sequences).
+// MODE kFull: the forward pass (outputs, and the final state of unsplit sequences;
+// with 64-column slices and prm.hs set, also the bf16 state entering every chunk,
+// as kChunkStates writes it).
 // MODE kChunkStates: no outputs; the state entering every chunk, in bf16, to
 // prm.hs (the backward pass's recomputed states).
 // MODE kSegGrad: the state-gradient pass of the backward's sequence split (k and v
@@ -694,15 +702,20 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     // 64 rows (8 KB) further on.
     constexpr unsigned kHalfX = (unsigned)tr_swz(64) << 4, kHalfOff = 64u * 128u;
     unsigned short* og = reinterpret_cast<unsigned short*>(prm.o) + rowbase * DV + vcol0;
-    // chunk-state mode: this unit's first slot, and the lane's element of a slot
-    // for tile 0, slot 0 (chunk_state_index with the tile and slot added per store)
+    // chunk states (the chunk-state mode, or the unsplit 64-column full pass when
+    // prm.hs is set): this unit's first slot, and the lane's element of a slot for
+    // tile 0, slot 0 (the tile and slot are added per store)
+    constexpr bool HS = STATES || (FULL && NT == 1);
     unsigned short* hs_unit = nullptr;
     int hs_lane = 0;
-    if constexpr (STATES) {
-      const long slot0 = prm.cu ? (long)h * prm.slots + n + bos / C
-                                : (long)h * prm.slots + n + (long)n * prm.T / C;
-      hs_unit = prm.hs + slot0 * DK * DV;
-      hs_lane = ((vt * 4 + cw) * NRB * 16 + gq) * 16 + m;
+    if constexpr (HS) {
+      if (STATES || prm.hs) {
+        const long slot0 = prm.cu ? (long)h * prm.slots + n + bos / C
+                                  : (long)h * prm.slots + n + (long)n * prm.T / C;
+        hs_unit = prm.hs + slot0 * DK * DV;
+        // chunk_state_index(srow(0, 4gq + (m & 3)), 64vt + 16cw + 4(m >> 2)); tile rb adds 256
+        hs_lane = ((((vt * 4 + cw) * NRB * 4 + (m & 3)) * 4 + gq) * 16) + 4 * (m >> 2);
+      }
     }
     f32x4 sacc[NT][NRB];
 #pragma unroll
@@ -862,15 +875,35 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         }
       }
 
-      if constexpr (STATES) {
-        // the state entering chunk u, bf16: for each (tile rb, slot s) the wave's
-        // 64 lanes write 128 contiguous bytes of the slot
-        unsigned short* const hu = hs_unit + (long)u * DK * DV;
+      if constexpr (HS) {
+        if (STATES || hs_unit) {
+          // the state entering chunk u, bf16, in the chunk_state_index order.  Lane
+          // (m = 4a + j, gq) holds rows srow(rb, 4gq + 0..3) of column 16cw + m; a
+          // 4 x 4 transpose inside each quad of lanes (two DPP exchange stages)
+          // leaves it row srow(rb, 4gq + j) of columns 16cw + 4a .. +3, which are 8
+          // contiguous bytes of the slot: 8 eight-byte stores per lane and chunk.
+          unsigned short* const hu = hs_unit + (long)u * DK * DV;
+          const bool o1 = lane & 1, o2 = lane & 2;
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
+          for (int rb = 0; rb < NRB; ++rb) {
+            float y[4], z[4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
-            hu[hs_lane + ((rb * 4 + s) << 6)] = f32_to_bf16_bits(sacc[0][rb][s]);
+            for (int p = 0; p < 2; ++p) {   // lane bit 0 <-> slot bit 0
+              const float x0 = sacc[0][rb][2 * p], x1 = sacc[0][rb][2 * p + 1];
+              const float r = quad_perm<0xB1>(o1 ? x0 : x1);   // [1, 0, 3, 2]
+              y[2 * p] = o1 ? r : x0;
+              y[2 * p + 1] = o1 ? x1 : r;
+            }
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {   // lane bit 1 <-> slot bit 1
+              const float r = quad_perm<0x4E>(o2 ? y[p] : y[p + 2]);   // [2, 3, 0, 1]
+              z[p] = o2 ? r : y[p];
+              z[p + 2] = o2 ? y[p + 2] : r;
+            }
+            *reinterpret_cast<uint2*>(hu + hs_lane + rb * 256) =
+                uint2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+          }
+        }
       }
       // ---- state: S <- post * (pre * S + KT^T V) ----
       // every operand is read first (the output phase's registers are free by now),

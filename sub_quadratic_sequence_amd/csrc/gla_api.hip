@@ -460,14 +460,19 @@ size_t gla_chunk_bwd_workspace_size(int num_seqs, int B, int H, int T, int dk, i
   return states + (nseg > 1 ? split_bytes(nseq * H, nseg, dk, dv) : 0);
 }
 
-int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
-                  const float* initial_state, const void* d_o, const float* d_final_state,
-                  void* d_q, void* d_k, void* d_v, void* d_g, float* d_initial_state,
-                  const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk, int dv,
-                  int chunk_size, int dtype, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+}  // extern "C"
+
+namespace {
+
+// gla_chunk_bwd, and gla_chunk_bwd_saved (states_ready: the workspace already
+// holds the chunk states, written by gla_chunk_fwd_states)
+int chunk_bwd_impl(const char* fn, bool states_ready, const void* q, const void* k, const void* v,
+                   const void* g, const float* initial_state, const void* d_o,
+                   const float* d_final_state, void* d_q, void* d_k, void* d_v, void* d_g,
+                   float* d_initial_state, const int32_t* cu_seqlens, int num_seqs, int B, int H,
+                   int T, int dk, int dv, int chunk_size, int dtype, void* workspace,
+                   size_t workspace_bytes, void* stream) {
   g_last_error[0] = '\0';
-  const char* fn = "gla_chunk_bwd";
   if (dtype != GLA_BF16 && dtype != GLA_F32)
     return fail(GLA_ERR_INVALID_ARG, "%s: dtype %d is not GLA_BF16 or GLA_F32", fn, dtype);
   if (dtype != GLA_BF16)
@@ -578,7 +583,7 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
   fp.seg_decay = nullptr;
   fp.hs = prm.hs;
   fp.slots = prm.slots;
-  int rc = gla::launch_chunk_fwd_states(fp, dk, (int)(units * nvt), s);
+  int rc = states_ready ? 0 : gla::launch_chunk_fwd_states(fp, dk, (int)(units * nvt), s);
   if (rc != 0) return launch_status(fn, rc, dk, dtype);
   if (nseg > 1) {
     // 2. each later segment's own state gradient and decay, 3. every segment's
@@ -614,6 +619,72 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
   }
   // 4. the gradients chunk by chunk, last to first, per (unit, segment)
   rc = gla::launch_chunk_bwd(prm, dk, dv, (int)(units * nseg), s);
+  return launch_status(fn, rc, dk, dtype);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
+                  const float* initial_state, const void* d_o, const float* d_final_state,
+                  void* d_q, void* d_k, void* d_v, void* d_g, float* d_initial_state,
+                  const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk, int dv,
+                  int chunk_size, int dtype, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  return chunk_bwd_impl("gla_chunk_bwd", false, q, k, v, g, initial_state, d_o, d_final_state, d_q, d_k,
+                        d_v, d_g, d_initial_state, cu_seqlens, num_seqs, B, H, T, dk, dv, chunk_size,
+                        dtype, workspace, workspace_bytes, stream);
+}
+
+int gla_chunk_bwd_saved(const void* q, const void* k, const void* v, const void* g,
+                        const float* initial_state, const void* d_o, const float* d_final_state,
+                        void* d_q, void* d_k, void* d_v, void* d_g, float* d_initial_state,
+                        const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk, int dv,
+                        int chunk_size, int dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return chunk_bwd_impl("gla_chunk_bwd_saved", true, q, k, v, g, initial_state, d_o, d_final_state, d_q,
+                        d_k, d_v, d_g, d_initial_state, cu_seqlens, num_seqs, B, H, T, dk, dv,
+                        chunk_size, dtype, workspace, workspace_bytes, stream);
+}
+
+int gla_chunk_fwd_states(const void* q, const void* k, const void* v, const void* g,
+                         const float* initial_state, void* o, float* final_state,
+                         const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk,
+                         int dv, int chunk_size, int dtype, void* chunk_states,
+                         size_t chunk_states_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  const char* fn = "gla_chunk_fwd_states";
+  gla::ChunkParams prm;
+  long long units = 0;
+  bool nothing = false;
+  const int st = check_chunk_args(fn, q, k, v, g, initial_state, o, final_state, cu_seqlens, num_seqs,
+                                  B, H, T, dk, dv, chunk_size, dtype, prm, units, nothing);
+  if (st != GLA_OK) return st;
+  if (dtype != GLA_BF16)
+    return fail(GLA_ERR_UNSUPPORTED, "%s: chunk states come from the bf16 path only", fn);
+  if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+    return fail(GLA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d (each must be 64 or 128, as for gla_chunk_bwd)", fn,
+                dk, dv);
+  if (!fits_i32(((long long)T / 64 + 1) * dk * dv * 2))
+    return fail(GLA_ERR_INVALID_ARG, "%s: T=%d is too long for one call's chunk states", fn, T);
+  if (nothing) return GLA_OK;
+  const size_t need = gla_chunk_bwd_workspace_size(cu_seqlens ? num_seqs : 0, B, H, T, dk, dv,
+                                                   chunk_size, dtype);
+  if (!chunk_states || chunk_states_bytes < need)
+    return fail(GLA_ERR_INVALID_ARG, "%s: chunk_states of %zu bytes given, %zu needed", fn,
+                chunk_states ? chunk_states_bytes : (size_t)0, need);
+  if ((reinterpret_cast<uintptr_t>(chunk_states) & 255u) != 0)
+    return fail(GLA_ERR_INVALID_ARG, "%s: chunk_states is not 256-byte aligned", fn);
+  const long long nseq = cu_seqlens ? num_seqs : B;
+  const long long tokens = cu_seqlens ? (long long)T : (long long)B * T;
+  // the backward's layout: 64-column slices, one run over every sequence
+  prm.dvt = 64;
+  prm.nvt = dv / 64;
+  prm.hs = static_cast<unsigned short*>(chunk_states);
+  prm.slots = (int)(nseq + tokens / 64 + 1);
+  const int rc = gla::launch_chunk_fwd(prm, dk, dtype, (int)(units * prm.nvt),
+                                       reinterpret_cast<hipStream_t>(stream));
   return launch_status(fn, rc, dk, dtype);
 }
 

@@ -56,6 +56,11 @@ def load_library():
         lib.gla_chunk_bwd_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
         lib.gla_chunk_bwd.restype = I
         lib.gla_chunk_bwd.argtypes = [P] * 13 + [I] * 8 + [P, ctypes.c_size_t, P]
+        lib.gla_chunk_bwd_saved.restype = I
+        lib.gla_chunk_bwd_saved.argtypes = [P] * 13 + [I] * 8 + [P, ctypes.c_size_t, P]
+        lib.gla_chunk_fwd_states.restype = I
+        lib.gla_chunk_fwd_states.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P,
+                                             ctypes.c_size_t, P]
         lib.gdn_chunk_fwd.restype = I
         lib.gdn_chunk_fwd.argtypes = [P] * 9 + [I] * 8 + [P]
         lib.gla_recurrent_step.restype = I
@@ -266,8 +271,57 @@ def _aligned_workspace(workspace, device):
     return ctypes.c_void_p(base + off), max(0, workspace.numel() - off)
 
 
+def gla_chunk_fwd_states(q, k, v, g, initial_state=None, output_final_state=False, cu_seqlens=None,
+                         chunk_size: int = 64, out=None, final_state=None, chunk_states=None):
+    """The forward (``gla_chunk_fwd_states``, bfloat16, d_k and d_v in {64, 128},
+    unsplit, 64-column slices) that also writes the state entering every chunk into
+    ``chunk_states``, the backward's workspace (a uint8 GPU tensor of at least
+    ``bwd_workspace_size`` bytes; allocated when not given).  Returns
+    ``(o, final_state, chunk_states)``; pass ``chunk_states`` to ``gla_chunk_bwd``
+    with ``states_saved=True`` to skip the backward's state recomputation."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    _check_gpu("q", q)
+    dt = q.dtype
+    _check_gpu("k", k, dt, q.shape, device=q.device)
+    _check_gpu("g", g, dt, q.shape, device=q.device)
+    _check_gpu("v", v, dt, (B, H, T, dv), device=q.device)
+    nseq, num_seqs = B, 0
+    if cu_seqlens is not None:
+        _check_gpu("cu_seqlens", cu_seqlens, torch.int32, device=q.device)
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be 1-D with num_seqs + 1 >= 2 offsets")
+        num_seqs = cu_seqlens.numel() - 1
+        nseq = num_seqs
+    if initial_state is not None:
+        _check_gpu("initial_state", initial_state, torch.float32, (nseq, H, dk, dv), device=q.device)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=dt, device=q.device)
+    else:
+        _check_gpu("out", out, dt, (B, H, T, dv), device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif final_state is not None:
+        _check_gpu("final_state", final_state, torch.float32, (nseq, H, dk, dv), device=q.device)
+    if chunk_states is None:
+        chunk_states = torch.empty(bwd_workspace_size(q, v, cu_seqlens, chunk_size) + 256,
+                                   dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = _aligned_workspace(chunk_states, q.device)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.gla_chunk_fwd_states(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(initial_state),
+                                      _ptr(out), _ptr(final_state), _ptr(cu_seqlens), num_seqs, B, H,
+                                      T, dk, dv, int(chunk_size), _dtype_code(q), ws_ptr, ws_bytes,
+                                      ctypes.c_void_p(stream))
+    if rc != GLA_OK:
+        raise GLAError(rc, last_error())
+    return out, final_state, chunk_states
+
+
 def gla_chunk_bwd(q, k, v, g, do, initial_state=None, d_final_state=None, cu_seqlens=None,
-                  chunk_size: int = 64, want_d_initial_state=None, workspace=None, out=None):
+                  chunk_size: int = 64, want_d_initial_state=None, workspace=None, out=None,
+                  states_saved: bool = False):
     """Chunkwise GLA backward (C entry point ``gla_chunk_bwd``).
 
     Gradients of sum(o * do) + sum(final_state * d_final_state) for the forward
@@ -277,8 +331,13 @@ def gla_chunk_bwd(q, k, v, g, do, initial_state=None, d_final_state=None, cu_seq
     ``d_initial_state`` is computed when ``initial_state`` is given (or
     ``want_d_initial_state``), else None.  The workspace (the chunk states) is a
     torch allocation unless ``workspace`` (a uint8 GPU tensor) is passed;
-    ``out`` optionally supplies (dq, dk, dv, dg) to write into.
+    ``out`` optionally supplies (dq, dk, dv, dg) to write into.  With
+    ``states_saved`` the workspace is the ``chunk_states`` of a
+    ``gla_chunk_fwd_states`` call on the same inputs, and the backward
+    (``gla_chunk_bwd_saved``) skips recomputing them.
     """
+    if states_saved and workspace is None:
+        raise ValueError("states_saved needs the workspace that gla_chunk_fwd_states filled")
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     _check_gpu("q", q)
@@ -315,35 +374,61 @@ def gla_chunk_bwd(q, k, v, g, do, initial_state=None, d_final_state=None, cu_seq
             need = bwd_workspace_size(q, v, cu_seqlens, chunk_size)
             workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
         ws_ptr, ws_bytes = _aligned_workspace(workspace, q.device)
-        rc = lib.gla_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(initial_state), _ptr(do),
-                               _ptr(d_final_state), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg),
-                               _ptr(ds0), _ptr(cu_seqlens), num_seqs, B, H, T, dk, dv,
-                               int(chunk_size), _dtype_code(q), ws_ptr, ws_bytes,
-                               ctypes.c_void_p(stream))
+        entry = lib.gla_chunk_bwd_saved if states_saved else lib.gla_chunk_bwd
+        rc = entry(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(initial_state), _ptr(do),
+                   _ptr(d_final_state), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(ds0),
+                   _ptr(cu_seqlens), num_seqs, B, H, T, dk, dv, int(chunk_size), _dtype_code(q),
+                   ws_ptr, ws_bytes, ctypes.c_void_p(stream))
     if rc != GLA_OK:
         raise GLAError(rc, last_error())
     return dq, dk_, dv_, dg, ds0
 
 
+def _saves_states(q, v, cu_seqlens):
+    """Whether the autograd forward keeps the chunk states: when the planned forward
+    runs unsplit on 64-column slices anyway, so that writing them costs the forward
+    nothing but the stores (long sequences of few units keep the faster split and
+    let the backward recompute them)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if q.dtype != torch.bfloat16 or dk not in (64, 128) or dv not in (64, 128):
+        return False
+    if workspace_size(q, v, cu_seqlens) > 0:
+        return False
+    nseq = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+    return dv == 64 or nseq * H * (dv // 128) < cus
+
+
 class GLAFunction(torch.autograd.Function):
     """Autograd wrapper: forward ``gla_chunk_fwd``, backward ``gla_chunk_bwd``
     (bfloat16, d_k and d_v in {64, 128}).  ``apply(q, k, v, g, initial_state,
-    cu_seqlens)`` returns ``(o, final_state)``."""
+    cu_seqlens, save_states)`` returns ``(o, final_state)``.  ``save_states``
+    (default None: decided by ``_saves_states``) keeps the forward's chunk states
+    for the backward (``gla_chunk_fwd_states`` / ``gla_chunk_bwd_saved``) instead
+    of recomputing them there."""
 
     @staticmethod
-    def forward(ctx, q, k, v, g, initial_state=None, cu_seqlens=None):
-        o, sf = gla_chunk_fwd(q, k, v, g, initial_state=initial_state, output_final_state=True,
-                              cu_seqlens=cu_seqlens)
-        ctx.save_for_backward(q, k, v, g, initial_state, cu_seqlens)
+    def forward(ctx, q, k, v, g, initial_state=None, cu_seqlens=None, save_states=None):
+        if save_states is None:
+            save_states = _saves_states(q, v, cu_seqlens)
+        hs = None
+        if save_states:
+            o, sf, hs = gla_chunk_fwd_states(q, k, v, g, initial_state=initial_state,
+                                             output_final_state=True, cu_seqlens=cu_seqlens)
+        else:
+            o, sf = gla_chunk_fwd(q, k, v, g, initial_state=initial_state, output_final_state=True,
+                                  cu_seqlens=cu_seqlens)
+        ctx.save_for_backward(q, k, v, g, initial_state, cu_seqlens, hs)
         return o, sf
 
     @staticmethod
     def backward(ctx, do, dsf):
-        q, k, v, g, s0, cu = ctx.saved_tensors
+        q, k, v, g, s0, cu, hs = ctx.saved_tensors
         dq, dk, dv, dg, ds0 = gla_chunk_bwd(q, k, v, g, do.contiguous(), initial_state=s0,
                                             d_final_state=None if dsf is None else dsf.contiguous(),
-                                            cu_seqlens=cu)
-        return dq, dk, dv, dg, ds0, None
+                                            cu_seqlens=cu, workspace=hs, states_saved=hs is not None)
+        return dq, dk, dv, dg, ds0, None, None
 
 
 def gla_recurrent_step(q, k, v, g, state, out=None):

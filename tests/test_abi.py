@@ -32,11 +32,11 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    assert names == ["gdn_chunk_fwd", "gla_chunk_bwd", "gla_chunk_bwd_workspace_size", "gla_chunk_fwd",
-                     "gla_chunk_fwd_noalloc", "gla_chunk_fwd_segments",
-                     "gla_chunk_fwd_segments_workspace_size", "gla_chunk_fwd_workspace_size",
-                     "gla_chunk_fwd_ws", "gla_last_error", "gla_recurrent_step", "gla_split_plan",
-                     "gla_status_string"]
+    assert names == ["gdn_chunk_fwd", "gla_chunk_bwd", "gla_chunk_bwd_saved",
+                     "gla_chunk_bwd_workspace_size", "gla_chunk_fwd", "gla_chunk_fwd_noalloc",
+                     "gla_chunk_fwd_segments", "gla_chunk_fwd_segments_workspace_size",
+                     "gla_chunk_fwd_states", "gla_chunk_fwd_workspace_size", "gla_chunk_fwd_ws",
+                     "gla_last_error", "gla_recurrent_step", "gla_split_plan", "gla_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -356,3 +356,32 @@ def test_chunk_fwd_segments_rejects(lib, kw, status, needle):
                                     P(a["ws"]) if a["ws"] else None, a["nbytes"], None)
     assert rc == status
     assert needle in gla.last_error()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=1), 2, "bf16 path only"),
+    (dict(dk=256), 2, "dk=256"),
+    (dict(ws=None), 1, "chunk_states of 0 bytes"),
+    (dict(nbytes=1024), 1, "needed"),
+    (dict(ws=FAKE + 16), 1, "256-byte aligned"),
+])
+def test_chunk_fwd_states_rejects(lib, kw, status, needle):
+    from sub_quadratic_sequence_amd import gla
+
+    P = ctypes.c_void_p
+    a = dict(dtype=0, dk=128, ws=FAKE, nbytes=1 << 30)
+    a.update(kw)
+    rc = lib.gla_chunk_fwd_states(P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, P(FAKE), None, None, 0, 2,
+                                  4, 256, a["dk"], 128, 64, a["dtype"], P(a["ws"]) if a["ws"] else None,
+                                  a["nbytes"], None)
+    assert rc == status
+    assert needle in gla.last_error()
+
+
+def test_chunk_bwd_saved_checks_like_chunk_bwd(lib):
+    from sub_quadratic_sequence_amd import gla
+
+    P = ctypes.c_void_p
+    rc = lib.gla_chunk_bwd_saved(*([P(FAKE)] * 4), None, P(FAKE), None, *([P(FAKE)] * 4), None, None,
+                                 0, 2, 4, 256, 128, 128, 64, 0, None, 0, None)
+    assert rc == 1 and "gla_chunk_bwd_saved: workspace of 0 bytes" in gla.last_error()

@@ -179,3 +179,65 @@ def test_autograd_function_matches_entry_point(dev):
     ref = _gpu_bwd(dev, d)
     for leaf, r in zip(leaves + [s0], ref):
         assert torch.equal(leaf.grad, r)
+
+
+def _aligned(ws, nbytes):
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + nbytes]
+
+
+@pytest.mark.parametrize("label,B,H,T,dk,dv,gate,lengths", [
+    ("fixed_d128_strong", 2, 2, 300, 128, 128, "strong", None),
+    ("dk128_dv64", 1, 2, 130, 128, 64, "weak", None),
+    ("dk64_dv128", 2, 1, 200, 64, 128, "weak", None),
+    ("backward_split_T3000", 1, 1, 3000, 128, 128, "strong", None),
+    ("varlen", 1, 2, 0, 128, 128, "weak", [1, 0, 65, 200, 17, 64]),
+])
+def test_saved_chunk_states_equal_recomputed(dev, label, B, H, T, dk, dv, gate, lengths):
+    """gla_chunk_fwd_states writes the chunk states the backward computes for itself
+    (bitwise), its outputs are gla_chunk_fwd's (bitwise, 64-column slices), and
+    gla_chunk_bwd_saved on them gives gla_chunk_bwd's gradients (bitwise)."""
+    from sub_quadratic_sequence_amd import gla
+
+    say(f"saved chunk states {label}: B={B} H={H} T={T} dk={dk} dv={dv} gate={gate} lengths={lengths}")
+    d = _case(B, H, T, dk, dv, gate=gate, lengths=lengths)
+    to = lambda x: None if x is None else x.to(dev)
+    q, k, v, g, do = (to(d[n]) for n in ("q", "k", "v", "g", "do"))
+    s0, dsT, cu = to(d["s0"]), to(d["dsT"]), to(d["cu_seqlens"])
+    need = gla.bwd_workspace_size(q, v, cu)
+    # both workspaces start zeroed: the slots no chunk starts in stay equal
+    ws_a = torch.zeros(need + 256, dtype=torch.uint8, device=dev)
+    ws_b = torch.zeros(need + 256, dtype=torch.uint8, device=dev)
+    ga = gla.gla_chunk_bwd(q, k, v, g, do, initial_state=s0, d_final_state=dsT, cu_seqlens=cu,
+                           workspace=ws_a)
+    o_s, sf_s, _ = gla.gla_chunk_fwd_states(q, k, v, g, initial_state=s0, output_final_state=True,
+                                            cu_seqlens=cu, chunk_states=ws_b)
+    o_r, sf_r = gla.gla_chunk_fwd(q, k, v, g, initial_state=s0, output_final_state=True,
+                                  cu_seqlens=cu, split=False)
+    gb = gla.gla_chunk_bwd(q, k, v, g, do, initial_state=s0, d_final_state=dsT, cu_seqlens=cu,
+                           workspace=ws_b, states_saved=True)
+    torch.cuda.synchronize()
+    nseq = B if cu is None else len(lengths)
+    tokens = B * T if cu is None else sum(lengths)
+    state_bytes = H * (nseq + tokens // 64 + 1) * dk * dv * 2
+    assert torch.equal(_aligned(ws_a, state_bytes), _aligned(ws_b, state_bytes))
+    assert torch.equal(o_s, o_r) and torch.equal(sf_s, sf_r)
+    for x, y in zip(ga, gb):
+        assert (x is None and y is None) or torch.equal(x, y)
+    _check(d, gb, f"bwd from saved states {label}")
+
+
+@pytest.mark.parametrize("save", [True, False])
+def test_autograd_saved_and_recomputed_states_agree(dev, save):
+    from sub_quadratic_sequence_amd import gla
+
+    say(f"GLAFunction save_states={save}, B=2 H=2 T=333 d128 strong gates")
+    d = _case(2, 2, 333, 128, 128, gate="strong")
+    leaves = [d[n].to(dev).requires_grad_(True) for n in ("q", "k", "v", "g")]
+    s0 = d["s0"].to(dev).requires_grad_(True)
+    o, sf = gla.GLAFunction.apply(*leaves, s0, None, save)
+    torch.autograd.backward([o, sf], [d["do"].to(dev), d["dsT"].to(dev)])
+    torch.cuda.synchronize()
+    ref = _gpu_bwd(dev, d)
+    for leaf, r in zip(leaves + [s0], ref):
+        assert torch.equal(leaf.grad, r)
