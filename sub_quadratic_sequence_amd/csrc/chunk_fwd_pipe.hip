@@ -138,9 +138,9 @@ __device__ __forceinline__ int srow(int rb, int m) {
 
 }  // namespace pipe
 
-// MODE kFull: the forward pass (outputs, and the final state of unsplit sequences;
-// with 64-column slices and prm.hs set, also the bf16 state entering every chunk,
-// as kChunkStates writes it).
+// MODE kFull: the forward pass (outputs, and the final state of unsplit sequences).
+// MODE kFullStates: kFull on 64-column slices that also writes the bf16 state
+// entering every chunk, as kChunkStates does.
 // MODE kChunkStates: no outputs; the state entering every chunk, in bf16, to
 // prm.hs (the backward pass's recomputed states).
 // MODE kSegGrad: the state-gradient pass of the backward's sequence split (k and v
@@ -151,10 +151,10 @@ __device__ __forceinline__ int srow(int rb, int m) {
 template <int DK, int MODE, int NT>
 __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm) {
   using namespace pipe;
-  constexpr bool FULL = MODE == kFull;
+  constexpr bool FULL = MODE == kFull || MODE == kFullStates;
   constexpr bool STATES = MODE == kChunkStates;
   constexpr bool REV = MODE == kSegGrad;
-  static_assert(!STATES || NT == 1, "chunk states come from 64-column slices");
+  static_assert(!(STATES || MODE == kFullStates) || NT == 1, "chunk states come from 64-column slices");
   static_assert(!REV || NT == 1, "the gradient pass runs on 64-column slices");
   using BufT = Buf<DK, NT>;
   constexpr int DVT = BufT::DVT;
@@ -702,20 +702,18 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     // 64 rows (8 KB) further on.
     constexpr unsigned kHalfX = (unsigned)tr_swz(64) << 4, kHalfOff = 64u * 128u;
     unsigned short* og = reinterpret_cast<unsigned short*>(prm.o) + rowbase * DV + vcol0;
-    // chunk states (the chunk-state mode, or the unsplit 64-column full pass when
-    // prm.hs is set): this unit's first slot, and the lane's element of a slot for
-    // tile 0, slot 0 (the tile and slot are added per store)
-    constexpr bool HS = STATES || (FULL && NT == 1);
+    // chunk states (the chunk-state mode, and the full pass that also writes them):
+    // this unit's first slot, and the lane's element of a slot for tile 0 (the tile
+    // is added per store)
+    constexpr bool HS = STATES || MODE == kFullStates;
     unsigned short* hs_unit = nullptr;
     int hs_lane = 0;
     if constexpr (HS) {
-      if (STATES || prm.hs) {
-        const long slot0 = prm.cu ? (long)h * prm.slots + n + bos / C
-                                  : (long)h * prm.slots + n + (long)n * prm.T / C;
-        hs_unit = prm.hs + slot0 * DK * DV;
-        // chunk_state_index(srow(0, 4gq + (m & 3)), 64vt + 16cw + 4(m >> 2)); tile rb adds 256
-        hs_lane = ((((vt * 4 + cw) * NRB * 4 + (m & 3)) * 4 + gq) * 16) + 4 * (m >> 2);
-      }
+      const long slot0 = prm.cu ? (long)h * prm.slots + n + bos / C
+                                : (long)h * prm.slots + n + (long)n * prm.T / C;
+      hs_unit = prm.hs + slot0 * DK * DV;
+      // chunk_state_index(srow(0, 4gq + (m & 3)), 64vt + 16cw + 4(m >> 2)); tile rb adds 256
+      hs_lane = ((((vt * 4 + cw) * NRB * 4 + (m & 3)) * 4 + gq) * 16) + 4 * (m >> 2);
     }
     f32x4 sacc[NT][NRB];
 #pragma unroll
@@ -876,7 +874,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       }
 
       if constexpr (HS) {
-        if (STATES || hs_unit) {
+        {
           // the state entering chunk u, bf16, in the chunk_state_index order.  Lane
           // (m = 4a + j, gq) holds rows srow(rb, 4gq + 0..3) of column 16cw + m; a
           // 4 x 4 transpose inside each quad of lanes (two DPP exchange stages)
@@ -1020,6 +1018,17 @@ int launch_chunk_fwd_states(const ChunkParams& prm, int dk, int nblocks, hipStre
     hipLaunchKernelGGL((chunk_fwd_pipe_kernel<128, kChunkStates, 1>), dim3(nblocks), dim3(512), 0, stream, prm);
   else if (dk == 64)
     hipLaunchKernelGGL((chunk_fwd_pipe_kernel<64, kChunkStates, 1>), dim3(nblocks), dim3(512), 0, stream, prm);
+  else
+    return -2;
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_chunk_fwd_full_states(const ChunkParams& prm, int dk, int nblocks, hipStream_t stream) {
+  if (prm.dvt != 64 || prm.nvt * 64 != prm.DV || prm.nseg != 1) return -2;
+  if (dk == 128)
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<128, kFullStates, 1>), dim3(nblocks), dim3(512), 0, stream, prm);
+  else if (dk == 64)
+    hipLaunchKernelGGL((chunk_fwd_pipe_kernel<64, kFullStates, 1>), dim3(nblocks), dim3(512), 0, stream, prm);
   else
     return -2;
   return hipGetLastError() == hipSuccess ? 0 : -1;

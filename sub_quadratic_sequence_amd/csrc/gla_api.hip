@@ -683,8 +683,8 @@ int gla_chunk_fwd_states(const void* q, const void* k, const void* v, const void
   prm.nvt = dv / 64;
   prm.hs = static_cast<unsigned short*>(chunk_states);
   prm.slots = (int)(nseq + tokens / 64 + 1);
-  const int rc = gla::launch_chunk_fwd(prm, dk, dtype, (int)(units * prm.nvt),
-                                       reinterpret_cast<hipStream_t>(stream));
+  const int rc = gla::launch_chunk_fwd_full_states(prm, dk, (int)(units * prm.nvt),
+                                                   reinterpret_cast<hipStream_t>(stream));
   return launch_status(fn, rc, dk, dtype);
 }
 

@@ -45,6 +45,7 @@ constexpr int kFull = 0;       // outputs (and the final state of unsplit sequen
 constexpr int kStateOnly = 1;  // a segment's state from zero and its total decay
 constexpr int kChunkStates = 2;  // the state entering every chunk, to ChunkParams::hs
 constexpr int kSegGrad = 3;      // the backward split's segment state gradients (k, v = q, dO)
+constexpr int kFullStates = 4;   // kFull plus the state entering every chunk, to ChunkParams::hs
 
 // Element (row c, column n) of a chunk-state slot (dk x dv, bf16).  The order
 // follows the forward consumer's accumulators (column slice n / 64, its 16-column
@@ -129,6 +130,7 @@ struct GdnParams {
 // Each returns 0 on success, -1 if the launch failed, -2 if no kernel exists
 // for the shape/dtype.
 int launch_chunk_fwd(const ChunkParams& prm, int dk, int dtype, int nblocks, hipStream_t stream);
+int launch_chunk_fwd_full_states(const ChunkParams& prm, int dk, int nblocks, hipStream_t stream);
 int launch_chunk_fwd_pipe(const ChunkParams& prm, int dk, bool state_only, int nblocks,
                           hipStream_t stream);
 int launch_chunk_fwd_states(const ChunkParams& prm, int dk, int nblocks, hipStream_t stream);
