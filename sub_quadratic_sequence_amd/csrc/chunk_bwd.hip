@@ -206,10 +206,10 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
   constexpr int LP = L + 8;        // [i][j] 16x16 score tile pitch (elements)
   constexpr int CB = DK / 16, NB = DV / 16;
   constexpr int NCG = DK / 8;
-  constexpr int NGL = 16 * NCG;             // gating lanes (waves 0 .. NGL/64-1)
+  constexpr int NGL = 16 * NCG;             // gating lanes per half (waves 0.. and 4..)
   constexpr int NVU = DV / 8;               // 16-byte units per value row
-  constexpr int NCP = C * NVU / 256;        // units per copy lane (waves 4-7)
-  static_assert(NGL <= 256, "shape");
+  constexpr int NCP = C * NVU / 512;        // units per lane of the value and dO copies
+  static_assert(NGL <= 256 && NCP >= 1, "shape");
 
   // bf16 tiles with swizzled 256-byte rows (see swz), then the unswizzled rest
   struct Smem {
@@ -267,8 +267,12 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
   unsigned short* const dv_out = static_cast<unsigned short*>(prm.dv) + sq.r0 * DV;
 
   // ---- lane roles for the load phase ------------------------------------------
-  const bool gl = tid < NGL;               // gating lane: tokens 4tg..+3, channels 8cg..+7
-  const bool cl = tid >= 256;              // copy lane (values and output gradients)
+  // Both halves of the workgroup scan the gates, lane (tg, cg) of each half over
+  // tokens 4tg..+3 and channels 8cg..+7, with the same code and so the same
+  // values: the first half builds q~, the Delta tile and the state factors, the
+  // second half k~.  Every lane copies a share of the values and dO.
+  const bool ql = tid < NGL;                      // query-side gating lane
+  const bool kl = tid >= 256 && tid < 256 + NGL;  // key-side gating lane
   // Lane-dependent offsets are recomputed where they are used, from an opaque
   // copy of the lane index: kept live across the chunk loop they would not fit
   // beside the states, and their spill reloads would wait for every
@@ -279,31 +283,32 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
     return (int)t;
   };
 
-  // Next chunk's raw inputs.  Gating lanes and copy lanes are disjoint, so they
-  // share one register array: q, k, g rows (gating) or v, dO units (copy).
-  constexpr int NPF = 12 > 2 * NCP ? 12 : 2 * NCP;
+  // Next chunk's raw inputs: q or k rows (pf[0..3]) and g rows (pf[4..7]) of a
+  // gating lane, then the lane's v and dO units (pf[8..]).
+  constexpr int NPF = 8 + 2 * NCP;
   uint4 pf[NPF];
   uint2 rh[NB];   // the chunk-start state of this wave's channels
   auto prefetch = [&](int u) __attribute__((always_inline)) {
     const int tl = fresh_tid();
-    const int tg = tl & 15, cg = tl >> 4, cp = tl - 256;
+    const int tg = tl & 15, cg = (tl & 255) >> 4;
     const unsigned qk_lane = (unsigned)((4 * tg) * DK + 8 * cg) * 2u;
-    if (gl) {
+    if (ql) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const unsigned so = (unsigned)(u * C + a) * DK * 2u;
-        pf[a] = ld16s(rs_q, qk_lane, so);
-        pf[4 + a] = ld16s(rs_k, qk_lane, so);
-        pf[8 + a] = ld16s(rs_g, qk_lane, so);
-      }
-    } else if (cl) {
+      for (int a = 0; a < 4; ++a) pf[a] = ld16s(rs_q, qk_lane, (unsigned)(u * C + a) * DK * 2u);
+    } else if (kl) {
 #pragma unroll
-      for (int it = 0; it < NCP; ++it) {
-        const int idx = cp + 256 * it, row = idx / NVU, un = idx % NVU;
-        const unsigned so = (unsigned)(u * C) * DV * 2u;
-        pf[it] = ld16s(rs_v, (unsigned)(row * DV + 8 * un) * 2u, so);
-        pf[NCP + it] = ld16s(rs_o, (unsigned)(row * DV + 8 * un) * 2u, so);
-      }
+      for (int a = 0; a < 4; ++a) pf[a] = ld16s(rs_k, qk_lane, (unsigned)(u * C + a) * DK * 2u);
+    }
+    if (ql || kl) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) pf[4 + a] = ld16s(rs_g, qk_lane, (unsigned)(u * C + a) * DK * 2u);
+    }
+#pragma unroll
+    for (int it = 0; it < NCP; ++it) {
+      const int idx = tl + 512 * it, row = idx / NVU, un = idx % NVU;
+      const unsigned so = (unsigned)(u * C) * DV * 2u;
+      pf[8 + it] = ld16s(rs_v, (unsigned)(row * DV + 8 * un) * 2u, so);
+      pf[8 + NCP + it] = ld16s(rs_o, (unsigned)(row * DV + 8 * un) * 2u, so);
     }
   };
   auto prefetch_state = [&](int u) __attribute__((always_inline)) {
@@ -343,12 +348,12 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
   for (int u = u_hi - 1; u >= u_lo; --u) {
     const long row0 = (long)u * C;   // first token of this chunk (sequence-relative)
     // ======================= load phase =======================
-    if (gl) {
+    if (ql || kl) {
       const int tl = fresh_tid();
-      const int tg = tl & 15, cg = tl >> 4;
+      const int tg = tl & 15, cg = (tl & 255) >> 4;
       // log2 cumulative gate over the chunk, per channel
       float gm[4][8];
-      const unsigned* gw[4] = {&pf[8].x, &pf[9].x, &pf[10].x, &pf[11].x};
+      const unsigned* gw[4] = {&pf[4].x, &pf[5].x, &pf[6].x, &pf[7].x};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -367,8 +372,7 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
         for (int a = 0; a < 4; ++a) gm[a][i] += ex;
       }
       const int s = tg >> 2;   // this lane's sub-chunk
-      const unsigned* qw[4] = {&pf[0].x, &pf[1].x, &pf[2].x, &pf[3].x};
-      const unsigned* kw[4] = {&pf[4].x, &pf[5].x, &pf[6].x, &pf[7].x};
+      const unsigned* xw[4] = {&pf[0].x, &pf[1].x, &pf[2].x, &pf[3].x};   // q or k rows
       // The carried states move between sub-chunks by one factor each:
       // 2^(Gamma_{s-1,last} - b_{s-1}) 2^(b_s - Gamma_{s-1,last}) = 2^(b_s - b_{s-1}).
       float piv[8], f0[8], f1[8];
@@ -384,30 +388,28 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
       }
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        float qv[8], kv[8], dv8[8];
+        float xv[8], dv8[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float d = gm[a][i] - piv[i];
           dv8[i] = d;
-          const unsigned wq = qw[a][i >> 1], wk = kw[a][i >> 1];
-          qv[i] = ((i & 1) ? hi_bf16(wq) : lo_bf16(wq)) * fast_exp2(d);
-          kv[i] = ((i & 1) ? hi_bf16(wk) : lo_bf16(wk)) * fast_exp2(-d);
+          const unsigned wx = xw[a][i >> 1];
+          xv[i] = ((i & 1) ? hi_bf16(wx) : lo_bf16(wx)) * fast_exp2(ql ? d : -d);   // q~ or k~
         }
         // row 4 tg + a: unit cg of the token tiles, units 2 cg and 2 cg + 1 of Delta
         const unsigned wt = (toff(4 * tg, cg, 0) ^ cx(a, 0)) + ca(a, 0);
-        const unsigned wd = toff(4 * tg, 2 * cg, 0, RD);
-        *reinterpret_cast<uint4*>(lds + oQ + wt) =
-            uint4{pack_bf16x2(qv[0], qv[1]), pack_bf16x2(qv[2], qv[3]), pack_bf16x2(qv[4], qv[5]),
-                  pack_bf16x2(qv[6], qv[7])};
-        *reinterpret_cast<uint4*>(lds + oK + wt) =
-            uint4{pack_bf16x2(kv[0], kv[1]), pack_bf16x2(kv[2], kv[3]), pack_bf16x2(kv[4], kv[5]),
-                  pack_bf16x2(kv[6], kv[7])};
-        *reinterpret_cast<float4*>(lds + oD + ((wd ^ cx(a, 0)) + ca(a, 0, RD))) =
-            make_float4(dv8[0], dv8[1], dv8[2], dv8[3]);
-        *reinterpret_cast<float4*>(lds + oD + ((wd ^ cx(a, 1)) + ca(a, 1, RD))) =
-            make_float4(dv8[4], dv8[5], dv8[6], dv8[7]);
+        *reinterpret_cast<uint4*>(lds + (ql ? oQ : oK) + wt) =
+            uint4{pack_bf16x2(xv[0], xv[1]), pack_bf16x2(xv[2], xv[3]), pack_bf16x2(xv[4], xv[5]),
+                  pack_bf16x2(xv[6], xv[7])};
+        if (ql) {
+          const unsigned wd = toff(4 * tg, 2 * cg, 0, RD);
+          *reinterpret_cast<float4*>(lds + oD + ((wd ^ cx(a, 0)) + ca(a, 0, RD))) =
+              make_float4(dv8[0], dv8[1], dv8[2], dv8[3]);
+          *reinterpret_cast<float4*>(lds + oD + ((wd ^ cx(a, 1)) + ca(a, 1, RD))) =
+              make_float4(dv8[4], dv8[5], dv8[6], dv8[7]);
+        }
       }
-      if ((tg & 3) == 0) {
+      if (ql && (tg & 3) == 0) {
         *reinterpret_cast<float4*>(&sm.fac[s][8 * cg]) = make_float4(f0[0], f0[1], f0[2], f0[3]);
         *reinterpret_cast<float4*>(&sm.fac[s][8 * cg + 4]) = make_float4(f0[4], f0[5], f0[6], f0[7]);
         if (s == NS - 1) {
@@ -416,14 +418,14 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
         }
       }
     }
-    if (cl) {
-      const int cp = fresh_tid() - 256;
+    {
+      const int cp = fresh_tid();
 #pragma unroll
-      for (int it = 0; it < NCP; ++it) {   // row cp / NVU + it * 256 / NVU, unit cp % NVU
-        constexpr unsigned RI = 256 / NVU;
+      for (int it = 0; it < NCP; ++it) {   // row cp / NVU + it * 512 / NVU, unit cp % NVU
+        constexpr unsigned RI = 512 / NVU;
         const unsigned wc = (toff(cp / NVU, cp % NVU, 0) ^ cx(RI * it, 0)) + ca(RI * it, 0);
-        *reinterpret_cast<uint4*>(lds + oV + wc) = pf[it];
-        *reinterpret_cast<uint4*>(lds + oO + wc) = pf[NCP + it];
+        *reinterpret_cast<uint4*>(lds + oV + wc) = pf[8 + it];
+        *reinterpret_cast<uint4*>(lds + oO + wc) = pf[8 + NCP + it];
       }
     }
     barrier_lds();
