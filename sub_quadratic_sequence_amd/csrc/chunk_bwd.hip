@@ -271,8 +271,11 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
   // tokens 4tg..+3 and channels 8cg..+7, with the same code and so the same
   // values: the first half builds q~, the Delta tile and the state factors, the
   // second half k~.  Every lane copies a share of the values and dO.
-  const bool ql = tid < NGL;                      // query-side gating lane
-  const bool kl = tid >= 256 && tid < 256 + NGL;  // key-side gating lane
+  // Both are wave-uniform (NGL is a multiple of 64): the q/k loads of a wave then
+  // keep one scalar buffer descriptor instead of a per-lane choice between two,
+  // which the compiler would have to issue as a loop over the distinct values.
+  const bool ql = wave < NGL / 64;                    // query-side gating wave
+  const bool kl = wave >= 4 && wave < 4 + NGL / 64;   // key-side gating wave
   // Lane-dependent offsets are recomputed where they are used, from an opaque
   // copy of the lane index: kept live across the chunk loop they would not fit
   // beside the states, and their spill reloads would wait for every
