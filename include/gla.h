@@ -210,9 +210,11 @@ int gla_chunk_fwd_segments(const void* q, const void* k, const void* v, const vo
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Device workspace, in bytes, that gla_chunk_bwd needs for this shape (the bf16
- * state entering every 64-token chunk: H x (sequences + tokens/64 + 1) slots of
- * dk x dv, rounded up to 256).  num_seqs > 0 for packed sequences (then T is
+ * Device workspace, in bytes, that gla_chunk_bwd needs for this shape: the bf16
+ * state entering every 64-token chunk (H x (sequences + tokens/64 + 1) slots of
+ * dk x dv, rounded up to 256), the sequence split's state gradients when the
+ * call splits, and for dv above 128 fp32 partial sums of dq, dk and dg
+ * (3 x H x tokens x dk floats).  num_seqs > 0 for packed sequences (then T is
  * the packed total), 0 otherwise.  Unsupported shapes give 0.
  */
 size_t gla_chunk_bwd_workspace_size(int num_seqs, int B, int H, int T, int dk, int dv,
@@ -240,8 +242,12 @@ size_t gla_chunk_bwd_workspace_size(int num_seqs, int B, int H, int T, int dk, i
  *                    bytes, 256-byte aligned, owned by the caller; scratch until
  *                    the call's kernels complete.
  *
- * Supported: dtype GLA_BF16, dk and dv in {64, 128}, chunk_size 64; others give
- * GLA_ERR_UNSUPPORTED.  A missing, small or misaligned workspace gives
+ * Supported: dtype GLA_BF16, dk in {64, 128}, dv a multiple of 64, chunk_size 64;
+ * others give GLA_ERR_UNSUPPORTED.  dv above 128 runs as column slices of 128 (the
+ * last one 64 for an odd multiple of 64), one kernel launch each, in order on the
+ * stream: dq, dk and dg are sums over the slices, kept in the workspace in fp32
+ * until the last slice rounds them to bf16.  A missing, small or misaligned
+ * workspace gives
  * GLA_ERR_INVALID_ARG.  Gates must keep every channel's decay over any 16
  * consecutive tokens of a sequence at or above 2^-240 (so alpha = 0 is not
  * supported here); a sequence that breaks this gets NaN gradients.
@@ -266,7 +272,8 @@ int gla_chunk_bwd(const void* q, const void* k, const void* v, const void* g,
  * section "The Gated Recurrent Update"), one state per chunk boundary.
  *
  * Arguments, layouts and errors as for gla_chunk_fwd, with the backward's limits:
- * dtype GLA_BF16 and dk, dv in {64, 128}, else GLA_ERR_UNSUPPORTED; a missing,
+ * dtype GLA_BF16, dk in {64, 128} and dv a multiple of 64, else
+ * GLA_ERR_UNSUPPORTED; a missing,
  * small or misaligned chunk_states buffer gives GLA_ERR_INVALID_ARG.
  */
 int gla_chunk_fwd_states(const void* q, const void* k, const void* v, const void* g,

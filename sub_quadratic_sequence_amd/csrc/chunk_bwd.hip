@@ -256,15 +256,37 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
   const __amdgpu_buffer_rsrc_t rs_q = seq_rsrc(prm.q, sq.r0 * DK, (int)(sq.len * DK * 2));
   const __amdgpu_buffer_rsrc_t rs_k = seq_rsrc(prm.k, sq.r0 * DK, (int)(sq.len * DK * 2));
   const __amdgpu_buffer_rsrc_t rs_g = seq_rsrc(prm.g, sq.r0 * DK, (int)(sq.len * DK * 2));
-  const __amdgpu_buffer_rsrc_t rs_v = seq_rsrc(prm.v, sq.r0 * DV, (int)(sq.len * DV * 2));
-  const __amdgpu_buffer_rsrc_t rs_o = seq_rsrc(prm.dout, sq.r0 * DV, (int)(sq.len * DV * 2));
-  // this unit's chunk-start states (bf16 [chunk][dk][dv])
+  // this launch's columns [col0, col0 + DV) of rows LDV long; reads past the
+  // sequence's last row fall outside the record and return zeros
+  const int LDV = prm.ldv, col0 = prm.col0;
+  const int v_bytes = sq.len > 0 ? (int)(sq.len * LDV * 2 - col0 * 2) : 0;
+  const __amdgpu_buffer_rsrc_t rs_v = seq_rsrc(prm.v, sq.r0 * LDV + col0, v_bytes);
+  const __amdgpu_buffer_rsrc_t rs_o = seq_rsrc(prm.dout, sq.r0 * LDV + col0, v_bytes);
+  // this unit's chunk-start states (bf16 [chunk][dk][LDV])
   const __amdgpu_buffer_rsrc_t rs_h =
-      seq_rsrc(prm.hs, sq.slot0 * DK * DV, (int)((long)(nch > 0 ? nch : 1) * DK * DV * 2));
+      seq_rsrc(prm.hs, sq.slot0 * DK * LDV, (int)((long)(nch > 0 ? nch : 1) * DK * LDV * 2));
   unsigned short* const dq_out = static_cast<unsigned short*>(prm.dq) + sq.r0 * DK;
   unsigned short* const dk_out = static_cast<unsigned short*>(prm.dk) + sq.r0 * DK;
   unsigned short* const dg_out = static_cast<unsigned short*>(prm.dg) + sq.r0 * DK;
-  unsigned short* const dv_out = static_cast<unsigned short*>(prm.dv) + sq.r0 * DV;
+  unsigned short* const dv_out = static_cast<unsigned short*>(prm.dv) + sq.r0 * LDV + col0;
+  // dq, dk or dg (which = 0, 1, 2) at element e of this unit's [len][DK] rows: written
+  // directly, or summed over the column slices in fp32 (prm.pmode)
+  auto put = [&](unsigned short* out, int which, long e, float x0, float x1, float x2, float x3)
+                 __attribute__((always_inline)) {
+    if (prm.pmode == 0) {
+      *reinterpret_cast<uint2*>(out + e) = pack4(x0, x1, x2, x3);
+      return;
+    }
+    float4* const pp = reinterpret_cast<float4*>(prm.part + ((long)which * prm.part_rows + sq.r0) * DK + e);
+    if (prm.pmode != 1) {
+      const float4 y = *pp;
+      x0 += y.x; x1 += y.y; x2 += y.z; x3 += y.w;
+    }
+    if (prm.pmode == 3)
+      *reinterpret_cast<uint2*>(out + e) = pack4(x0, x1, x2, x3);
+    else
+      *pp = make_float4(x0, x1, x2, x3);
+  };
 
   // ---- lane roles for the load phase ------------------------------------------
   // Both halves of the workgroup scan the gates, lane (tg, cg) of each half over
@@ -309,9 +331,9 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
 #pragma unroll
     for (int it = 0; it < NCP; ++it) {
       const int idx = tl + 512 * it, row = idx / NVU, un = idx % NVU;
-      const unsigned so = (unsigned)(u * C) * DV * 2u;
-      pf[8 + it] = ld16s(rs_v, (unsigned)(row * DV + 8 * un) * 2u, so);
-      pf[8 + NCP + it] = ld16s(rs_o, (unsigned)(row * DV + 8 * un) * 2u, so);
+      const unsigned so = (unsigned)(u * C) * LDV * 2u;
+      pf[8 + it] = ld16s(rs_v, (unsigned)(row * LDV + 8 * un) * 2u, so);
+      pf[8 + NCP + it] = ld16s(rs_o, (unsigned)(row * LDV + 8 * un) * 2u, so);
     }
   };
   auto prefetch_state = [&](int u) __attribute__((always_inline)) {
@@ -320,20 +342,21 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
     const unsigned h_lane = 2u * (unsigned)chunk_state_index(c0 + (tl & 15), 4 * ((tl >> 4) & 3), DK);
     if (sw) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) rh[b] = ld8s(rs_h, h_lane + 32u * DK * b, (unsigned)u * DK * DV * 2u);
+      for (int b = 0; b < NB; ++b)
+        rh[b] = ld8s(rs_h, h_lane + 32u * DK * (unsigned)(b + col0 / 16), (unsigned)u * DK * LDV * 2u);
     }
   };
 
   // the state gradient entering this work item from later tokens: dS_T, or the
   // segment scan's result when the sequence is split
   f32x4 Ht[NB], Bt[NB];
-  const float* const b_in = prm.nseg > 1 ? prm.seg_state + (long)item * DK * DV
-                                         : (prm.dsT ? prm.dsT + (long)unit * DK * DV : nullptr);
+  const float* const b_in = prm.nseg > 1 ? prm.seg_state + (long)item * DK * LDV
+                                         : (prm.dsT ? prm.dsT + (long)unit * DK * LDV : nullptr);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     Bt[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (sw && b_in) {
-      const float4 x = *reinterpret_cast<const float4*>(b_in + (c0 + m) * DV + 16 * b + 4 * grp);
+      const float4 x = *reinterpret_cast<const float4*>(b_in + (long)(c0 + m) * LDV + col0 + 16 * b + 4 * grp);
       Bt[b] = f32x4{x.x, x.y, x.z, x.w};
     }
   }
@@ -515,9 +538,8 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
         qd[s][3] = hi_bf16(qv.y) * acc[3];
         const long t = row0 + 16 * s + m;
         if (t < sq.len)
-          *reinterpret_cast<uint2*>(dq_out + t * DK + c0 + 4 * grp) =
-              pack4(fast_exp2(d.x) * acc[0], fast_exp2(d.y) * acc[1], fast_exp2(d.z) * acc[2],
-                    fast_exp2(d.w) * acc[3]);
+          put(dq_out, 0, t * DK + c0 + 4 * grp, fast_exp2(d.x) * acc[0], fast_exp2(d.y) * acc[1],
+              fast_exp2(d.z) * acc[2], fast_exp2(d.w) * acc[3]);
         // H^ + k~^T V over the sub-chunk's tokens, then the factor to H^ of
         // sub-chunk s + 1 (after the last one: to H at the chunk's end)
 #pragma unroll
@@ -585,10 +607,9 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
         }
         const long t = row0 + 16 * s + m;
         if (t < sq.len) {
-          *reinterpret_cast<uint2*>(dk_out + t * DK + c0 + 4 * grp) =
-              pack4(fast_exp2(-d.x) * acc[0], fast_exp2(-d.y) * acc[1], fast_exp2(-d.z) * acc[2],
-                    fast_exp2(-d.w) * acc[3]);
-          *reinterpret_cast<uint2*>(dg_out + t * DK + c0 + 4 * grp) = pack4(dgv[0], dgv[1], dgv[2], dgv[3]);
+          put(dk_out, 1, t * DK + c0 + 4 * grp, fast_exp2(-d.x) * acc[0], fast_exp2(-d.y) * acc[1],
+              fast_exp2(-d.z) * acc[2], fast_exp2(-d.w) * acc[3]);
+          put(dg_out, 2, t * DK + c0 + 4 * grp, dgv[0], dgv[1], dgv[2], dgv[3]);
         }
         // B^ + q~^T dO over the sub-chunk's tokens, then the factor to B^ of
         // sub-chunk s - 1 (after the first one: to B at the chunk's start)
@@ -609,7 +630,7 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
         mma16_add(acc, rdt(oO + at(tW, 16 * s, 0)), rdt(oP + s * L * LP * 2 + tL));
         const long t = row0 + 16 * s + m;
         if (t < sq.len)
-          *reinterpret_cast<uint2*>(dv_out + t * DV + n0 + 4 * grp) = pack4(acc[0], acc[1], acc[2], acc[3]);
+          *reinterpret_cast<uint2*>(dv_out + t * LDV + n0 + 4 * grp) = pack4(acc[0], acc[1], acc[2], acc[3]);
       }
       barrier_lds();
     }
@@ -618,7 +639,7 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
   if (sw && prm.ds0 && seg == 0) {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
-      *reinterpret_cast<float4*>(prm.ds0 + ((long)unit * DK + c0 + m) * DV + 16 * b + 4 * grp) =
+      *reinterpret_cast<float4*>(prm.ds0 + ((long)unit * DK + c0 + m) * LDV + col0 + 16 * b + 4 * grp) =
           make_float4(Bt[b][0], Bt[b][1], Bt[b][2], Bt[b][3]);
   }
 }

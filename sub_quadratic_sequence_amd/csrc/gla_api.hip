@@ -214,6 +214,15 @@ size_t split_bytes(long long units, int nseg, int dk, int dv) {
   return ((st + 255) / 256) * 256 + ((dec + 255) / 256) * 256;
 }
 
+// The backward runs d_v above 128 as column slices of 128 (the last one 64 when
+// d_v is an odd multiple of 64), one launch each; dq, dk and dg are sums over the
+// slices, kept in fp32 between launches: 3 x rows x dk floats.
+int bwd_slices(int dv) { return (dv + 127) / 128; }
+size_t bwd_partial_bytes(long long rows, int dk, int dv) {
+  if (bwd_slices(dv) <= 1) return 0;
+  return ((size_t)3 * rows * dk * sizeof(float) + 255) / 256 * 256;
+}
+
 // The three kernels of a split forward (prm filled by check_chunk_args; nseg > 1)
 // with the segment states and decays in ws (split_bytes(...) bytes, 256-aligned).
 int run_split(const char* fn, gla::ChunkParams& prm, long long units, int nseg, int seg_len,
@@ -450,14 +459,14 @@ int gla_chunk_fwd_segments(const void* q, const void* k, const void* v, const vo
 size_t gla_chunk_bwd_workspace_size(int num_seqs, int B, int H, int T, int dk, int dv,
                                     int chunk_size, int dtype) {
   if (dtype != GLA_BF16 || chunk_size != 64 || B <= 0 || H <= 0 || T < 0) return 0;
-  if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return 0;
+  if ((dk != 64 && dk != 128) || dv <= 0 || dv % 64 != 0) return 0;
   const long long nseq = num_seqs > 0 ? num_seqs : B;
   const long long tokens = num_seqs > 0 ? (long long)T : (long long)B * T;
   const long long slots = nseq + tokens / 64 + 1;
   const size_t states = ((size_t)H * slots * dk * dv * 2 + 255) / 256 * 256;
   int seg_len = T;
   const int nseg = split_plan(num_seqs > 0, dtype, nseq * H, T, seg_len);
-  return states + (nseg > 1 ? split_bytes(nseq * H, nseg, dk, dv) : 0);
+  return states + (nseg > 1 ? split_bytes(nseq * H, nseg, dk, dv) : 0) + bwd_partial_bytes(H * tokens, dk, dv);
 }
 
 }  // extern "C"
@@ -482,8 +491,9 @@ int chunk_bwd_impl(const char* fn, bool states_ready, const void* q, const void*
                 B, H, T, dk, dv);
   if (chunk_size != 64)
     return fail(GLA_ERR_UNSUPPORTED, "%s: chunk_size %d (only 64 is implemented)", fn, chunk_size);
-  if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
-    return fail(GLA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d (each must be 64 or 128)", fn, dk, dv);
+  if ((dk != 64 && dk != 128) || dv % 64 != 0)
+    return fail(GLA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d (dk must be 64 or 128, dv a multiple of 64)", fn, dk,
+                dv);
   int nseq = B;
   if (cu_seqlens) {
     if (B != 1)
@@ -542,6 +552,11 @@ int chunk_bwd_impl(const char* fn, bool states_ready, const void* q, const void*
   prm.DV = dv;
   prm.nvt = nvt;
   prm.slots = (int)(nseq + tokens / 64 + 1);
+  prm.ldv = dv;
+  prm.col0 = 0;
+  prm.pmode = 0;
+  prm.part = nullptr;
+  prm.part_rows = (long)(H * tokens);
   prm.xcd_remap = ((units * nvt) % 8 == 0) ? 1 : 0;
   // sequence split: as in the forward, fixed-length sequences of too few units
   // to fill the device are cut into segments of whole chunks
@@ -552,12 +567,16 @@ int chunk_bwd_impl(const char* fn, bool states_ready, const void* q, const void*
   if (cu_seqlens) prm.seg_len = 1 << 30;   // one segment whatever the packed lengths
   prm.seg_state = nullptr;
   prm.seg_decay = nullptr;
+  const size_t states_bytes = ((size_t)H * prm.slots * dk * dv * 2 + 255) / 256 * 256;
   if (nseg > 1) {
-    char* const sp = static_cast<char*>(workspace) + ((size_t)H * prm.slots * dk * dv * 2 + 255) / 256 * 256;
+    char* const sp = static_cast<char*>(workspace) + states_bytes;
     const size_t st_bytes = ((size_t)units * nseg * dk * dv * sizeof(float) + 255) / 256 * 256;
     prm.seg_state = reinterpret_cast<float*>(sp);
     prm.seg_decay = reinterpret_cast<float*>(sp + st_bytes);
   }
+  if (bwd_slices(dv) > 1)
+    prm.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + states_bytes +
+                                        (nseg > 1 ? split_bytes(units, nseg, dk, dv) : 0));
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // 1. the state entering every chunk: the forward's pipelined kernel, states only
   gla::ChunkParams fp;
@@ -617,8 +636,15 @@ int chunk_bwd_impl(const char* fn, bool states_ready, const void* q, const void*
     rc = gla::launch_seg_scan(sp, (int)units, s);
     if (rc != 0) return launch_status(fn, rc, dk, dtype);
   }
-  // 4. the gradients chunk by chunk, last to first, per (unit, segment)
-  rc = gla::launch_chunk_bwd(prm, dk, dv, (int)(units * nseg), s);
+  // 4. the gradients chunk by chunk, last to first, per (unit, segment); d_v above
+  //    128 one column slice per launch, in order on the stream, dq, dk and dg summed
+  const int nsl = bwd_slices(dv);
+  for (int sl = 0; sl < nsl; ++sl) {
+    prm.col0 = 128 * sl;
+    prm.pmode = nsl == 1 ? 0 : sl == 0 ? 1 : sl == nsl - 1 ? 3 : 2;
+    rc = gla::launch_chunk_bwd(prm, dk, dv - prm.col0 >= 128 ? 128 : 64, (int)(units * nseg), s);
+    if (rc != 0) break;
+  }
   return launch_status(fn, rc, dk, dtype);
 }
 
@@ -663,9 +689,9 @@ int gla_chunk_fwd_states(const void* q, const void* k, const void* v, const void
   if (st != GLA_OK) return st;
   if (dtype != GLA_BF16)
     return fail(GLA_ERR_UNSUPPORTED, "%s: chunk states come from the bf16 path only", fn);
-  if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
-    return fail(GLA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d (each must be 64 or 128, as for gla_chunk_bwd)", fn,
-                dk, dv);
+  if ((dk != 64 && dk != 128) || dv % 64 != 0)
+    return fail(GLA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d (as for gla_chunk_bwd: dk 64 or 128, dv a multiple of 64)",
+                fn, dk, dv);
   if (!fits_i32(((long long)T / 64 + 1) * dk * dv * 2))
     return fail(GLA_ERR_INVALID_ARG, "%s: T=%d is too long for one call's chunk states", fn, T);
   if (nothing) return GLA_OK;

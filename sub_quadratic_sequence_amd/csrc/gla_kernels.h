@@ -107,6 +107,18 @@ struct BwdParams {
   int seg_len;
   float* seg_state;      // [units][nseg][dk][dv] fp32: a segment's state gradient from zero, then its incoming one
   float* seg_decay;      // [units][nseg][dk] fp32: exp of the segment's summed log-gates
+  // Column slice of d_v handled by one backward launch (d_v above 128 runs as
+  // slices of 128 or 64 columns in turn): ldv is the full d_v, the row stride of v,
+  // d_o and d_v and the column count of every state-shaped tensor; col0 is the
+  // slice's first column.
+  int ldv;
+  int col0;
+  // dq, dk and dg summed over the slices: 0 one slice (bf16 written directly);
+  // 1 the first slice (fp32 sums to part); 2 a middle slice (adds to part); 3 the
+  // last slice (adds part's sums and writes bf16).
+  int pmode;
+  float* part;           // [3][part_rows][dk] fp32 partial dq, dk, dg (pmode != 0)
+  long part_rows;        // rows of each partial tensor: B*H*T (packed: H*T)
 };
 
 // Arguments of the Gated DeltaNet chunk forward (see include/gla.h for meanings).

@@ -391,13 +391,15 @@ def _saves_states(q, v, cu_seqlens):
     let the backward recompute them)."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
-    if q.dtype != torch.bfloat16 or dk not in (64, 128) or dv not in (64, 128):
+    if q.dtype != torch.bfloat16 or dk not in (64, 128) or dv % 64 != 0:
         return False
     if workspace_size(q, v, cu_seqlens) > 0:
         return False
     nseq = B if cu_seqlens is None else cu_seqlens.numel() - 1
     cus = torch.cuda.get_device_properties(q.device).multi_processor_count
-    return dv == 64 or nseq * H * (dv // 128) < cus
+    # the planned forward takes 128-column slices only when d_v is a multiple of 128
+    # and its work items fill the device
+    return dv % 128 != 0 or nseq * H * (dv // 128) < cus
 
 
 class GLAFunction(torch.autograd.Function):

@@ -180,7 +180,13 @@ def test_bwd_workspace_size(lib):
     # packed: 16 heads x (16 sequences + 33000 // 64 + 1) states of 128 x 64, rounded up to 256 bytes
     assert lib.gla_chunk_bwd_workspace_size(16, 1, 16, 33000, 128, 64, 64, 0) == 16 * 532 * 128 * 64 * 2
     assert lib.gla_chunk_bwd_workspace_size(0, 8, 16, 2048, 128, 128, 64, 1) == 0   # fp32
-    assert lib.gla_chunk_bwd_workspace_size(0, 8, 16, 2048, 128, 256, 64, 0) == 0   # dv 256
+    # dv 256: states of 128 x 256, the split's state gradients, and the fp32 partial
+    # sums of dq, dk and dg over the two 128-column slices
+    states256 = 16 * 265 * 128 * 256 * 2
+    split256 = 128 * 2 * 128 * 256 * 4 + 128 * 2 * 128 * 4
+    partial = 3 * 16 * 8 * 2048 * 128 * 4
+    assert lib.gla_chunk_bwd_workspace_size(0, 8, 16, 2048, 128, 256, 64, 0) == states256 + split256 + partial
+    assert lib.gla_chunk_bwd_workspace_size(0, 8, 16, 2048, 128, 96, 64, 0) == 0    # dv not a multiple of 64
     assert lib.gla_chunk_bwd_workspace_size(0, 8, 16, 2048, 128, 128, 128, 0) == 0  # chunk 128
 
 
@@ -199,7 +205,8 @@ def _bwd(lib, **kw):
 @pytest.mark.parametrize("kw,status,needle", [
     (dict(dtype=1), 2, "only GLA_BF16"),
     (dict(dtype=7), 1, "dtype 7"),
-    (dict(dv=256), 2, "dk=128 dv=256"),
+    (dict(dv=96), 2, "dk=128 dv=96"),
+    (dict(dv=256), 1, "workspace of 0 bytes"),   # d_v 256 is accepted: it needs its workspace
     (dict(dk=96), 2, "dk=96"),
     (dict(chunk=128), 2, "chunk_size 128"),
     (dict(do=None), 1, "must be non-null"),

@@ -91,6 +91,8 @@ def _unit_err_one(x, r, n, h, d):
     (1, 2, 130, 64, 128, "strong"),
     (1, 1, 1, 128, 128, "weak"),       # one token
     (1, 2, 128, 64, 64, "zero"),       # alpha = 1
+    (1, 2, 200, 128, 256, "weak"),     # d_v 256: two 128-column slices, dq/dk/dg summed
+    (2, 1, 150, 64, 192, "strong"),    # d_v 192: a 128- and a 64-column slice
 ])
 def test_bwd_matches_oracle(dev, B, H, T, dk, dv, gate):
     say(f"gla_chunk_bwd B={B} H={H} T={T} dk={dk} dv={dv} gate={gate} s0 dsT")
@@ -103,6 +105,7 @@ def test_bwd_matches_oracle(dev, B, H, T, dk, dv, gate):
     (1, 1, 3000, 128, 128, "strong"),  # 5 segments
     (2, 2, 2050, 64, 64, "weak"),      # 4 segments, the last one a single token
     (1, 2, 1100, 128, 64, "strong"),
+    (1, 1, 1500, 128, 256, "weak"),    # split and column slices together
 ])
 def test_bwd_sequence_split(dev, B, H, T, dk, dv, gate):
     from sub_quadratic_sequence_amd import gla
@@ -124,13 +127,13 @@ def test_bwd_without_initial_or_final_state(dev):
     _check(d, got, "bwd no states")
 
 
-@pytest.mark.parametrize("gate", ["weak", "strong"])
-def test_bwd_varlen_with_empty_and_short(dev, gate):
+@pytest.mark.parametrize("gate,dv", [("weak", 128), ("strong", 128), ("strong", 256)])
+def test_bwd_varlen_with_empty_and_short(dev, gate, dv):
     lengths = [1, 0, 65, 200, 17, 64]
-    say(f"gla_chunk_bwd varlen lengths={lengths} H=2 d128 gate={gate}")
-    d = _case(1, 2, 0, 128, 128, gate=gate, lengths=lengths)
+    say(f"gla_chunk_bwd varlen lengths={lengths} H=2 dk128 dv{dv} gate={gate}")
+    d = _case(1, 2, 0, 128, dv, gate=gate, lengths=lengths)
     got = _gpu_bwd(dev, d)
-    _check(d, got, f"bwd varlen {gate}")
+    _check(d, got, f"bwd varlen dv{dv} {gate}")
     # the empty sequence passes its state through: dS0 = dS_T
     assert torch.equal(got[4][1].cpu(), d["dsT"][1])
 
@@ -192,6 +195,8 @@ def _aligned(ws, nbytes):
     ("dk64_dv128", 2, 1, 200, 64, 128, "weak", None),
     ("backward_split_T3000", 1, 1, 3000, 128, 128, "strong", None),
     ("varlen", 1, 2, 0, 128, 128, "weak", [1, 0, 65, 200, 17, 64]),
+    ("dv256", 1, 2, 200, 128, 256, "weak", None),
+    ("dv192_varlen", 1, 2, 0, 64, 192, "strong", [70, 0, 130]),
 ])
 def test_saved_chunk_states_equal_recomputed(dev, label, B, H, T, dk, dv, gate, lengths):
     """gla_chunk_fwd_states writes the chunk states the backward computes for itself

@@ -99,7 +99,7 @@ def test_random_forward(dev, i):
 # ------------------------------------------------------------------ GLA backward
 def bwd_case(i):
     r = _rng(2, i)
-    c = {"dk": int(r.choice([64, 128])), "dv": int(r.choice([64, 128])),
+    c = {"dk": int(r.choice([64, 128])), "dv": int(r.choice([64, 128, 192, 256])),
          "gate": str(r.choice(["weak", "strong"])), "s0": bool(r.random() < 0.5),
          "final": bool(r.random() < 0.5), "layout": str(r.choice(["fixed", "varlen", "long"]))}
     if c["layout"] == "fixed":
