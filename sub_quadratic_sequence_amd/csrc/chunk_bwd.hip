@@ -199,7 +199,9 @@ __device__ __forceinline__ Seq seq_of(const BwdParams& prm, int n, int h) {
 // in-chunk reverse sums stay inside the wave.  Wave w < DV/16 computes dv for
 // columns [16w, 16w+16).
 // ============================================================================
-template <int DK, int DV>
+// SLICED: one column slice of a wider d_v (prm.pmode sums dq, dk and dg over the
+// slices); otherwise they are written directly, with no per-store test.
+template <int DK, int DV, bool SLICED>
 __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
   using namespace bwd;
   constexpr unsigned RD = DK * 4;  // bytes per row of the fp32 Delta tile
@@ -258,7 +260,8 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
   const __amdgpu_buffer_rsrc_t rs_g = seq_rsrc(prm.g, sq.r0 * DK, (int)(sq.len * DK * 2));
   // this launch's columns [col0, col0 + DV) of rows LDV long; reads past the
   // sequence's last row fall outside the record and return zeros
-  const int LDV = prm.ldv, col0 = prm.col0;
+  // (one slice of width DV: prm.ldv == DV and prm.col0 == 0, known at compile time)
+  const int LDV = SLICED ? prm.ldv : DV, col0 = SLICED ? prm.col0 : 0;
   const int v_bytes = sq.len > 0 ? (int)(sq.len * LDV * 2 - col0 * 2) : 0;
   const __amdgpu_buffer_rsrc_t rs_v = seq_rsrc(prm.v, sq.r0 * LDV + col0, v_bytes);
   const __amdgpu_buffer_rsrc_t rs_o = seq_rsrc(prm.dout, sq.r0 * LDV + col0, v_bytes);
@@ -273,7 +276,7 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
   // directly, or summed over the column slices in fp32 (prm.pmode)
   auto put = [&](unsigned short* out, int which, long e, float x0, float x1, float x2, float x3)
                  __attribute__((always_inline)) {
-    if (prm.pmode == 0) {
+    if (!SLICED) {
       *reinterpret_cast<uint2*>(out + e) = pack4(x0, x1, x2, x3);
       return;
     }
@@ -645,16 +648,24 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
 }
 
 int launch_chunk_bwd(const BwdParams& prm, int dk, int dv, int nblocks, hipStream_t stream) {
+#define GLA_BWD(K, V)                                                                          \
+  do {                                                                                         \
+    if (prm.pmode)                                                                             \
+      hipLaunchKernelGGL((chunk_bwd_kernel<K, V, true>), dim3(nblocks), dim3(512), 0, stream, prm);  \
+    else                                                                                       \
+      hipLaunchKernelGGL((chunk_bwd_kernel<K, V, false>), dim3(nblocks), dim3(512), 0, stream, prm); \
+  } while (0)
   if (dk == 128 && dv == 128)
-    hipLaunchKernelGGL((chunk_bwd_kernel<128, 128>), dim3(nblocks), dim3(512), 0, stream, prm);
+    GLA_BWD(128, 128);
   else if (dk == 128 && dv == 64)
-    hipLaunchKernelGGL((chunk_bwd_kernel<128, 64>), dim3(nblocks), dim3(512), 0, stream, prm);
+    GLA_BWD(128, 64);
   else if (dk == 64 && dv == 128)
-    hipLaunchKernelGGL((chunk_bwd_kernel<64, 128>), dim3(nblocks), dim3(512), 0, stream, prm);
+    GLA_BWD(64, 128);
   else if (dk == 64 && dv == 64)
-    hipLaunchKernelGGL((chunk_bwd_kernel<64, 64>), dim3(nblocks), dim3(512), 0, stream, prm);
+    GLA_BWD(64, 64);
   else
     return -2;
+#undef GLA_BWD
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
