@@ -1013,7 +1013,7 @@ int launch_chunk_seg_grad(const ChunkParams& prm, int dk, int nblocks, hipStream
 }
 
 int launch_chunk_fwd_states(const ChunkParams& prm, int dk, int nblocks, hipStream_t stream) {
-  if (prm.dvt != 64 || prm.nvt * 64 != prm.DV || prm.nseg != 1 || prm.sort_units) return -2;
+  if (prm.dvt != 64 || prm.nvt * 64 != prm.DV || prm.nseg != 1) return -2;
   if (dk == 128)
     hipLaunchKernelGGL((chunk_fwd_pipe_kernel<128, kChunkStates, 1>), dim3(nblocks), dim3(512), 0, stream, prm);
   else if (dk == 64)

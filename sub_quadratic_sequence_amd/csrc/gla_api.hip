@@ -597,7 +597,8 @@ int chunk_bwd_impl(const char* fn, bool states_ready, const void* q, const void*
   fp.nseg = 1;
   fp.seg_len = T;
   fp.nseq = nseq;
-  fp.sort_units = 0;
+  // packed sequences: the longest units' work items first, as in the forward
+  fp.sort_units = (cu_seqlens && nseq <= gla::kMaxSortSeqs && units % 8 == 0) ? 1 : 0;
   fp.seg_state = nullptr;
   fp.seg_decay = nullptr;
   fp.hs = prm.hs;

@@ -127,15 +127,21 @@ def test_bwd_without_initial_or_final_state(dev):
     _check(d, got, "bwd no states")
 
 
-@pytest.mark.parametrize("gate,dv", [("weak", 128), ("strong", 128), ("strong", 256)])
-def test_bwd_varlen_with_empty_and_short(dev, gate, dv):
-    lengths = [1, 0, 65, 200, 17, 64]
+@pytest.mark.parametrize("gate,dv,lengths", [
+    ("weak", 128, [1, 0, 65, 200, 17, 64]),
+    ("strong", 128, [1, 0, 65, 200, 17, 64]),
+    ("strong", 256, [1, 0, 65, 200, 17, 64]),
+    ("weak", 128, [0, 300, 65, 129]),        # 8 units: the state pass takes the longest first
+])
+def test_bwd_varlen_with_empty_and_short(dev, gate, dv, lengths):
     say(f"gla_chunk_bwd varlen lengths={lengths} H=2 dk128 dv{dv} gate={gate}")
     d = _case(1, 2, 0, 128, dv, gate=gate, lengths=lengths)
     got = _gpu_bwd(dev, d)
     _check(d, got, f"bwd varlen dv{dv} {gate}")
-    # the empty sequence passes its state through: dS0 = dS_T
-    assert torch.equal(got[4][1].cpu(), d["dsT"][1])
+    # an empty sequence passes its state through: dS0 = dS_T
+    for i, n in enumerate(lengths):
+        if n == 0:
+            assert torch.equal(got[4][i].cpu(), d["dsT"][i])
 
 
 def test_bwd_training_shape_sampled_units(dev):
@@ -197,6 +203,7 @@ def _aligned(ws, nbytes):
     ("varlen", 1, 2, 0, 128, 128, "weak", [1, 0, 65, 200, 17, 64]),
     ("dv256", 1, 2, 200, 128, 256, "weak", None),
     ("dv192_varlen", 1, 2, 0, 64, 192, "strong", [70, 0, 130]),
+    ("varlen_longest_first", 1, 2, 0, 128, 128, "weak", [0, 300, 65, 129]),
 ])
 def test_saved_chunk_states_equal_recomputed(dev, label, B, H, T, dk, dv, gate, lengths):
     """gla_chunk_fwd_states writes the chunk states the backward computes for itself
