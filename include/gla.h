@@ -88,6 +88,27 @@ int gla_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                   int dk, int dv, int chunk_size, int dtype, void* stream);
 
 /*
+ * gla_chunk_fwd with the width of its d_v slices chosen by the caller.  The
+ * columns of the state evolve independently under the recurrence (page "Gated
+ * Linear Attention (GLA) ...", section "The Gated Recurrent Update"), so each
+ * work item is one (sequence, head, slice of dv_slice value columns); the page's
+ * section "Architectural Trade-Offs and Limitations" (item 2) asks for such
+ * tile sizes to be tuned to the hardware.
+ *
+ *   dv_slice   64, 128 (bf16 with dv a multiple of 128, else
+ *              GLA_ERR_UNSUPPORTED), or 0 for gla_slice_plan's choice, which is
+ *              what gla_chunk_fwd takes.  Other values: GLA_ERR_INVALID_ARG.
+ *
+ * Never splits sequences.  Other arguments, layouts and errors as for
+ * gla_chunk_fwd; the results equal gla_chunk_fwd's up to rounding at either
+ * width.
+ */
+int gla_chunk_fwd_sliced(const void* q, const void* k, const void* v, const void* g,
+                         const float* initial_state, void* o, float* final_state,
+                         const int32_t* cu_seqlens, int num_seqs, int B, int H, int T,
+                         int dk, int dv, int chunk_size, int dtype, int dv_slice, void* stream);
+
+/*
  * Device workspace, in bytes, that gla_chunk_fwd_ws needs for this shape; 0 when
  * the call would not split its sequences (then the workspace may be NULL).
  * Arguments as for gla_chunk_fwd (num_seqs > 0 means packed sequences, which
@@ -179,6 +200,22 @@ int gla_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const voi
  * units <= 0 or dv not a positive multiple of 64 give 1.
  */
 int gla_split_plan(long long units, int T, int dv, int dtype, int num_cus, int* seg_len);
+
+/*
+ * The d_v slice width, 64 or 128 value columns per work item, that the unsplit
+ * forward (gla_chunk_fwd, and gla_chunk_fwd_ws / gla_chunk_fwd_noalloc when they
+ * do not split) takes for units = Nseq x H (sequence, head) pairs, dv value
+ * columns and dtype on a device with num_cus compute units.  Host-only.
+ *
+ * A work item holds a compute unit for its whole sequence, so a call runs in
+ * rounds of num_cus items; a last partial round with a fraction f of the units
+ * busy counts 0.5 + 0.5 f of a full round, and a round of 128-column items 1.8
+ * rounds of 64-column items (both ratios measured on MI355X).  The result is
+ * 128 when 1.8 x rounds(units x dv / 128) < rounds(units x dv / 64), else 64;
+ * always 64 unless dtype is GLA_BF16 and dv a positive multiple of 128, and
+ * for units <= 0 or num_cus <= 0.
+ */
+int gla_slice_plan(long long units, int dv, int dtype, int num_cus);
 
 /*
  * Device workspace, in bytes, that gla_chunk_fwd_segments needs: 0 when

@@ -137,16 +137,38 @@ int device_cus() {
   return n;
 }
 
-// d_v slice of the bf16 forward: 128 columns when the batch still gives every
-// compute unit at least one work item with them (the gating of q and k and the
-// score blocks then serve twice the columns), else 64.
-void choose_slice(gla::ChunkParams& prm, long long units, int dtype) {
-  if (dtype != GLA_BF16 || prm.DV % 128 != 0) return;
+// d_v slice of the bf16 forward: 64 or 128 columns per work item.  With 128 the
+// gating of q and k and the score blocks serve twice the columns, but there are
+// half as many work items to spread over the compute units.
+//
+// Rounds of ncu work items that `items` take, a last partial round weighted by
+// how full it is (slice_model).
+double slice_rounds(long long items, int ncu) {
+  const long long full = items / ncu, rem = items - full * ncu;
+  return (double)full +
+         (rem ? gla::slice_model::kPartial + (1.0 - gla::slice_model::kPartial) * (double)rem / ncu : 0.0);
+}
+
+// d_v slice width (64 or 128) of the unsplit forward over `units` (sequence,
+// head) pairs: 128 only for bf16 with dv a multiple of 128, and only where the
+// slice model gives it the shorter time.
+int slice_plan(long long units, int dv, int dtype, int ncu) {
+  if (dtype != GLA_BF16 || dv <= 0 || dv % 128 != 0 || units <= 0 || ncu <= 0) return 64;
+  const long long wide = units * (dv / 128);
+  return gla::slice_model::kWide * slice_rounds(wide, ncu) < slice_rounds(2 * wide, ncu) ? 128 : 64;
+}
+
+// prm (filled by check_chunk_args with 64-column slices) switched to 128-column
+// slices; the caller has checked bf16 and dv % 128 == 0.
+void use_wide_slices(gla::ChunkParams& prm, long long units) {
   const long long items = units * (prm.DV / 128);
-  if (items < device_cus()) return;
   prm.dvt = 128;
   prm.nvt = prm.DV / 128;
   prm.xcd_remap = (items % 8 == 0) ? 1 : 0;
+}
+
+void choose_slice(gla::ChunkParams& prm, long long units, int dtype) {
+  if (slice_plan(units, prm.DV, dtype, device_cus()) == 128) use_wide_slices(prm, units);
 }
 
 
@@ -388,6 +410,35 @@ int gla_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const voi
   char* ws = static_cast<char*>(scratch_for_current_device(fn));
   if (!ws) return GLA_ERR_LAUNCH;
   return run_split(fn, prm, units, nseg, seg_len, dk, dv, dtype, initial_state, final_state, ws, s);
+}
+
+int gla_chunk_fwd_sliced(const void* q, const void* k, const void* v, const void* g,
+                         const float* initial_state, void* o, float* final_state,
+                         const int32_t* cu_seqlens, int num_seqs, int B, int H, int T, int dk,
+                         int dv, int chunk_size, int dtype, int dv_slice, void* stream) {
+  g_last_error[0] = '\0';
+  const char* fn = "gla_chunk_fwd_sliced";
+  if (dv_slice != 0 && dv_slice != 64 && dv_slice != 128)
+    return fail(GLA_ERR_INVALID_ARG, "%s: dv_slice = %d (0, 64 or 128)", fn, dv_slice);
+  gla::ChunkParams prm;
+  long long units = 0;
+  bool nothing = false;
+  const int st = check_chunk_args(fn, q, k, v, g, initial_state, o, final_state, cu_seqlens,
+                                  num_seqs, B, H, T, dk, dv, chunk_size, dtype, prm, units, nothing);
+  if (st != GLA_OK) return st;
+  if (dv_slice == 128 && (dtype != GLA_BF16 || dv % 128 != 0))
+    return fail(GLA_ERR_UNSUPPORTED, "%s: 128-column slices need bf16 and dv a multiple of 128 (dtype=%d dv=%d)",
+                fn, dtype, dv);
+  if (nothing) return GLA_OK;
+  const int width = dv_slice ? dv_slice : slice_plan(units, dv, dtype, device_cus());
+  if (width == 128) use_wide_slices(prm, units);
+  const int rc = gla::launch_chunk_fwd(prm, dk, dtype, (int)(units * prm.nvt),
+                                       reinterpret_cast<hipStream_t>(stream));
+  return launch_status(fn, rc, dk, dtype);
+}
+
+int gla_slice_plan(long long units, int dv, int dtype, int num_cus) {
+  return slice_plan(units, dv, dtype, num_cus);
 }
 
 int gla_split_plan(long long units, int T, int dv, int dtype, int num_cus, int* seg_len) {

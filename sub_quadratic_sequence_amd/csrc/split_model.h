@@ -1,4 +1,5 @@
-// Fitted constants of the forward's sequence-split cost model (microseconds).
+// Fitted constants of the forward's cost models: the sequence split
+// (microseconds) and the d_v slice width (ratios).
 //
 // The page "Qwen Team Releases FlashQLA for High-Performance Linear Attention",
 // section "Core Technical Principles", models a split in its "one wave" case:
@@ -28,4 +29,27 @@ constexpr double kMu1 = 2.13;      // per chunk and wave of the unsplit call
 constexpr double kMu0 = 10.8;      // per unsplit call
 
 }  // namespace split_model
+
+// d_v slice width of the unsplit bf16 forward: 64 or 128 value columns per work
+// item (one workgroup that holds a compute unit for its whole sequence).  A call
+// runs in rounds of num_cus work items.  A last, partial round with a fraction f
+// of the compute units busy costs kPartial + (1 - kPartial) f of a full round,
+// and a round of 128-column items costs kWide rounds of 64-column items (twice
+// the columns per item, the gating of q and k shared by them).  The 128-column
+// slice is taken when kWide x rounds(items at 128) < rounds(items at 64).
+//
+// Values: from 115 pairs of timings of both widths on one MI355X (256 CUs), taken by
+//   python -m sub_quadratic_sequence_amd.fit_slice
+// (bf16, d_k = 128, d_v in {128, 256}, units = B x H from 32 to 800, T from 512
+// to 8192).  Searched on a 0.05 grid, the (kWide, kPartial) pairs whose choices
+// lose least form a band from (1.5, 1.0) to (1.95, 0.1); (1.8, 0.5) lies in it.  Its choices run on
+// average 0.4% slower than the faster width at each point (5% at most, except
+// one 80-item point at 20%), against 3.9% (at most 28%) for the threshold
+// "128 columns once their work items fill the device".
+namespace slice_model {
+
+constexpr double kWide = 1.8;
+constexpr double kPartial = 0.5;
+
+}  // namespace slice_model
 }  // namespace gla

@@ -46,6 +46,10 @@ def load_library():
         lib.gla_chunk_fwd_ws.restype = I
         lib.gla_chunk_fwd_ws.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P,
                                          ctypes.c_size_t, P]
+        lib.gla_chunk_fwd_sliced.restype = I
+        lib.gla_chunk_fwd_sliced.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P]
+        lib.gla_slice_plan.restype = I
+        lib.gla_slice_plan.argtypes = [ctypes.c_longlong, I, I, I]
         lib.gla_split_plan.restype = I
         lib.gla_split_plan.argtypes = [ctypes.c_longlong, I, I, I, I, ctypes.POINTER(I)]
         lib.gla_chunk_fwd_segments_workspace_size.restype = ctypes.c_size_t
@@ -118,7 +122,7 @@ def workspace_size(q, v, cu_seqlens=None, chunk_size: int = 64) -> int:
 
 def gla_chunk_fwd(q, k, v, g, initial_state=None, output_final_state=False, cu_seqlens=None,
                   chunk_size: int = 64, out=None, final_state=None, split: bool = True,
-                  workspace=None, noalloc: bool = False):
+                  workspace=None, noalloc: bool = False, dv_slice=None):
     """Chunkwise GLA forward.
 
     q, k, g: [B, H, T, dk]; v: [B, H, T, dv] (bfloat16 or float32, same dtype);
@@ -133,7 +137,9 @@ def gla_chunk_fwd(q, k, v, g, initial_state=None, output_final_state=False, cu_s
     torch allocation (or ``workspace``, a uint8 GPU tensor).  ``split=False``
     calls ``gla_chunk_fwd``, which never splits.  ``noalloc=True`` calls
     ``gla_chunk_fwd_noalloc`` (the same split, its scratch in the library's own
-    device array; see ``gla_chunk_fwd_noalloc`` below).
+    device array; see ``gla_chunk_fwd_noalloc`` below).  ``dv_slice`` (64, 128
+    or 0) calls ``gla_chunk_fwd_sliced``: never split, value columns per work
+    item chosen by the caller (0: the library's choice, as ``split=False``).
     """
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -167,7 +173,9 @@ def gla_chunk_fwd(q, k, v, g, initial_state=None, output_final_state=False, cu_s
         args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(initial_state), _ptr(out),
                 _ptr(final_state), _ptr(cu_seqlens), num_seqs, B, H, T, dk, dv, int(chunk_size),
                 _dtype_code(q))
-        if noalloc:
+        if dv_slice is not None:
+            rc = lib.gla_chunk_fwd_sliced(*args, int(dv_slice), ctypes.c_void_p(stream))
+        elif noalloc:
             rc = lib.gla_chunk_fwd_noalloc(*args, ctypes.c_void_p(stream))
         elif split:
             need = workspace_size(q, v, cu_seqlens, chunk_size)
@@ -211,6 +219,16 @@ def split_plan(units: int, T: int, dv: int, dtype=torch.bfloat16, num_cus=None):
     n = load_library().gla_split_plan(int(units), int(T), int(dv), code, int(num_cus),
                                       ctypes.byref(seg_len))
     return int(n), int(seg_len.value)
+
+
+def slice_plan(units: int, dv: int, dtype=torch.bfloat16, num_cus=None) -> int:
+    """Value columns per work item (64 or 128) that the unsplit forward takes for
+    ``units`` (sequence, head) pairs and ``dv`` value columns (``gla_slice_plan``;
+    host-only).  ``num_cus`` defaults to the current GPU's compute-unit count."""
+    if num_cus is None:
+        num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    code = GLA_BF16 if dtype == torch.bfloat16 else GLA_F32
+    return int(load_library().gla_slice_plan(int(units), int(dv), code, int(num_cus)))
 
 
 def gla_chunk_fwd_segments(q, k, v, g, num_segments: int, initial_state=None,

@@ -35,8 +35,9 @@ def test_header_declares_the_boundary():
     assert names == ["gdn_chunk_fwd", "gla_chunk_bwd", "gla_chunk_bwd_saved",
                      "gla_chunk_bwd_workspace_size", "gla_chunk_fwd", "gla_chunk_fwd_noalloc",
                      "gla_chunk_fwd_segments", "gla_chunk_fwd_segments_workspace_size",
-                     "gla_chunk_fwd_states", "gla_chunk_fwd_workspace_size", "gla_chunk_fwd_ws",
-                     "gla_last_error", "gla_recurrent_step", "gla_split_plan", "gla_status_string"]
+                     "gla_chunk_fwd_sliced", "gla_chunk_fwd_states", "gla_chunk_fwd_workspace_size",
+                     "gla_chunk_fwd_ws", "gla_last_error", "gla_recurrent_step", "gla_slice_plan",
+                     "gla_split_plan", "gla_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -65,12 +66,13 @@ FAKE = 0x10000  # a 16-byte aligned address; never dereferenced (every call belo
 
 def _chunk(lib, entry="gla_chunk_fwd", **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, s0=None, o=FAKE, sT=None, cu=None, num_seqs=0, B=1,
-             H=2, T=64, dk=128, dv=128, C=64, dtype=0)
+             H=2, T=64, dk=128, dv=128, C=64, dtype=0, dv_slice=0)
     a.update(kw)
     P = ctypes.c_void_p
+    extra = (a["dv_slice"],) if entry == "gla_chunk_fwd_sliced" else ()
     return getattr(lib, entry)(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["s0"]), P(a["o"]),
                                P(a["sT"]), P(a["cu"]), a["num_seqs"], a["B"], a["H"], a["T"],
-                               a["dk"], a["dv"], a["C"], a["dtype"], None)
+                               a["dk"], a["dv"], a["C"], a["dtype"], *extra, None)
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -90,7 +92,7 @@ def _chunk(lib, entry="gla_chunk_fwd", **kw):
     (dict(cu=FAKE, num_seqs=0), 1, "num_seqs"),
     (dict(B=4096, H=4096, T=4096), 1, "int32"),
 ])
-@pytest.mark.parametrize("entry", ["gla_chunk_fwd", "gla_chunk_fwd_noalloc"])
+@pytest.mark.parametrize("entry", ["gla_chunk_fwd", "gla_chunk_fwd_noalloc", "gla_chunk_fwd_sliced"])
 def test_chunk_fwd_rejects(lib, entry, kw, status, needle):
     from sub_quadratic_sequence_amd import gla
 
@@ -100,10 +102,28 @@ def test_chunk_fwd_rejects(lib, entry, kw, status, needle):
     assert entry in gla.last_error()
 
 
-@pytest.mark.parametrize("entry", ["gla_chunk_fwd", "gla_chunk_fwd_noalloc"])
+@pytest.mark.parametrize("entry", ["gla_chunk_fwd", "gla_chunk_fwd_noalloc", "gla_chunk_fwd_sliced"])
 def test_chunk_fwd_zero_tokens_without_outputs_is_a_noop(lib, entry):
     # T == 0 and no final state: nothing to do, returns OK without touching the GPU
     assert _chunk(lib, entry, q=None, k=None, v=None, g=None, o=None, T=0) == 0
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dv_slice=96), 1, "dv_slice = 96"),
+    (dict(dv_slice=-1), 1, "dv_slice = -1"),
+    (dict(dv_slice=256, dv=256), 1, "dv_slice = 256"),
+    (dict(dv_slice=128, dtype=1), 2, "128-column slices"),
+    (dict(dv_slice=128, dv=192), 2, "dv=192"),
+    (dict(dv_slice=128, dv=64), 2, "dv=64"),
+    (dict(dv_slice=128, dv=64, T=0, q=None, k=None, v=None, g=None, o=None), 2, "128-column"),
+    (dict(dv_slice=96, T=0, q=None, k=None, v=None, g=None, o=None), 1, "dv_slice"),
+])
+def test_chunk_fwd_sliced_rejects(lib, kw, status, needle):
+    from sub_quadratic_sequence_amd import gla
+
+    assert _chunk(lib, "gla_chunk_fwd_sliced", **kw) == status
+    assert needle in gla.last_error(), gla.last_error()
+    assert "gla_chunk_fwd_sliced" in gla.last_error()
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -265,10 +285,12 @@ def test_gdn_zero_tokens_without_outputs_is_a_noop(lib):
 
 
 # ------------------------------------------------------------ sequence-split plan
-def _model_constants():
+def _model_constants(ns="split_model"):
+    """The constexpr doubles of namespace `ns` in csrc/split_model.h."""
     text = open(os.path.join(ROOT, "sub_quadratic_sequence_amd", "csrc", "split_model.h")).read()
+    body = re.search(r"namespace %s \{(.*?)\}  // namespace %s" % (ns, ns), text, re.S).group(1)
     return {m.group(1): float(m.group(2))
-            for m in re.finditer(r"constexpr double (k\w+) = ([0-9.eE+-]+);", text)}
+            for m in re.finditer(r"constexpr double (k\w+) = ([0-9.eE+-]+);", body)}
 
 
 def _plan(lib, units, T, dv, dtype=0, ncu=256):
@@ -329,6 +351,53 @@ def test_split_plan_declines_what_it_cannot_split(lib):
     n, _ = _plan(lib, 16, 65536, 128)
     assert lib.gla_chunk_fwd_workspace_size(0, 1, 16, 65536, 128, 128, 64, 0) == \
         n * 16 * (128 * 128 + 128) * 4
+
+
+# ------------------------------------------------------------ d_v slice plan
+def _slice(lib, units, dv, dtype=0, ncu=256):
+    lib.gla_slice_plan.restype = ctypes.c_int
+    lib.gla_slice_plan.argtypes = [ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    return lib.gla_slice_plan(units, dv, dtype, ncu)
+
+
+def _rounds(items, ncu, partial):
+    """Rounds of ncu work items, a last partial round weighted partial + (1 - partial) x fill."""
+    full, rem = divmod(items, ncu)
+    return full + (partial + (1 - partial) * rem / ncu if rem else 0)
+
+
+@pytest.mark.parametrize("ncu", [256, 80, 304])
+def test_slice_plan_follows_the_model(lib, ncu):
+    c = _model_constants("slice_model")
+    assert set(c) == {"kWide", "kPartial"}
+    seen = set()
+    for units in list(range(1, 1200, 7)) + [ncu // 2, ncu, 3 * ncu // 2, 2 * ncu]:
+        for dv in (128, 256, 384, 512):
+            wide = units * dv // 128
+            cost_wide = c["kWide"] * _rounds(wide, ncu, c["kPartial"])
+            want = 128 if cost_wide < _rounds(2 * wide, ncu, c["kPartial"]) else 64
+            assert _slice(lib, units, dv, ncu=ncu) == want, (units, dv, ncu)
+            seen.add(want)
+    assert seen == {64, 128}   # the grid reaches both decisions
+
+
+def test_slice_plan_decisions_measured_on_mi355x(lib):
+    # (units = B x H, dv) -> the faster width in the bf16 timings (d_k = 128, T = 512 .. 8192)
+    # on one MI355X (256 CUs) that the constants were chosen on
+    for units, dv, width in [(128, 128, 64),    # B8 H16, the training shape
+                             (96, 128, 64), (192, 128, 128), (224, 128, 128), (256, 128, 128),
+                             (288, 128, 64), (384, 128, 64), (448, 128, 128), (512, 128, 128),
+                             (64, 256, 64), (96, 256, 128),
+                             (256, 256, 128)]:  # 16 packed sequences x H16 at dv 256
+        assert _slice(lib, units, dv) == width, (units, dv)
+
+
+def test_slice_plan_declines_what_has_no_wide_kernel(lib):
+    assert _slice(lib, 512, 128, dtype=1) == 64     # fp32
+    assert _slice(lib, 512, 192) == 64              # dv not a multiple of 128
+    assert _slice(lib, 512, 64) == 64
+    assert _slice(lib, 0, 128) == 64 and _slice(lib, -5, 128) == 64
+    assert _slice(lib, 512, 0) == 64 and _slice(lib, 512, 128, ncu=0) == 64
 
 
 def test_segments_workspace_size(lib):

@@ -31,13 +31,13 @@ def say(msg):
     print(f"\n[case] {msg}", flush=True)
 
 
-def _fwd(dev, d, s0=None, final=True, cu=None):
+def _fwd(dev, d, s0=None, final=True, cu=None, dv_slice=None):
     from sub_quadratic_sequence_amd import gla
 
     args = [d[n].to(dev) for n in "qkvg"]
     o, sf = gla.gla_chunk_fwd(*args, initial_state=None if s0 is None else s0.to(dev),
                               output_final_state=final,
-                              cu_seqlens=None if cu is None else cu.to(dev))
+                              cu_seqlens=None if cu is None else cu.to(dev), dv_slice=dv_slice)
     torch.cuda.synchronize()
     return o, sf
 
@@ -274,40 +274,33 @@ def test_bf16_shapes(dev, label, B, H, T, dk, dv, gate):
 
 
 # ------------------------------------------------------------------ 128-column d_v slice
-# When (units) x (d_v / 128) reaches the device's compute-unit count, the bf16
-# forward gives each workgroup 128 columns of d_v instead of 64.  H is sized
-# from the CU count so that these cases take that slice on any device.
-def _wide_heads(dev, B, dv):
-    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
-    per = B * (dv // 128)
-    return (ncu + per - 1) // per
-
-
+# gla_chunk_fwd_sliced with dv_slice = 128 runs the bf16 forward with 128 value
+# columns per workgroup at any unit count; gla_chunk_fwd takes that width where
+# gla_slice_plan's model says it is faster.
 WIDE_CASES = [
-    ("dk128_dv256_weak_T130", 2, 130, 128, 256, "weak"),
-    ("dk128_dv128_strong_T97", 4, 97, 128, 128, "strong"),
-    ("dk64_dv256_weak_T200", 2, 200, 64, 256, "weak"),
-    ("dk64_dv384_strong_T65", 1, 65, 64, 384, "strong"),
+    ("dk128_dv256_weak_T130", 2, 3, 130, 128, 256, "weak"),
+    ("dk128_dv128_strong_T97", 4, 2, 97, 128, 128, "strong"),
+    ("dk64_dv256_weak_T200", 2, 2, 200, 64, 256, "weak"),
+    ("dk64_dv384_strong_T65", 1, 3, 65, 64, 384, "strong"),
+    ("dk128_dv128_weak_T1", 3, 2, 1, 128, 128, "weak"),
 ]
 
 
-@pytest.mark.parametrize("label,B,T,dk,dv,gate", WIDE_CASES, ids=[c[0] for c in WIDE_CASES])
-def test_bf16_wide_slice(dev, label, B, T, dk, dv, gate):
-    H = _wide_heads(dev, B, dv)
+@pytest.mark.parametrize("label,B,H,T,dk,dv,gate", WIDE_CASES, ids=[c[0] for c in WIDE_CASES])
+def test_bf16_wide_slice(dev, label, B, H, T, dk, dv, gate):
     w = I.ChunkWorkload("bf16_wide", B=B, H=H, T=T, dk=dk, dv=dv, dtype="bf16", seed=31)
     say(f"bf16 128-column slice {label}: B={B} H={H} T={T} dk={dk} dv={dv} gate={gate}, initial state")
     d = I.chunk_inputs(w, gate=gate, s0=True)
-    o, sf = _fwd(dev, d, s0=d["s0"])
+    o, sf = _fwd(dev, d, s0=d["s0"], dv_slice=128)
     _check_fixed(d, o, sf, d["s0"], TOL_BF16, label)
 
 
 def test_bf16_wide_slice_extreme_gates(dev):
     """The 128-column slice with gates that decay by more than 2^100 inside a
     sub-chunk (exact diagonal partials) and alpha = 0 tokens."""
-    H = _wide_heads(dev, 2, 128)
-    w = I.ChunkWorkload("bf16_wide_extreme", B=2, H=H, T=80, dk=128, dv=128, dtype="bf16", seed=37,
+    w = I.ChunkWorkload("bf16_wide_extreme", B=2, H=4, T=80, dk=128, dv=128, dtype="bf16", seed=37,
                         k_scaled=True)
-    say(f"bf16 128-column slice, extreme gates: B=2 H={H} T=80 dk=128 dv=128")
+    say("bf16 128-column slice, extreme gates: B=2 H=4 T=80 dk=128 dv=128")
     d = I.chunk_inputs(w, s0=True)
     gen = torch.Generator().manual_seed(6)
     g = d["g"].float()
@@ -316,26 +309,56 @@ def test_bf16_wide_slice_extreme_gates(dev):
     g[0, 1, 40, 7] = float("-inf")
     g[1, 3, 10:20, :] = float("-inf")
     d["g"] = g.to(torch.bfloat16)
-    o, sf = _fwd(dev, d, s0=d["s0"])
+    o, sf = _fwd(dev, d, s0=d["s0"], dv_slice=128)
     _check_fixed(d, o, sf, d["s0"], TOL_BF16, "wide extreme")
 
 
-def test_bf16_wide_slice_packed(dev):
-    """Packed sequences (empty, one token, ragged tails) on the 128-column slice,
-    dispatched longest sequence first."""
-    lengths = [300, 5, 0, 129, 1, 64, 200, 77]
-    H = _wide_heads(dev, len(lengths), 256)
+@pytest.mark.parametrize("H,lengths", [(2, [300, 5, 0, 129, 1, 64, 200, 77]),
+                                       (3, [300, 5, 0, 129, 1, 64, 200])])
+def test_bf16_wide_slice_packed(dev, H, lengths):
+    """Packed sequences (empty, one token, ragged tails) on the 128-column slice:
+    16 units (a multiple of 8) are dispatched longest sequence first, 21 in order."""
     w = I.ChunkWorkload("bf16_wide_varlen", B=1, H=H, T=0, dk=128, dv=256, dtype="bf16", seed=41,
                         k_scaled=True)
     say(f"bf16 128-column slice, packed H={H} lengths={lengths} dv=256, strong gates")
     d = I.chunk_inputs(w, lengths=lengths, s0=True, gate="strong")
-    o, sf = _fwd(dev, d, s0=d["s0"], cu=d["cu_seqlens"])
+    o, sf = _fwd(dev, d, s0=d["s0"], cu=d["cu_seqlens"], dv_slice=128)
     o_ref, s_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], s0=d["s0"],
                                      cu_seqlens=d["cu_seqlens"], nthreads=NTHREADS)
     e_o, e_s = unit_err_varlen(o, o_ref, d["cu_seqlens"]), unit_err_fixed(sf, s_ref)
     print(f"wide packed: O err {e_o:.3e} S err {e_s:.3e}", flush=True)
     assert e_o <= TOL_BF16 and e_s <= TOL_BF16
     assert torch.equal(sf[2].cpu(), d["s0"][2])
+
+
+@pytest.mark.parametrize("dv_slice", [0, 64, 128])
+def test_both_slice_widths_match_oracle(dev, dv_slice):
+    """gla_chunk_fwd_sliced at either width, and at the plan's choice (0), on
+    the same inputs: all within tolerance of the oracle."""
+    w = I.ChunkWorkload("bf16_slices", B=2, H=3, T=190, dk=128, dv=256, dtype="bf16", seed=43)
+    say(f"bf16 dv_slice={dv_slice}: B=2 H=3 T=190 dk=128 dv=256, initial state")
+    d = I.chunk_inputs(w, s0=True, gate="strong")
+    o, sf = _fwd(dev, d, s0=d["s0"], dv_slice=dv_slice)
+    _check_fixed(d, o, sf, d["s0"], TOL_BF16, f"dv_slice {dv_slice}")
+
+
+def test_planned_wide_slice_below_one_round(dev):
+    """Work items of 128 columns that fill three quarters of the compute units:
+    the plan takes the 128-column slice (one partial round against two of 64
+    columns), and gla_chunk_fwd then gives the same bits as dv_slice = 128."""
+    from sub_quadratic_sequence_amd import gla
+
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    H = (3 * ncu + 3) // 4
+    assert gla.slice_plan(H, 128) == 128
+    assert gla.slice_plan((ncu + 1) // 2, 128) == 64
+    w = I.ChunkWorkload("bf16_planned_wide", B=1, H=H, T=70, dk=128, dv=128, dtype="bf16", seed=47)
+    say(f"bf16 planned 128-column slice: B=1 H={H} T=70 dk=128 dv=128 ({ncu} CUs)")
+    d = I.chunk_inputs(w, s0=True)
+    o, sf = _fwd(dev, d, s0=d["s0"])
+    o_w, sf_w = _fwd(dev, d, s0=d["s0"], dv_slice=128)
+    assert torch.equal(o, o_w) and torch.equal(sf, sf_w)
+    _check_fixed(d, o, sf, d["s0"], TOL_BF16, "planned wide")
 
 
 # ------------------------------------------------------------------ invariants

@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 NTHREADS = min(16, os.cpu_count() or 1)
 BASE = 20261202
-N_FWD, N_BWD, N_DEC, N_GDN = 40, 16, 16, 16
+N_FWD, N_BWD, N_DEC, N_GDN = 48, 16, 16, 16
 
 
 @pytest.fixture(scope="module")
@@ -69,6 +69,10 @@ def fwd_case(i):
         c.update(B=1, H=int(r.integers(1, 4)), T=0, lengths=_lengths(r, int(r.integers(1, 7)), 300))
     else:   # few units, long sequences: the call goes through the sequence split when it pays
         c.update(B=1, H=int(r.integers(1, 3)), T=int(r.integers(1000, 2601)), lengths=None)
+    # a caller-chosen d_v slice width (gla_chunk_fwd_sliced) on some bf16 calls
+    c["dv_slice"] = None
+    if c["dtype"] == "bf16" and c["dv"] % 128 == 0 and c["layout"] != "long":
+        c["dv_slice"] = [0, 64, 128, 128][int(r.integers(0, 4))]
     return c
 
 
@@ -83,7 +87,8 @@ def test_random_forward(dev, i):
     d = I.chunk_inputs(w, lengths=c["lengths"])
     cu = d["cu_seqlens"]
     o, sf = gla.gla_chunk_fwd(*(d[n].to(dev) for n in "qkvg"), initial_state=_to(dev, d["s0"]),
-                              output_final_state=c["final"], cu_seqlens=_to(dev, cu))
+                              output_final_state=c["final"], cu_seqlens=_to(dev, cu),
+                              dv_slice=c["dv_slice"])
     torch.cuda.synchronize()
     o_ref, s_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], s0=d["s0"], cu_seqlens=cu,
                                      nthreads=NTHREADS)
