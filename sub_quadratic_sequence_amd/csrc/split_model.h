@@ -45,7 +45,9 @@ constexpr double kMu0 = 10.8;      // per unsplit call
 // lose least form a band from (1.5, 1.0) to (1.95, 0.1); (1.8, 0.5) lies in it.  Its choices run on
 // average 0.4% slower than the faster width at each point (5% at most, except
 // one 80-item point at 20%), against 3.9% (at most 28%) for the threshold
-// "128 columns once their work items fill the device".
+// "128 columns once their work items fill the device".  A second run of the
+// script on another MI355X put the least loss at (1.9, 0.15): 0.23% on average,
+// against 0.27% for (1.8, 0.5) and 4.0% for the threshold.
 namespace slice_model {
 
 constexpr double kWide = 1.8;
