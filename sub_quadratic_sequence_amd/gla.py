@@ -415,9 +415,7 @@ def _saves_states(q, v, cu_seqlens):
         return False
     nseq = B if cu_seqlens is None else cu_seqlens.numel() - 1
     cus = torch.cuda.get_device_properties(q.device).multi_processor_count
-    # the planned forward takes 128-column slices only when d_v is a multiple of 128
-    # and its work items fill the device
-    return dv % 128 != 0 or nseq * H * (dv // 128) < cus
+    return slice_plan(nseq * H, dv, q.dtype, cus) == 64
 
 
 class GLAFunction(torch.autograd.Function):
