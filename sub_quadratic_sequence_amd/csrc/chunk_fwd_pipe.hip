@@ -256,7 +256,11 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     const int tg = m;                      // tokens 4tg..4tg+3
     const int ch0 = w * WCH + gq * CPL;    // first channel of this lane
     const int sub = tg >> 2;               // 16-token sub-chunk
-    const int vc0 = w * 16 + gq * 4;       // first of 4 V columns (of each 64-column half)
+    // V is loaded and written in its own lane order: lane (tv, gv) = (lane / 4, lane % 4)
+    // holds tokens 4tv..4tv+3 of columns vc0..vc0+3, so that four consecutive lanes
+    // read one row's 32 bytes (the memory pipeline groups consecutive lanes)
+    const int tv = lane >> 2;
+    const int vc0 = w * 16 + (lane & 3) * 4;   // first of 4 V columns (of each 64-column half)
     // Raw buffer loads over the sequence's rows: a read past its last row
     // returns zeros (the buffer's record count ends there), which is exactly
     // the padding of a partial last chunk (q = k = v = 0, log-gate 0).  Offsets
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
         const_cast<void*>(static_cast<const void*>(static_cast<const unsigned short*>(prm.v) + r0 * DV)),
         (short)0, v_rec, kBufferFlags);
     const unsigned qk_lane = ((4 * tg) * DK + ch0) * 2u;          // token 4tg, channel ch0
-    const unsigned v_lane = ((4 * tg) * DV + vcol0 + vc0) * 2u;   // token 4tg, column vcol0 + vc0
+    const unsigned v_lane = ((4 * tv) * DV + vcol0 + vc0) * 2u;   // token 4tv, column vcol0 + vc0
 
     unsigned rq[4][NWR], rk[4][NWR], rg[4][NWR], rv[NT][4][2];
 
@@ -325,8 +329,8 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
     // compile-time part, plus a compile-time row offset, as for the consumers):
     //  * token a (row 4tg+a) of a [token][channel] operand tile: 16-byte unit
     //    ch0 / 8 (DK = 128) or the 8-byte half of it (DK = 64);
-    //  * channel ch0 + i (state keys) / column vc0 + c (values) of a
-    //    [channel | column][token] tile, tokens 4tg..4tg+3.
+    //  * channel ch0 + i (state keys, tokens 4tg..4tg+3) / column vc0 + c (values,
+    //    tokens 4tv..4tv+3) of a [channel | column][token] tile.
     constexpr unsigned kQ = offsetof(BufT, q), kK = offsetof(BufT, k), kKT = offsetof(BufT, kt),
                        kVT = offsetof(BufT, vt);
     const unsigned lp_tok =
@@ -334,7 +338,7 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
             ? (unsigned)(4 * tg * 256 + ((((ch0 >> 3) ^ TokTile<DK>::swz(4 * tg)) & 15) << 4) + ((ch0 >> 2) & 1) * 8)
             : (unsigned)(4 * tg * TokTile<DK>::kPitch * 2 + ch0 * 2);
     const unsigned lp_kt = (unsigned)(ch0 * 128 + ((((tg >> 1) ^ tr_swz(ch0)) & 7) << 4) + (tg & 1) * 8);
-    const unsigned lp_vt = (unsigned)(vc0 * 128 + ((((tg >> 1) ^ tr_swz(vc0)) & 7) << 4) + (tg & 1) * 8);
+    const unsigned lp_vt = (unsigned)(vc0 * 128 + ((((tv >> 1) ^ tr_swz(vc0)) & 7) << 4) + (tv & 1) * 8);
     char* const lds = reinterpret_cast<char*>(bufs);
     unsigned b_tok = 0, b_kt = 0, b_vt = 0;   // this chunk's buffer plus the lane parts
     auto slot = [&](unsigned tile, int a) __attribute__((always_inline)) -> unsigned short* {
