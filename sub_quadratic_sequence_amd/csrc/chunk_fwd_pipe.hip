@@ -716,8 +716,9 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
       const long slot0 = prm.cu ? (long)h * prm.slots + n + bos / C
                                 : (long)h * prm.slots + n + (long)n * prm.T / C;
       hs_unit = prm.hs + slot0 * DK * DV;
-      // chunk_state_index(srow(0, 4gq + (m & 3)), 64vt + 16cw + 4(m >> 2)); tile rb adds 256
-      hs_lane = ((((vt * 4 + cw) * NRB * 4 + (m & 3)) * 4 + gq) * 16) + 4 * (m >> 2);
+      // chunk_state_index(srow(0, 4gq + (m & 3)), 64vt + 16cw + 4(m >> 2)) = tile 4vt + cw,
+      // row block 2gq, column group m >> 2, row m & 3; state tile rb adds hs_tile(rb)
+      hs_lane = (vt * 4 + cw) * 16 * DK + 128 * gq + 4 * m;
     }
     f32x4 sacc[NT][NRB];
 #pragma unroll
@@ -902,7 +903,9 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
               z[p] = o2 ? r : y[p];
               z[p + 2] = o2 ? y[p + 2] : r;
             }
-            *reinterpret_cast<uint2*>(hu + hs_lane + rb * 256) =
+            // rows srow(rb, .) start at row block 8 (rb >> 1) + (rb & 1) of the tile
+            const int hs_tile = 512 * (rb >> 1) + 64 * (rb & 1);
+            *reinterpret_cast<uint2*>(hu + hs_lane + hs_tile) =
                 uint2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
           }
         }

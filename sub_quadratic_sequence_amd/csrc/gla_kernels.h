@@ -47,14 +47,14 @@ constexpr int kChunkStates = 2;  // the state entering every chunk, to ChunkPara
 constexpr int kSegGrad = 3;      // the backward split's segment state gradients (k, v = q, dO)
 constexpr int kFullStates = 4;   // kFull plus the state entering every chunk, to ChunkParams::hs
 
-// Element (row c, column n) of a chunk-state slot (dk x dv, bf16).  The order
-// follows the forward consumer's accumulators (column slice n / 64, its 16-column
-// tile, the 16-row state tile and accumulator slot of row c, then 16 columns),
-// so the forward stores 128 contiguous bytes per instruction and a backward lane
-// reads 4 consecutive columns of one row as 8 contiguous bytes.
+// Element (row c, column n) of a chunk-state slot (dk x dv, bf16): 16-column tiles
+// of dk rows, each in blocks of 4 rows x 16 columns, a block as 4 groups of 4
+// columns x the 4 rows x 4 columns.  A forward consumer lane stores 4 columns of
+// one row (8 bytes) and each 16 lanes of a store instruction fill 128 contiguous
+// bytes; a backward lane reads 4 columns of one row, and the four lanes of a quad
+// (4 consecutive rows) read 32 contiguous bytes.
 __host__ __device__ constexpr int chunk_state_index(int c, int n, int dk) {
-  return (((((n >> 4) * (dk / 16) + 2 * (c >> 5) + ((c >> 2) & 1)) * 4 + (c & 3)) * 4 + ((c >> 3) & 3)) << 4) +
-         (n & 15);
+  return (n >> 4) * (16 * dk) + (c >> 2) * 64 + ((n >> 2) & 3) * 16 + (c & 3) * 4 + (n & 3);
 }
 
 // Arguments of the segment scan of the sequence split.
