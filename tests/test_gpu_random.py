@@ -5,7 +5,8 @@ DeltaNet forward, each against its fp64 oracle on the same seeded inputs.
 
 Every case is drawn from its own generator (numpy, seed [BASE, kind, index]),
 so a failing case can be rerun alone by its test id; each prints its full
-configuration before touching the GPU.  Tolerances and the per-unit metric are
+configuration before touching the GPU.  GLA_RANDOM_SCALE=k in the environment runs
+k times as many cases.  Tolerances and the per-unit metric are
 those of the hand-written parity tests (parity.py)."""
 import os
 
@@ -23,7 +24,9 @@ pytestmark = pytest.mark.gpu
 
 NTHREADS = min(16, os.cpu_count() or 1)
 BASE = 20261202
-N_FWD, N_BWD, N_DEC, N_GDN = 48, 16, 16, 16
+# GLA_RANDOM_SCALE=k runs k times as many cases (a deeper sweep; the first cases are the same)
+SCALE = max(1, int(os.environ.get("GLA_RANDOM_SCALE", "1")))
+N_FWD, N_BWD, N_DEC, N_GDN = 48 * SCALE, 16 * SCALE, 16 * SCALE, 16 * SCALE
 
 
 @pytest.fixture(scope="module")
