@@ -207,6 +207,25 @@ def gla_chunk_fwd_noalloc(q, k, v, g, initial_state=None, output_final_state=Fal
                          chunk_size=chunk_size, out=out, final_state=final_state, noalloc=True)
 
 
+def gla_chunk_fwd_ws(q, k, v, g, initial_state=None, output_final_state=False, cu_seqlens=None,
+                     chunk_size: int = 64, out=None, final_state=None, workspace=None):
+    """``gla_chunk_fwd`` through the C entry point ``gla_chunk_fwd_ws`` (the sequence
+    split when it pays; ``workspace`` a uint8 GPU tensor, else allocated with torch)."""
+    return gla_chunk_fwd(q, k, v, g, initial_state=initial_state,
+                         output_final_state=output_final_state, cu_seqlens=cu_seqlens,
+                         chunk_size=chunk_size, out=out, final_state=final_state, split=True,
+                         workspace=workspace)
+
+
+def gla_chunk_fwd_sliced(q, k, v, g, dv_slice: int, initial_state=None, output_final_state=False,
+                         cu_seqlens=None, chunk_size: int = 64, out=None, final_state=None):
+    """``gla_chunk_fwd`` through the C entry point ``gla_chunk_fwd_sliced``: never split,
+    ``dv_slice`` (64, 128, or 0 for the library's choice) value columns per work item."""
+    return gla_chunk_fwd(q, k, v, g, initial_state=initial_state,
+                         output_final_state=output_final_state, cu_seqlens=cu_seqlens,
+                         chunk_size=chunk_size, out=out, final_state=final_state, dv_slice=dv_slice)
+
+
 def split_plan(units: int, T: int, dv: int, dtype=torch.bfloat16, num_cus=None):
     """``(segments, segment_length)`` that the sequence-split forward uses for
     fixed-length inputs of ``units`` = B x H (sequence, head) pairs of ``T``
@@ -229,6 +248,10 @@ def slice_plan(units: int, dv: int, dtype=torch.bfloat16, num_cus=None) -> int:
         num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
     code = GLA_BF16 if dtype == torch.bfloat16 else GLA_F32
     return int(load_library().gla_slice_plan(int(units), int(dv), code, int(num_cus)))
+
+
+gla_split_plan = split_plan   # the C entry point's name
+gla_slice_plan = slice_plan
 
 
 def gla_chunk_fwd_segments(q, k, v, g, num_segments: int, initial_state=None,
@@ -400,6 +423,17 @@ def gla_chunk_bwd(q, k, v, g, do, initial_state=None, d_final_state=None, cu_seq
     if rc != GLA_OK:
         raise GLAError(rc, last_error())
     return dq, dk_, dv_, dg, ds0
+
+
+def gla_chunk_bwd_saved(q, k, v, g, do, chunk_states, initial_state=None, d_final_state=None,
+                        cu_seqlens=None, chunk_size: int = 64, want_d_initial_state=None, out=None):
+    """``gla_chunk_bwd`` through the C entry point ``gla_chunk_bwd_saved``: the chunk
+    states come from ``chunk_states``, the workspace a ``gla_chunk_fwd_states`` call on
+    the same inputs filled."""
+    return gla_chunk_bwd(q, k, v, g, do, initial_state=initial_state, d_final_state=d_final_state,
+                         cu_seqlens=cu_seqlens, chunk_size=chunk_size,
+                         want_d_initial_state=want_d_initial_state, workspace=chunk_states, out=out,
+                         states_saved=True)
 
 
 def _saves_states(q, v, cu_seqlens):

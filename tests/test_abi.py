@@ -40,6 +40,17 @@ def test_header_declares_the_boundary():
                      "gla_split_plan", "gla_status_string"]
 
 
+def test_binding_names_every_compute_entry_point():
+    """The Python binding has a function of the same name for every entry point
+    that computes or plans (status strings and size queries have their own names)."""
+    from sub_quadratic_sequence_amd import gla
+
+    for name in _declared_functions():
+        if name.endswith("_workspace_size") or name in ("gla_status_string", "gla_last_error"):
+            continue
+        assert callable(getattr(gla, name, None)), name
+
+
 def test_library_exports_every_declared_symbol(lib):
     from sub_quadratic_sequence_amd import gla
 

@@ -226,8 +226,8 @@ def test_saved_chunk_states_equal_recomputed(dev, label, B, H, T, dk, dv, gate, 
                                             cu_seqlens=cu, chunk_states=ws_b)
     o_r, sf_r = gla.gla_chunk_fwd(q, k, v, g, initial_state=s0, output_final_state=True,
                                   cu_seqlens=cu, split=False)
-    gb = gla.gla_chunk_bwd(q, k, v, g, do, initial_state=s0, d_final_state=dsT, cu_seqlens=cu,
-                           workspace=ws_b, states_saved=True)
+    gb = gla.gla_chunk_bwd_saved(q, k, v, g, do, ws_b, initial_state=s0, d_final_state=dsT,
+                                 cu_seqlens=cu)
     torch.cuda.synchronize()
     nseq = B if cu is None else len(lengths)
     tokens = B * T if cu is None else sum(lengths)

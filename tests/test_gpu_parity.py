@@ -331,6 +331,25 @@ def test_bf16_wide_slice_packed(dev, H, lengths):
     assert torch.equal(sf[2].cpu(), d["s0"][2])
 
 
+def test_named_forward_wrappers(dev):
+    """gla.gla_chunk_fwd_ws and gla.gla_chunk_fwd_sliced (the C entry points' names)
+    give what gla_chunk_fwd gives with split=True and with dv_slice, bit for bit."""
+    from sub_quadratic_sequence_amd import gla
+
+    w = I.ChunkWorkload("wrappers", B=1, H=3, T=1500, dk=128, dv=256, dtype="bf16", seed=45)
+    say("named wrappers: B=1 H=3 T=1500 dk=128 dv=256, initial state")
+    d = I.chunk_inputs(w, s0=True)
+    q, k, v, g, s0 = (d[n].to(dev) for n in ("q", "k", "v", "g", "s0"))
+    a = gla.gla_chunk_fwd_ws(q, k, v, g, initial_state=s0, output_final_state=True)
+    b = gla.gla_chunk_fwd(q, k, v, g, initial_state=s0, output_final_state=True, split=True)
+    c = gla.gla_chunk_fwd_sliced(q, k, v, g, 128, initial_state=s0, output_final_state=True)
+    e = gla.gla_chunk_fwd(q, k, v, g, initial_state=s0, output_final_state=True, dv_slice=128)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert torch.equal(c[0], e[0]) and torch.equal(c[1], e[1])
+    _check_fixed(d, a[0], a[1], d["s0"], TOL_BF16, "gla_chunk_fwd_ws")
+
+
 @pytest.mark.parametrize("dv_slice", [0, 64, 128])
 def test_both_slice_widths_match_oracle(dev, dv_slice):
     """gla_chunk_fwd_sliced at either width, and at the plan's choice (0), on
