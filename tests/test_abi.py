@@ -157,6 +157,36 @@ def test_recurrent_step_rejects(lib, kw, status, needle):
     assert needle in gla.last_error()
 
 
+def test_last_error_is_per_thread(lib):
+    """gla_last_error reports the calling thread's own last failure: two threads
+    that fail differently, interleaved, each read back their own message."""
+    import threading
+
+    lib.gla_last_error.restype = ctypes.c_char_p
+    barrier = threading.Barrier(2, timeout=30)   # a failing worker breaks it, not hangs it
+    seen = {}
+
+    def worker(name, kw, needle):
+        try:
+            for _ in range(50):
+                assert _chunk(lib, "gla_chunk_fwd", **kw) != 0
+                barrier.wait()   # the other thread fails in between
+                msg = lib.gla_last_error().decode()
+                if needle not in msg:
+                    seen[name] = msg
+                    barrier.abort()
+                    return
+                barrier.wait()
+            seen[name] = "ok"
+        except threading.BrokenBarrierError:
+            seen.setdefault(name, "broken barrier")
+
+    a = threading.Thread(target=worker, args=("a", dict(dk=96), "dk=96"))
+    b = threading.Thread(target=worker, args=("b", dict(B=0), "must be positive"))
+    a.start(); b.start(); a.join(); b.join()
+    assert seen == {"a": "ok", "b": "ok"}, seen
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
 
