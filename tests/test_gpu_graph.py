@@ -1,9 +1,11 @@
-"""The entry points under HIP graph capture (torch.cuda.CUDAGraph on the
-capturing stream): each graph is replayed several times, with eager work of the
-program between the replays (other calls of the same entry point, which reuse
-the library's scratch array, torch kernels and device synchronisations), and
-every replay must give exactly the eager result on the same inputs.  The
-library records kernel launches only: no memset, copy or allocation."""
+"""The entry points on several streams and under HIP graph capture.  Calls on two
+streams at once give what each gives alone.  Each captured graph
+(torch.cuda.CUDAGraph on the capturing stream) is replayed several times, with
+eager work of the program between the replays (other calls of the same entry
+point, which reuse the library's scratch array, torch kernels and device
+synchronisations), and every replay must give exactly the eager result on the
+same inputs.  The library records kernel launches only: no memset, copy or
+allocation."""
 import pytest
 import torch
 
@@ -158,3 +160,52 @@ def test_split_backward_replays(dev):
         got = res["r"]
         for name, a, b in zip(("dq", "dk", "dv", "dg", "ds0"), got, ref):
             assert torch.equal(a, b), (rep, name)
+
+
+def test_calls_on_two_streams_are_independent(dev):
+    """Forward, backward and decode calls on two streams at once (different inputs,
+    no ordering between the streams) give exactly what each gives alone: the
+    entry points other than the scratch-array one share no device state."""
+    from sub_quadratic_sequence_amd import gla
+
+    say("two streams: forward (both slice widths), backward and decode, interleaved")
+
+    def make(seed):
+        w = I.ChunkWorkload("streams", B=2, H=4, T=700, dk=128, dv=128, dtype="bf16", seed=seed,
+                            k_scaled=True, s0=True)
+        d = I.chunk_inputs(w)
+        d.update(I.upstream_grads(w, d, final=True))
+        t = {n: d[n].to(dev) for n in ("q", "k", "v", "g", "do", "s0", "dsT")}
+        wd = I.DecodeWorkload("streams_dec", N=16, H=2, dk=128, dv=128, steps=1, seed=seed, dtype="bf16")
+        dd = I.decode_inputs(wd)
+        t.update({"dq_" + n: dd[n][0].to(dev) for n in "qkvg"})
+        t["state"] = dd["s0"].to(dev)
+        return t
+
+    def run(t, state):
+        f1 = gla.gla_chunk_fwd(t["q"], t["k"], t["v"], t["g"], initial_state=t["s0"],
+                               output_final_state=True, dv_slice=64)
+        f2 = gla.gla_chunk_fwd(t["q"], t["k"], t["v"], t["g"], initial_state=t["s0"],
+                               output_final_state=True, dv_slice=128)
+        b = gla.gla_chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["do"], initial_state=t["s0"],
+                              d_final_state=t["dsT"])
+        o = gla.gla_recurrent_step(t["dq_q"], t["dq_k"], t["dq_v"], t["dq_g"], state)
+        return [*f1, *f2, *b, o, state]
+
+    ta, tb = make(71), make(72)
+    sa, sb = ta["state"].clone(), tb["state"].clone()
+    ref_a, ref_b = run(ta, sa), run(tb, sb)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    sa2, sb2 = ta["state"].clone(), tb["state"].clone()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s1):
+        got_a = run(ta, sa2)
+    with torch.cuda.stream(s2):
+        got_b = run(tb, sb2)
+    torch.cuda.synchronize()
+    for ref, got in ((ref_a, got_a), (ref_b, got_b)):
+        for i, (x, y) in enumerate(zip(ref, got)):
+            assert (x is None and y is None) or torch.equal(x, y), i
