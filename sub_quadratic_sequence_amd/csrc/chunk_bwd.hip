@@ -524,14 +524,15 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
       // earlier stores read waits for every outstanding store.)
       if (s == 1 && u > u_lo) prefetch(u - 1);
       if (sw) {   // Ht holds H^ of sub-chunk s
+        // k~^T[c][j] A[i][j] over j in the sub-chunk first: it does not wait for
+        // the carried state, which the products after it do
+        const s16x4 kt = rdt(oK + at(tW, 16 * s, 0));
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        mma16_add(acc, kt, rd8(oA + s * L * LP * 2 + r16L));
 #pragma unroll
         for (int kk = 0; kk < DV / 32; ++kk)   // H^[c][n] dO[i][n]
           mma32(acc, state_op(Ht[2 * kk], Ht[2 * kk + 1]),
                 cat(rd8(oO + at(r16, 16 * s, 4 * kk)), rd8(oO + at(r16, 16 * s, 4 * kk + 2))));
-        // k~^T[c][j] A[i][j] over j in the sub-chunk
-        const s16x4 kt = rdt(oK + at(tW, 16 * s, 0));
-        mma16_add(acc, kt, rd8(oA + s * L * LP * 2 + r16L));
         // lane: channels c0 + 4 grp + r at token 16 s + m
         const float4 d = *reinterpret_cast<const float4*>(lds + oD + ((eD ^ cx(16 * s, 0)) + ca(16 * s, 0, RD)));
         const uint2 qv = *reinterpret_cast<const uint2*>(lds + oQ + at(eQ, 16 * s, 0));
@@ -584,14 +585,14 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
       }
       barrier_lds();
       if (sw) {
+        // q~^T[c][i] A[i][j] over i in the sub-chunk first (independent of B^)
+        const s16x4 qt = rdt(oQ + at(tW, 16 * s, 0));
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        mma16_add(acc, qt, rdt(oA + s * L * LP * 2 + tL));
 #pragma unroll
         for (int kk = 0; kk < DV / 32; ++kk)   // B^[c][n] v[j][n]
           mma32(acc, state_op(Bt[2 * kk], Bt[2 * kk + 1]),
                 cat(rd8(oV + at(r16, 16 * s, 4 * kk)), rd8(oV + at(r16, 16 * s, 4 * kk + 2))));
-        // q~^T[c][i] A[i][j] over i in the sub-chunk
-        const s16x4 qt = rdt(oQ + at(tW, 16 * s, 0));
-        mma16_add(acc, qt, rdt(oA + s * L * LP * 2 + tL));
         const float4 d = *reinterpret_cast<const float4*>(lds + oD + ((eD ^ cx(16 * s, 0)) + ca(16 * s, 0, RD)));
         const uint2 kv = *reinterpret_cast<const uint2*>(lds + oK + at(eQ, 16 * s, 0));
         float x[4] = {qd[s][0] - lo_bf16(kv.x) * acc[0], qd[s][1] - hi_bf16(kv.x) * acc[1],
@@ -624,13 +625,13 @@ __global__ __launch_bounds__(512, 1) void chunk_bwd_kernel(BwdParams prm) {
         for (int b = 0; b < NB; ++b) Bt[b] = Bt[b] * f;
       }
       if (vw) {
+        // dO^T[n][i] P[i][j] over i in the sub-chunk, then B^^T[n][c] k~[j][c]
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        mma16_add(acc, rdt(oO + at(tW, 16 * s, 0)), rdt(oP + s * L * LP * 2 + tL));
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk)   // B^^T[n][c] k~[j][c]
+        for (int kk = 0; kk < DK / 32; ++kk)
           mma32(acc, cat(rdt(oS + at(tS, 32 * kk, 0)), rdt(oS + at(tS, 32 * kk + 4, 0))),
                 rd16(oK + at(r32, 16 * s, 4 * kk)));
-        // dO^T[n][i] P[i][j] over i in the sub-chunk
-        mma16_add(acc, rdt(oO + at(tW, 16 * s, 0)), rdt(oP + s * L * LP * 2 + tL));
         const long t = row0 + 16 * s + m;
         if (t < sq.len)
           *reinterpret_cast<uint2*>(dv_out + t * LDV + n0 + 4 * grp) = pack4(acc[0], acc[1], acc[2], acc[3]);
