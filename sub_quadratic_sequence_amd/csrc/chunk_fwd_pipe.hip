@@ -814,6 +814,22 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
               }
             }
           }
+          // the inter term does not wait for the scores: its products go into the
+          // matrix pipeline while the score results are still on their way
+          f32x4 o2[NT];
+#pragma unroll
+          for (int t = 0; t < NT; ++t) o2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            if constexpr (SAFE) {
+              const Frag<BF16> b = scaled(qf[ks], B.bq[p], ks);
+#pragma unroll
+              for (int t = 0; t < NT; ++t) mma(o2[t], sa[t][ks], b);
+            } else {
+#pragma unroll
+              for (int t = 0; t < NT; ++t) mma(o2[t], sa[t][ks], qf[ks]);
+            }
+          }
           if constexpr (EXT) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -829,9 +845,9 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
           for (int s = 0; s < 4; ++s) pacc[p][s] = (gq * 4 + s > m) ? 0.f : pacc[p][s];  // causal
 
           // O^T(p) = V^T P^T + S_prev^T (Q 2^Gamma)^T
-          f32x4 o1[NT], o2[NT];
+          f32x4 o1[NT];
 #pragma unroll
-          for (int t = 0; t < NT; ++t) o1[t] = o2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int t = 0; t < NT; ++t) o1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; 2 * ks <= p; ++ks) {
             const float pv[8] = {pacc[2 * ks][0],     pacc[2 * ks][1],     pacc[2 * ks][2],
@@ -841,17 +857,6 @@ __global__ __launch_bounds__(512, 1) void chunk_fwd_pipe_kernel(ChunkParams prm)
             frag_from_f32(pb, pv);
 #pragma unroll
             for (int t = 0; t < NT; ++t) mma(o1[t], va[t][ks], pb);
-          }
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            if constexpr (SAFE) {
-              const Frag<BF16> b = scaled(qf[ks], B.bq[p], ks);
-#pragma unroll
-              for (int t = 0; t < NT; ++t) mma(o2[t], sa[t][ks], b);
-            } else {
-#pragma unroll
-              for (int t = 0; t < NT; ++t) mma(o2[t], sa[t][ks], qf[ks]);
-            }
           }
           if constexpr (NT == 1) {
             oacc[0][p] = o1[0] + o2[0];
